@@ -1,0 +1,135 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 chunked SSD forward pass.
+ *
+ * The method (page "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in
+ * NVIDIA CUDA Tile", section "Mamba-2 architecture"): for each batch b and head h,
+ *     h_t = exp(A[h] * dt[b,t,h]) * h_{t-1} + dt[b,t,h] * B[b,t,g] x[b,t,h]^T
+ *     y[b,t,h] = C[b,t,g]^T h_t + D[h] * x[b,t,h]          (g = h / (nheads/ngroups))
+ * evaluated chunk by chunk in three stages: a per-chunk cumulative decay in log2 space
+ * (section "Kernel 1: Computing cumulative sums"), chunk-initial states by the jump
+ * formula carried across chunks (section "Kernel 2: fwd_pass_state"), and a fused
+ * per-chunk output (section "Kernel 3: compute_out").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensors are dense, row-major (last index fastest), in device memory, and every
+ *    pointer must be 16-byte aligned. Layouts:
+ *        x        [batch, seqlen, nheads, headdim]        in_dtype
+ *        dt       [batch, seqlen, nheads]                 in_dtype
+ *        B, C     [batch, seqlen, ngroups, dstate]        in_dtype
+ *        A, D     [nheads]                                fp32
+ *        h0,final [batch, nheads, headdim, dstate]        fp32 (state stored P x S)
+ *        G, dt_t  [batch, nheads, seqlen]                 fp32 (head-major, tokens fastest)
+ *        states   [batch, nheads, nchunks, headdim, dstate]   states_dtype
+ *        y        [batch, seqlen, nheads, headdim]        fp32
+ *    with nchunks = seqlen / chunk.
+ *  - Ownership: the caller allocates and frees every buffer, including the workspace.
+ *    The library never allocates device memory, keeps no pointer after returning and
+ *    holds no global state, so concurrent calls on different buffers are safe.
+ *  - Execution: kernels are enqueued on `stream` (a hipStream_t; NULL means the null
+ *    stream) and the call returns without synchronising. Outputs are valid once the
+ *    caller synchronises that stream. Inputs must not alias outputs.
+ *  - Errors: every argument is validated on the host before anything is enqueued; an
+ *    invalid call returns a non-zero ssd_status and touches no memory. A failed launch
+ *    returns SSD_ERR_HIP. No call aborts the process or throws.
+ *  - Supported sizes: chunk in {64, 128, 256}; headdim in {16, 32, 64, 128};
+ *    dstate in {16, 32, 64, 128, 256}; seqlen a positive multiple of chunk;
+ *    nheads a multiple of ngroups; in_dtype and states_dtype in {SSD_F32, SSD_BF16}.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = 2,       /* a size < 1, nheads % ngroups != 0, or seqlen % chunk != 0 */
+    SSD_ERR_DTYPE = 3,       /* a dtype code that is neither SSD_F32 nor SSD_BF16 */
+    SSD_ERR_UNSUPPORTED = 4, /* chunk, headdim or dstate outside the supported sets */
+    SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
+    SSD_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+    SSD_ERR_HIP = 7          /* the HIP runtime reported an error for a launch */
+} ssd_status;
+
+typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Problem sizes. The names follow the page's kernels: headdim is the per-head size of
+ * x (the page's "head size"), dstate the state size, chunk the chunk length. */
+typedef struct ssd_shape {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int32_t in_dtype;     /* dtype of x, dt, B, C */
+    int32_t states_dtype; /* dtype of the chunk-initial states (ssd_state_pass output,
+                             ssd_chunk_out input, and the forward pass's internal copy) */
+} ssd_shape;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* ssd_status_string(int status);
+
+/* Host-only check of a shape against the supported sets; enqueues nothing. */
+ssd_status ssd_validate_shape(const ssd_shape* shape);
+
+/* Workspace sizes in bytes for ssd_forward and ssd_state_pass. Host-only. */
+ssd_status ssd_forward_workspace_bytes(const ssd_shape* shape, size_t* bytes);
+ssd_status ssd_state_pass_workspace_bytes(const ssd_shape* shape, size_t* bytes);
+
+/*
+ * Stage 1 -- per-chunk cumulative decay (section "Kernel 1: Computing cumulative sums").
+ * For token t of chunk c = t / chunk:
+ *     G[b,h,t]    = log2(e) * sum_{k = c*chunk .. t} A[h] * dt[b,k,h]   (inclusive, fp32)
+ *     dt_t[b,h,t] = dt[b,t,h] widened to fp32
+ * Both outputs use the head-major [batch, nheads, seqlen] layout that the page moves
+ * decay and dt to for contiguous access (section "Mamba-2 performance optimization",
+ * GMEM layout). dt_t may be NULL when only G is wanted.
+ */
+ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float* A, float* G,
+                            float* dt_t, void* stream);
+
+/*
+ * Stage 2 -- chunk-initial states by the jump formula (section "Kernel 2: fwd_pass_state").
+ * With Gl = G at the chunk's last token, the state entering chunk c+1 is
+ *     S_{c+1} = 2^{Gl} S_c + sum_{j in chunk c} dt_j 2^{Gl - G_j} x_j^T (outer) B_j
+ * (stored P x S), starting from S_0 = h0 (zeros when h0 is NULL).
+ * Outputs: states[b,h,c] = S_c for every chunk c (states_dtype), and, when final_state
+ * is not NULL, final_state[b,h] = S_nchunks in fp32.
+ * Inputs: x, B in in_dtype; G and dt_t as produced by ssd_chunk_cumsum; h0 fp32.
+ * The workspace must hold ssd_state_pass_workspace_bytes bytes.
+ */
+ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const void* B, const float* G,
+                          const float* dt_t, const float* h0, void* states, float* final_state,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 3 -- fused chunk output (section "Kernel 3: compute_out"). For chunk c, rows i
+ * and columns j the chunk's tokens:
+ *     y_i = 2^{G_i} C_i^T S_c + sum_{j <= i} 2^{G_i - G_j} (C_i . B_j) dt_j x_j + D[h] x_i
+ * The causal mask keeps the diagonal (y_t reads the state after token t). The
+ * interaction matrix C B^T never leaves the chip; decays of masked pairs are selected
+ * away, never multiplied, so their overflow cannot reach y. y is written in fp32.
+ * D may be NULL (no skip term).
+ */
+ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, const void* C,
+                         const float* G, const float* dt_t, const void* states, const float* D,
+                         float* y, void* stream);
+
+/*
+ * The whole forward pass: stage 1, stage 2, stage 3 on one stream. Returns y (fp32) and,
+ * when final_state is not NULL, the state after the last token (fp32), which may be fed
+ * back as the next call's h0 (section "Kernel 2: fwd_pass_state", after the chunk loop).
+ * h0 and D may be NULL. The workspace must hold ssd_forward_workspace_bytes bytes.
+ */
+ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, const float* h0, float* y,
+                       float* final_state, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */
