@@ -1,0 +1,216 @@
+"""Benchmark of the SSD forward pass on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole forward pass (cumulative decay, chunk states, carry,
+chunk output) over one batch of seeded synthetic input already resident in HBM. The
+timed steps call the C ABI's three stage entry points in order on one stream with HIP
+events between them, which gives each stage's duration over the timed region; the
+one-call ssd_forward path is timed the same way for comparison. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/s (B·L/s) at 1 MI355X + % bf16 MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
+
+
+def algorithmic(w):
+    """Bytes each stage must move (inputs read once, outputs written once) and the
+    per-head dense flop count of the matrix stages."""
+    B, L, H, P, S, G, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    e = 2 if w.dtype == "bf16" else 4
+    es = e  # chunk-initial states are stored in the input dtype
+    nC = L // T
+    dec = B * H * L * 4
+    n_states = B * H * nC * P * S
+    x = B * L * H * P * e
+    bc = B * L * G * S * e
+    h0 = B * H * P * S * 4 if w.h0 else 0
+    fin = B * H * P * S * 4
+    by = {
+        "cumsum": B * L * H * e + H * 4 + 2 * dec,
+        "chunk_state": x + bc + 2 * dec + n_states * 4,
+        "state_carry": n_states * 4 + B * H * nC * 4 + h0 + n_states * es + fin,
+        "chunk_out": x + 2 * bc + 2 * dec + n_states * es + H * 4 + B * L * H * P * 4,
+    }
+    fl = {
+        "chunk_state": 2.0 * B * nC * H * T * P * S,
+        "chunk_out": B * nC * H * (2.0 * T * T * S + 2.0 * T * S * P + 2.0 * T * T * P),
+    }
+    return by, fl
+
+
+def cpu_baseline(w, cpu, budget_s=15.0):
+    """Time the oracle (as it stands) on the workload's first k heads, all batches and
+    all tokens, keeping the heads' shared B/C groups; k is sized for ~budget_s of work."""
+    import oracle
+
+    oracle.build(force=False)
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = max(1, min(cores, int(omp)))
+    hpg = w.nheads // w.ngroups
+
+    def subset(k):
+        g = -(-k // hpg)
+        f = lambda t: t.float().contiguous().numpy()  # noqa: E731
+        return dict(x=f(cpu["x"][:, :, :k]), dt=f(cpu["dt"][:, :, :k]), A=cpu["A"][:k].numpy(),
+                    B=f(cpu["B"][:, :, :g]), C=f(cpu["C"][:, :, :g]), D=cpu["D"][:k].numpy(),
+                    h0=None if cpu["h0"] is None else f(cpu["h0"][:, :k]))
+
+    def run(sub):
+        t0 = time.perf_counter()
+        oracle.forward(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["D"], sub["h0"],
+                       nthreads=cores)
+        return time.perf_counter() - t0
+
+    k_cal = min(w.nheads, hpg * max(1, -(-cores // (w.batch * hpg))))
+    t_cal = run(subset(k_cal))
+    k = int(k_cal * budget_s / max(t_cal, 1e-6))
+    k = max(k_cal, min(w.nheads, (k // hpg) * hpg))
+    dt = run(subset(k)) if k != k_cal else t_cal
+    value = (k / w.nheads) * w.tokens / dt
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"heads 0..{k - 1} of {w.nheads} (all {w.batch} batch rows, all "
+                      f"{w.seqlen} tokens) in {dt:.2f} s wall; fp64 token recurrence on "
+                      f"{cores} threads, scaled to the whole workload's tokens"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="2.7b-bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "layout of this path is a design note, not a measured configuration.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from state_space_sequence_chunk_amd import inputs as gen
+    from state_space_sequence_chunk_amd import ssd
+
+    w = gen.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    cpu = gen.make_inputs(w)
+    d = {k: (None if v is None else v.cuda().contiguous()) for k, v in cpu.items()}
+    B, L, H, P, S, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk
+    nC = L // T
+    sh = ssd.shape_of(d["x"], d["B"], T)
+    dev = "cuda"
+    G = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    dt_t = torch.empty_like(G)
+    states = torch.empty((B, H, nC, P, S), dtype=d["x"].dtype, device=dev)
+    fin = torch.empty((B, H, P, S), dtype=torch.float32, device=dev)
+    y = torch.empty((B, L, H, P), dtype=torch.float32, device=dev)
+    ws_sp = torch.empty(ssd.state_pass_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+    fwd = ssd.Forward(d["x"], d["B"], T)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dt_t, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ssd.ssd_state_pass(sh, d["x"], d["B"], G, dt_t, d["h0"], states, fin, ws_sp, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        ssd.ssd_chunk_out(sh, d["x"], d["B"], d["C"], G, dt_t, states, d["D"], y, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+        fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    span_ms = evs[0][0].elapsed_time(evs[-1][3])
+    stage_ms = {"cumsum": 0.0, "state_pass": 0.0, "chunk_out": 0.0}
+    for e in evs:
+        stage_ms["cumsum"] += e[0].elapsed_time(e[1]) / K
+        stage_ms["state_pass"] += e[1].elapsed_time(e[2]) / K
+        stage_ms["chunk_out"] += e[2].elapsed_time(e[3]) / K
+    ms_per_step = span_ms / K
+
+    # the one-call entry point, same kernels, timed the same way
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_forward = e0.elapsed_time(e1) / K
+
+    by, fl = algorithmic(w)
+    kernels = {
+        "cumsum": {"ms": stage_ms["cumsum"], "bytes": by["cumsum"]},
+        "state_pass": {"ms": stage_ms["state_pass"],
+                       "bytes": by["chunk_state"] + by["state_carry"]},
+        "chunk_out": {"ms": stage_ms["chunk_out"], "bytes": by["chunk_out"],
+                      "flops_per_head_dense": fl["chunk_out"]},
+    }
+    for k, v in kernels.items():
+        v["GBps"] = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+        v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
+    co = kernels["chunk_out"]
+    peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    co["eff_TFLOPs"] = co["flops_per_head_dense"] / (co["ms"] * 1e-3) / 1e12
+    co["eff_mfma_frac"] = co["eff_TFLOPs"] / peak_tf
+    dom = "chunk_out"
+    roofline = {"bound": "hbm", "achieved": kernels[dom]["GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": kernels[dom]["GBps"] / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "chunk_out_kernel",
+                "bytes_per_launch": kernels[dom]["bytes"]}
+
+    out = {
+        "metric": METRIC,
+        "value": w.tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded; distributions of the Mamba-2-shaped workload)",
+        "config": w.describe(),
+        "roofline": roofline,
+        "kernels": kernels,
+        "ms_per_step_ssd_forward": ms_forward,
+        "wall_ms_per_step": wall / K * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, cpu)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

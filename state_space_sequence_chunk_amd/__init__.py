@@ -1,0 +1,7 @@
+"""Mamba-2 chunked SSD forward pass for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``include/ssd.h``; ``ssd`` is the Python binding (marshalling only) and ``inputs``
+draws seeded synthetic workloads.
+"""
+from . import inputs  # noqa: F401

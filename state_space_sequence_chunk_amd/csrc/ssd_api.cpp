@@ -1,0 +1,195 @@
+// C ABI of the SSD forward pass (declared in include/ssd.h).
+//
+// Host-side only: argument validation (before anything is enqueued), workspace layout
+// and the launch order of the stages on the caller's stream. No device memory is
+// allocated here and no synchronisation happens.
+#include <hip/hip_runtime.h>
+
+#include "../../include/ssd.h"
+#include "ssd_launch.h"
+
+using ssd::Dims;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool one_of(int64_t v, std::initializer_list<int64_t> set) {
+    for (int64_t s : set)
+        if (v == s) return true;
+    return false;
+}
+
+size_t esize(int32_t dt) { return dt == SSD_BF16 ? 2 : 4; }
+
+ssd_status check_shape(const ssd_shape* s) {
+    if (!s) return SSD_ERR_NULL;
+    if (s->batch < 1 || s->seqlen < 1 || s->nheads < 1 || s->headdim < 1 || s->dstate < 1 ||
+        s->ngroups < 1 || s->chunk < 1)
+        return SSD_ERR_SHAPE;
+    if (s->nheads % s->ngroups != 0) return SSD_ERR_SHAPE;
+    if (s->seqlen % s->chunk != 0) return SSD_ERR_SHAPE;
+    if ((s->in_dtype != SSD_F32 && s->in_dtype != SSD_BF16) ||
+        (s->states_dtype != SSD_F32 && s->states_dtype != SSD_BF16))
+        return SSD_ERR_DTYPE;
+    if (!one_of(s->chunk, {64, 128, 256}) || !one_of(s->headdim, {16, 32, 64, 128}) ||
+        !one_of(s->dstate, {16, 32, 64, 128, 256}))
+        return SSD_ERR_UNSUPPORTED;
+    // Every element count handed to a kernel must fit in 31 bits of workgroup ids and
+    // in the index arithmetic; reject sizes beyond that rather than overflow.
+    const double states = (double)s->batch * s->nheads * (s->seqlen / s->chunk) * s->headdim *
+                          s->dstate;
+    const double xs = (double)s->batch * s->seqlen * s->nheads * s->headdim;
+    if (states > 2.0e9 || xs > 2.0e9) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+Dims dims_of(const ssd_shape* s) {
+    Dims d;
+    d.batch = (int)s->batch;
+    d.seqlen = (int)s->seqlen;
+    d.nheads = (int)s->nheads;
+    d.headdim = (int)s->headdim;
+    d.dstate = (int)s->dstate;
+    d.ngroups = (int)s->ngroups;
+    d.chunk = (int)s->chunk;
+    return d;
+}
+
+size_t decay_bytes(const ssd_shape* s) {  // one [batch, nheads, seqlen] fp32 array
+    return round_up((size_t)s->batch * s->nheads * s->seqlen * sizeof(float));
+}
+size_t chunk_states_elems(const ssd_shape* s) {
+    return (size_t)s->batch * s->nheads * (s->seqlen / s->chunk) * s->headdim * s->dstate;
+}
+size_t state_pass_ws(const ssd_shape* s) {  // per-chunk state increments, fp32
+    return round_up(chunk_states_elems(s) * sizeof(float));
+}
+size_t forward_ws(const ssd_shape* s) {  // G, dt_t, increments, chunk-initial states
+    return 2 * decay_bytes(s) + state_pass_ws(s) +
+           round_up(chunk_states_elems(s) * esize(s->states_dtype));
+}
+
+ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+#define SSD_REQUIRE(cond, code) \
+    do {                        \
+        if (!(cond)) return code; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(int status) {
+    switch (status) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "invalid sizes (a size < 1, nheads % ngroups != 0 or seqlen % chunk != 0)";
+        case SSD_ERR_DTYPE: return "unknown dtype code";
+        case SSD_ERR_UNSUPPORTED: return "chunk, headdim or dstate outside the supported sets";
+        case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case SSD_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+ssd_status ssd_validate_shape(const ssd_shape* shape) { return check_shape(shape); }
+
+ssd_status ssd_forward_workspace_bytes(const ssd_shape* shape, size_t* bytes) {
+    SSD_REQUIRE(bytes, SSD_ERR_NULL);
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    *bytes = forward_ws(shape);
+    return SSD_OK;
+}
+
+ssd_status ssd_state_pass_workspace_bytes(const ssd_shape* shape, size_t* bytes) {
+    SSD_REQUIRE(bytes, SSD_ERR_NULL);
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    *bytes = state_pass_ws(shape);
+    return SSD_OK;
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float* A, float* G,
+                            float* dt_t, void* stream) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    SSD_REQUIRE(dt && A && G, SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(dt) && aligned16(A) && aligned16(G) && aligned16(dt_t), SSD_ERR_ALIGN);
+    return hip_status(ssd::launch_cumsum(shape->in_dtype, dt, A, G, dt_t, dims_of(shape),
+                                         (hipStream_t)stream));
+}
+
+ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const void* B, const float* G,
+                          const float* dt_t, const float* h0, void* states, float* final_state,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    SSD_REQUIRE(x && B && G && dt_t && states, SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(B) && aligned16(G) && aligned16(dt_t) &&
+                    aligned16(h0) && aligned16(states) && aligned16(final_state),
+                SSD_ERR_ALIGN);
+    SSD_REQUIRE(workspace && workspace_bytes >= state_pass_ws(shape), SSD_ERR_WORKSPACE);
+    SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
+    const Dims d = dims_of(shape);
+    hipStream_t s = (hipStream_t)stream;
+    float* dS = (float*)workspace;
+    hipError_t e = ssd::launch_chunk_state(shape->in_dtype, x, B, G, dt_t, dS, d, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+    return hip_status(ssd::launch_state_carry(shape->states_dtype, dS, G, h0, states,
+                                              final_state, d, s));
+}
+
+ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, const void* C,
+                         const float* G, const float* dt_t, const void* states, const float* D,
+                         float* y, void* stream) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    SSD_REQUIRE(x && B && C && G && dt_t && states && y, SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(B) && aligned16(C) && aligned16(G) &&
+                    aligned16(dt_t) && aligned16(states) && aligned16(D) && aligned16(y),
+                SSD_ERR_ALIGN);
+    return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype, x, B, C, G,
+                                            dt_t, states, D, y, dims_of(shape),
+                                            (hipStream_t)stream));
+}
+
+ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, const float* h0, float* y,
+                       float* final_state, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    SSD_REQUIRE(x && dt && A && B && C && y, SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(dt) && aligned16(A) && aligned16(B) && aligned16(C) &&
+                    aligned16(D) && aligned16(h0) && aligned16(y) && aligned16(final_state),
+                SSD_ERR_ALIGN);
+    SSD_REQUIRE(workspace && workspace_bytes >= forward_ws(shape), SSD_ERR_WORKSPACE);
+    SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
+
+    const Dims d = dims_of(shape);
+    hipStream_t s = (hipStream_t)stream;
+    char* w = (char*)workspace;
+    float* G = (float*)w;
+    float* dt_t = (float*)(w + decay_bytes(shape));
+    float* dS = (float*)(w + 2 * decay_bytes(shape));
+    void* states = (void*)(w + 2 * decay_bytes(shape) + state_pass_ws(shape));
+
+    hipError_t e = ssd::launch_cumsum(shape->in_dtype, dt, A, G, dt_t, d, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+    e = ssd::launch_chunk_state(shape->in_dtype, x, B, G, dt_t, dS, d, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+    e = ssd::launch_state_carry(shape->states_dtype, dS, G, h0, states, final_state, d, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+    return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype, x, B, C, G,
+                                            dt_t, states, D, y, d, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Device-side building blocks for the gfx950 SSD kernels: element types, MFMA operand
+// fragments, conversions, base-2 exponential and a wave64 DPP prefix scan.
+//
+// MFMA fragment convention (16x16 output tiles, K = 32 per step)
+// ---------------------------------------------------------------
+// A "fragment" is the 8 values one lane contributes to a K=32 step. Lane l has
+// row/column index (l & 15) of its operand and "slot group" g = l >> 4 (0..3); its
+// item v (0..7) fills slot (g, v). Each kernel decides which k (token or state index)
+// each slot (g, v) carries; the A and B fragments of one product always use the same
+// assignment, so the sum over k is the same whatever order the matrix core walks the
+// slots in.
+//   bf16 : one v_mfma_f32_16x16x32_bf16 per step (8 bf16 per lane and operand).
+//   fp32 : eight v_mfma_f32_16x16x4_f32 per step; the v-th one takes item v of every
+//          lane (so slot (g, v) is row k = g of the v-th product).
+// The 16x16 fp32 accumulator tile holds element (row 4*g + r, column l & 15) in
+// register r (0..3) of lane l.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x8 v; };
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[v], b.v[v], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }  // RNE
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+// 2^x with the hardware transcendental unit (v_exp_f32). Very negative x gives 0;
+// large positive x gives +inf, which callers select away and never multiply.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
+// four row_shr steps scan each row of 16 lanes, then row_bcast:15 and row_bcast:31 carry
+// row totals into the later rows. Lanes whose DPP source is outside the row keep `old`
+// (0 here), which is the additive identity.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+    int x = __float_as_int(v);
+#define SSD_DPP_ADD(ctrl, rmask)                                                        \
+    {                                                                                   \
+        int t = __builtin_amdgcn_update_dpp(0, x, ctrl, rmask, 0xf, false);             \
+        x = __float_as_int(__int_as_float(x) + __int_as_float(t));                      \
+    }
+    SSD_DPP_ADD(0x111, 0xf)  // row_shr:1
+    SSD_DPP_ADD(0x112, 0xf)  // row_shr:2
+    SSD_DPP_ADD(0x114, 0xf)  // row_shr:4
+    SSD_DPP_ADD(0x118, 0xf)  // row_shr:8
+    SSD_DPP_ADD(0x142, 0xa)  // row_bcast:15 into rows 1 and 3
+    SSD_DPP_ADD(0x143, 0xc)  // row_bcast:31 into rows 2 and 3
+#undef SSD_DPP_ADD
+    return __int_as_float(x);
+}
+
+// 16-byte vector type for cooperative global<->LDS copies.
+typedef uint32_t Vec16 __attribute__((ext_vector_type(4)));
+
+// Map a linear workgroup id so that consecutive logical ids run on the same XCD:
+// hardware hands workgroups to the 8 XCDs round-robin, so logical id
+// (xcd * per_xcd + k) is given to hardware id (k * 8 + xcd). Consecutive logical ids
+// (neighbouring heads of one chunk, which read the same B/C rows) then share an L2.
+__device__ __forceinline__ int xcd_remap(int hw_id, int nblocks) {
+    if (nblocks % 8 != 0) return hw_id;
+    const int per_xcd = nblocks / 8;
+    return (hw_id % 8) * per_xcd + hw_id / 8;
+}
+
+}  // namespace ssd

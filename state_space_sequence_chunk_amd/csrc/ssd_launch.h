@@ -1,0 +1,33 @@
+// Internal launch interface between the C ABI (ssd_api.cpp) and the kernels.
+// Sizes are already validated by the caller; these functions only pick the template
+// instance, size the grid and enqueue on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+enum { kF32 = 0, kBF16 = 1 };
+
+struct Dims {
+    int batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int nchunks() const { return seqlen / chunk; }
+};
+
+hipError_t launch_cumsum(int in_dtype, const void* dt, const float* A, float* G, float* dt_t,
+                         const Dims& d, hipStream_t stream);
+
+hipError_t launch_chunk_state(int in_dtype, const void* x, const void* Bm, const float* G,
+                              const float* dt_t, float* dstate_chunks, const Dims& d,
+                              hipStream_t stream);
+
+hipError_t launch_state_carry(int states_dtype, const float* dstate_chunks, const float* G,
+                              const float* h0, void* states, float* final_state, const Dims& d,
+                              hipStream_t stream);
+
+hipError_t launch_chunk_out(int in_dtype, int states_dtype, const void* x, const void* Bm,
+                            const void* Cm, const float* G, const float* dt_t, const void* states,
+                            const float* D, float* y, const Dims& d, hipStream_t stream);
+
+}  // namespace ssd

@@ -1,0 +1,187 @@
+"""Python binding of the C ABI in include/ssd.h (argument marshalling only).
+
+Every function here forwards device pointers of torch tensors and the current HIP
+stream to the shared library built from ``csrc/``; all computation happens in the HIP
+kernels. When the library is missing or cannot be loaded, calls raise -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libssd_mi355x.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
+          4: "SSD_ERR_UNSUPPORTED", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_ALIGN", 7: "SSD_ERR_HIP"}
+
+# Entry points declared in include/ssd.h.
+EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_bytes",
+           "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
+           "ssd_chunk_out", "ssd_forward")
+
+
+class SSDError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({msg})")
+        self.code = code
+
+
+class ssd_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
+                ("states_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"HIP library not built: {LIB_PATH} is missing. Build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` or "
+            "`python state_space_sequence_chunk_amd/build.py`.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    sp = ctypes.POINTER(ssd_shape)
+    lib.ssd_status_string.argtypes = [i32]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_validate_shape.argtypes = [sp]
+    lib.ssd_forward_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
+    lib.ssd_state_pass_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
+    lib.ssd_chunk_cumsum.argtypes = [sp, vp, vp, vp, vp, vp]
+    lib.ssd_state_pass.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_chunk_out.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for name in EXPORTS[1:]:
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        msg = load_library().ssd_status_string(code).decode()
+        raise SSDError(code, where, msg)
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return SSD_BF16
+    if dt == torch.float32:
+        return SSD_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype,
+               states_dtype=None) -> ssd_shape:
+    ind = in_dtype if isinstance(in_dtype, int) else dtype_code(in_dtype)
+    if states_dtype is None:
+        std = ind
+    else:
+        std = states_dtype if isinstance(states_dtype, int) else dtype_code(states_dtype)
+    return ssd_shape(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate),
+                     int(ngroups), int(chunk), ind, std)
+
+
+def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int, states_dtype=None) -> ssd_shape:
+    """Shape struct from x [b, L, h, P] and B [b, L, g, S]."""
+    b, L, H, P = x.shape
+    G, S = B.shape[2], B.shape[3]
+    return make_shape(b, L, H, P, S, G, chunk, x.dtype, states_dtype)
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the SSD library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def validate_shape(shape: ssd_shape) -> int:
+    return int(load_library().ssd_validate_shape(ctypes.byref(shape)))
+
+
+def forward_workspace_bytes(shape: ssd_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_forward_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)),
+           "ssd_forward_workspace_bytes")
+    return int(n.value)
+
+
+def state_pass_workspace_bytes(shape: ssd_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_state_pass_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)),
+           "ssd_state_pass_workspace_bytes")
+    return int(n.value)
+
+
+def ssd_chunk_cumsum(shape, dt, A, G, dt_t=None, stream=None):
+    _check(load_library().ssd_chunk_cumsum(ctypes.byref(shape), _p(dt), _p(A), _p(G), _p(dt_t),
+                                           _stream(stream)), "ssd_chunk_cumsum")
+
+
+def ssd_state_pass(shape, x, B, G, dt_t, h0, states, final_state, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ssd_state_pass(ctypes.byref(shape), _p(x), _p(B), _p(G), _p(dt_t),
+                                         _p(h0), _p(states), _p(final_state), _p(workspace),
+                                         nbytes, _stream(stream)), "ssd_state_pass")
+
+
+def ssd_chunk_out(shape, x, B, C, G, dt_t, states, D, y, stream=None):
+    _check(load_library().ssd_chunk_out(ctypes.byref(shape), _p(x), _p(B), _p(C), _p(G),
+                                        _p(dt_t), _p(states), _p(D), _p(y), _stream(stream)),
+           "ssd_chunk_out")
+
+
+def ssd_forward(shape, x, dt, A, B, C, D, h0, y, final_state, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ssd_forward(ctypes.byref(shape), _p(x), _p(dt), _p(A), _p(B), _p(C),
+                                      _p(D), _p(h0), _p(y), _p(final_state), _p(workspace),
+                                      nbytes, _stream(stream)), "ssd_forward")
+
+
+class Forward:
+    """Holds the output and workspace buffers of one problem size and runs ssd_forward.
+
+    torch supplies the device memory; the call itself is one C-ABI invocation.
+    """
+
+    def __init__(self, x, B, chunk, states_dtype=None, device=None):
+        self.shape = shape_of(x, B, chunk, states_dtype)
+        dev = device or x.device
+        b, L, H, P = x.shape
+        S = B.shape[3]
+        self.y = torch.empty((b, L, H, P), dtype=torch.float32, device=dev)
+        self.final = torch.empty((b, H, P, S), dtype=torch.float32, device=dev)
+        self.workspace = torch.empty(forward_workspace_bytes(self.shape), dtype=torch.uint8,
+                                     device=dev)
+
+    def __call__(self, x, dt, A, B, C, D=None, h0=None, stream=None):
+        ssd_forward(self.shape, x, dt, A, B, C, D, h0, self.y, self.final, self.workspace,
+                    stream)
+        return self.y, self.final
+
+
+def forward(x, dt, A, B, C, D=None, h0=None, *, chunk, states_dtype=None, stream=None):
+    """One-shot forward pass; returns (y fp32 [b, L, h, P], final state fp32 [b, h, P, S])."""
+    f = Forward(x, B, chunk, states_dtype)
+    return f(x, dt, A, B, C, D, h0, stream)

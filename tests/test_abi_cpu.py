@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects invalid
+arguments on the host before anything is enqueued (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from state_space_sequence_chunk_amd import ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ssd.LIB_PATH),
+                                reason="HIP library not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_stages():
+    names = declared_functions()
+    for n in ("ssd_chunk_cumsum", "ssd_state_pass", "ssd_chunk_out", "ssd_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssd.load_library()
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
+    assert sorted(ssd.EXPORTS) == names
+
+
+def shape(**kw):
+    base = dict(batch=2, seqlen=512, nheads=8, headdim=64, dstate=128, ngroups=2, chunk=256,
+                in_dtype=ssd.SSD_BF16, states_dtype=None)
+    base.update(kw)
+    return ssd.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(nheads=0), 2), (dict(ngroups=3), 2),
+    (dict(seqlen=500), 2), (dict(chunk=96, seqlen=576), 4), (dict(chunk=32, seqlen=512), 4),
+    (dict(headdim=48), 4), (dict(dstate=96), 4), (dict(dstate=512), 4),
+    (dict(in_dtype=7), 3), (dict(states_dtype=5), 3),
+    (dict(headdim=16, dstate=16, chunk=64, in_dtype=ssd.SSD_F32), 0),
+])
+def test_validate_shape(kw, code):
+    assert ssd.validate_shape(shape(**kw)) == code
+
+
+def test_workspace_sizes():
+    s = shape(states_dtype=ssd.SSD_BF16)
+    nchunks = 512 // 256
+    elems = 2 * 8 * nchunks * 64 * 128
+    assert ssd.state_pass_workspace_bytes(s) == elems * 4
+    dec = 2 * 8 * 512 * 4
+    assert ssd.forward_workspace_bytes(s) == 2 * dec + elems * 4 + elems * 2
+    with pytest.raises(ssd.SSDError):
+        ssd.forward_workspace_bytes(shape(seqlen=100))
+
+
+def test_null_shape_and_null_out_pointer():
+    lib = ssd.load_library()
+    assert lib.ssd_validate_shape(None) == 1
+    assert lib.ssd_forward_workspace_bytes(ctypes.byref(shape()), None) == 1
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address: validation fails before any launch
+
+
+def _v(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_forward_rejects_before_launch():
+    lib = ssd.load_library()
+    s = shape()
+    need = ssd.forward_workspace_bytes(s)
+    args = [_v(FAKE)] * 9  # x dt A B C D h0 y final
+    # missing x
+    assert lib.ssd_forward(ctypes.byref(s), None, *args[1:], _v(FAKE), need, None) == 1
+    # misaligned y
+    bad = list(args)
+    bad[7] = _v(FAKE + 4)
+    assert lib.ssd_forward(ctypes.byref(s), *bad, _v(FAKE), need, None) == 6
+    # workspace too small / missing
+    assert lib.ssd_forward(ctypes.byref(s), *args, _v(FAKE), need - 1, None) == 5
+    assert lib.ssd_forward(ctypes.byref(s), *args, None, need, None) == 5
+    # invalid shape wins over everything else
+    s2 = shape(seqlen=100)
+    assert lib.ssd_forward(ctypes.byref(s2), *args, _v(FAKE), need, None) == 2
+
+
+def test_stage_entry_points_reject_before_launch():
+    lib = ssd.load_library()
+    s = shape()
+    f = _v(FAKE)
+    assert lib.ssd_chunk_cumsum(ctypes.byref(s), None, f, f, f, None) == 1
+    assert lib.ssd_chunk_cumsum(ctypes.byref(s), f, f, _v(FAKE + 8), f, None) == 6
+    need = ssd.state_pass_workspace_bytes(s)
+    assert lib.ssd_state_pass(ctypes.byref(s), f, f, f, f, None, None, None, f, need, None) == 1
+    assert lib.ssd_state_pass(ctypes.byref(s), f, f, f, f, None, f, None, f, need - 16, None) == 5
+    assert lib.ssd_chunk_out(ctypes.byref(s), f, f, f, f, f, None, None, f, None) == 1
+    assert lib.ssd_chunk_out(ctypes.byref(s), f, f, f, f, f, f, _v(FAKE + 2), f, None) == 6
+
+
+def test_status_strings():
+    lib = ssd.load_library()
+    for code in range(8):
+        assert lib.ssd_status_string(code)
+    assert lib.ssd_status_string(99) == b"unknown status"
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(ssd, "_lib", None)
+    monkeypatch.setattr(ssd, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        ssd.load_library()
