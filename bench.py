@@ -40,7 +40,7 @@ def algorithmic(w):
     fin = B * H * P * S * 4
     by = {
         "cumsum": B * L * H * e + H * 4 + 2 * dec,
-        "chunk_state": x + bc + 2 * dec + n_states * 4,
+        "chunk_state": x + bc + dec + H * 4 + n_states * 4,
         "state_carry": n_states * 4 + B * H * nC * 4 + h0 + n_states * es + fin,
         "chunk_out": x + 2 * bc + 2 * dec + n_states * es + H * 4 + B * L * H * P * 4,
     }
@@ -130,7 +130,8 @@ def main():
         ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dt_t, stream)
         if ev is not None:
             ev[1].record(stream)
-        ssd.ssd_state_pass(sh, d["x"], d["B"], G, dt_t, d["h0"], states, fin, ws_sp, stream)
+        ssd.ssd_state_pass(sh, d["x"], d["A"], d["B"], G, dt_t, d["h0"], states, fin, ws_sp,
+                           stream)
         if ev is not None:
             ev[2].record(stream)
         ssd.ssd_chunk_out(sh, d["x"], d["B"], d["C"], G, dt_t, states, d["D"], y, stream)

@@ -34,7 +34,9 @@
  *    returns SSD_ERR_HIP. No call aborts the process or throws.
  *  - Supported sizes: chunk in {64, 128, 256}; headdim in {16, 32, 64, 128};
  *    dstate in {16, 32, 64, 128, 256}; seqlen a positive multiple of chunk;
- *    nheads a multiple of ngroups; in_dtype and states_dtype in {SSD_F32, SSD_BF16}.
+ *    nheads a multiple of ngroups; in_dtype and states_dtype in {SSD_F32, SSD_BF16},
+ *    except fp32 inputs with bf16 states (SSD_ERR_UNSUPPORTED: it would only lose the
+ *    precision the fp32 inputs ask for).
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
@@ -51,7 +53,7 @@ typedef enum ssd_status {
     SSD_ERR_NULL = 1,        /* a required pointer is NULL */
     SSD_ERR_SHAPE = 2,       /* a size < 1, nheads % ngroups != 0, or seqlen % chunk != 0 */
     SSD_ERR_DTYPE = 3,       /* a dtype code that is neither SSD_F32 nor SSD_BF16 */
-    SSD_ERR_UNSUPPORTED = 4, /* chunk, headdim or dstate outside the supported sets */
+    SSD_ERR_UNSUPPORTED = 4, /* chunk, headdim, dstate or dtype pair outside the supported sets */
     SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
     SSD_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
     SSD_ERR_HIP = 7          /* the HIP runtime reported an error for a launch */
@@ -92,17 +94,21 @@ ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float*
 
 /*
  * Stage 2 -- chunk-initial states by the jump formula (section "Kernel 2: fwd_pass_state").
- * With Gl = G at the chunk's last token, the state entering chunk c+1 is
- *     S_{c+1} = 2^{Gl} S_c + sum_{j in chunk c} dt_j 2^{Gl - G_j} x_j^T (outer) B_j
- * (stored P x S), starting from S_0 = h0 (zeros when h0 is NULL).
+ * The state entering chunk c+1 is
+ *     S_{c+1} = 2^{G_last} S_c + sum_{j in chunk c} dt_j 2^{G_last - G_j} x_j^T (outer) B_j
+ * (stored P x S), starting from S_0 = h0 (zeros when h0 is NULL); G_last is G at the
+ * chunk's last token, and the exponent G_last - G_j = log2(e) * sum_{k=j+1}^{last} A dt_k
+ * is summed from the chunk's end (hence A is an input), which keeps its rounding error
+ * relative to the exponents that dominate the state.
  * Outputs: states[b,h,c] = S_c for every chunk c (states_dtype), and, when final_state
  * is not NULL, final_state[b,h] = S_nchunks in fp32.
- * Inputs: x, B in in_dtype; G and dt_t as produced by ssd_chunk_cumsum; h0 fp32.
- * The workspace must hold ssd_state_pass_workspace_bytes bytes.
+ * Inputs: x, B in in_dtype; A fp32 [nheads]; G and dt_t as produced by ssd_chunk_cumsum;
+ * h0 fp32. The workspace must hold ssd_state_pass_workspace_bytes bytes.
  */
-ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const void* B, const float* G,
-                          const float* dt_t, const float* h0, void* states, float* final_state,
-                          void* workspace, size_t workspace_bytes, void* stream);
+ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A, const void* B,
+                          const float* G, const float* dt_t, const float* h0, void* states,
+                          float* final_state, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /*
  * Stage 3 -- fused chunk output (section "Kernel 3: compute_out"). For chunk c, rows i

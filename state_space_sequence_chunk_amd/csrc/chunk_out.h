@@ -1,0 +1,381 @@
+// Stage 3: fused per-chunk output (kernel template; instantiated in k_chunk_out_*.hip).
+//
+// Page "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA CUDA
+// Tile", section "Mamba-2 architecture" (the decayed chunk-output formula) and section
+// "Kernel 3: compute_out". For chunk c, token rows i and columns j of the chunk:
+//     y_i = 2^{G_i} C_i . S_c  +  sum_{j <= i} 2^{G_i - G_j} (C_i . B_j) dt_j x_j  +  D x_i
+// where S_c is the chunk-initial state. The interaction C B^T, its decay and the causal
+// mask exist only in registers; decays of masked (j > i) pairs are removed by selection,
+// never by multiplying, so an overflowing 2^{positive} cannot reach y.
+//
+// gfx950 mapping
+// --------------
+// One workgroup of T/32 waves handles one (batch, chunk) and a block of NH heads of one
+// B/C group, one head after another:
+//  - B's chunk rows are staged once in LDS (when they fit next to the per-head buffers)
+//    and C's rows of each wave's two 16-row tiles stay in VGPRs; both serve all NH heads.
+//  - Per head, x's chunk rows, the chunk-initial state, G and dt sit in LDS; the next
+//    head's copies are loaded into registers while the current head computes and are
+//    written to LDS after it, so HBM reads overlap the matrix work.
+//  - Wave w owns row tiles w and T/16-1-w, which splits the causal triangle evenly.
+//    For each pair of 16-column tiles it forms S^T = B_j C_i^T on the matrix core
+//    (K = dstate). In that accumulator layout each lane holds one row i and four j's per
+//    tile -- exactly the A-operand layout of y += W x -- so decay, dt_j and the mask are
+//    applied in registers and W is rounded once to the input dtype and used directly.
+//  - The carried-state term C_i . S_c (K = dstate) is scaled per row by 2^{G_i}; D x_i
+//    is added and y is written in fp32.
+// The page's operand swap for Blackwell's tensor memory does not apply: gfx950 MFMA takes
+// both operands from VGPRs.
+#pragma once
+
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+// 8 consecutive elements of a row into a fragment (zeros when !valid).
+__device__ __forceinline__ void load8(Frag<bf16>& f, const bf16* p, bool valid) {
+    if (valid) f.v = *(const bf16x8*)p;
+    else f.v = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+__device__ __forceinline__ void load8(Frag<float>& f, const float* p, bool valid) {
+    if (valid) {
+        const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+        f.v = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+        f.v = f32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+}
+
+// State fragment in the input's MFMA type. With bf16 inputs and fp32 states each value is
+// split into a bf16 high part and a bf16 remainder (two products).
+template <typename TIn, typename TS> struct StateFrag {
+    static constexpr bool kSplit = false;
+    Frag<TIn> hi, lo;
+    __device__ __forceinline__ void load(const TS* p, bool valid) { load8(hi, p, valid); }
+};
+template <> struct StateFrag<bf16, float> {
+    static constexpr bool kSplit = true;
+    Frag<bf16> hi, lo;
+    __device__ __forceinline__ void load(const float* p, bool valid) {
+        Frag<float> t;
+        load8(t, p, valid);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            hi.v[v] = (bf16)t.v[v];
+            lo.v[v] = (bf16)(t.v[v] - to_f32(hi.v[v]));
+        }
+    }
+};
+
+template <typename TIn, typename TS, int P, int S, int T>
+struct OutCfg {
+    static constexpr int NW = T / 32, NTHR = 2 * T, NIT = T / 16;
+    static constexpr int NPT = P / 16, NKS = (S + 31) / 32;
+    static constexpr int XS = P + 8;  // LDS row stride of x (elements)
+    static constexpr int SS = S + 8;  // LDS row stride of the state and of B (elements)
+    static constexpr int VE = 16 / (int)sizeof(TIn), VES = 16 / (int)sizeof(TS);
+    static constexpr int NXV = T * P / VE / NTHR;                       // x vectors / thread
+    static constexpr int NSV = (P * S / VES + NTHR - 1) / NTHR;         // state vectors / thread
+    static constexpr int NBV = T * S / VE / NTHR;                       // B vectors / thread
+    static constexpr size_t X_BYTES = (size_t)T * XS * sizeof(TIn);
+    static constexpr size_t ST_BYTES = (size_t)P * SS * sizeof(TS);
+    static constexpr size_t GD_BYTES = 2 * (size_t)T * sizeof(float);
+    static constexpr size_t B_BYTES = (size_t)T * SS * sizeof(TIn);
+    static constexpr bool B_IN_LDS = X_BYTES + ST_BYTES + GD_BYTES + B_BYTES <= 163840;
+    static constexpr size_t LDS_BYTES = X_BYTES + ST_BYTES + GD_BYTES + (B_IN_LDS ? B_BYTES : 0);
+};
+
+template <typename TIn, typename TS, int P, int S, int T>
+__global__ __launch_bounds__(2 * T) void chunk_out_kernel(
+    const TIn* __restrict__ x, const TIn* __restrict__ Bm, const TIn* __restrict__ Cm,
+    const float* __restrict__ G, const float* __restrict__ dt_t, const TS* __restrict__ states,
+    const float* __restrict__ Dv, float* __restrict__ y, int L, int H, int ngroups, int NH) {
+    using Cfg = OutCfg<TIn, TS, P, S, T>;
+    constexpr int NPT = Cfg::NPT, NKS = Cfg::NKS, XS = Cfg::XS, SS = Cfg::SS;
+    constexpr int VE = Cfg::VE, VES = Cfg::VES, NTHR = Cfg::NTHR;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    TIn* s_x = (TIn*)smem;                                                  // [T][XS]
+    TS* s_st = (TS*)(smem + Cfg::X_BYTES);                                  // [P][SS]
+    float* s_g = (float*)(smem + Cfg::X_BYTES + Cfg::ST_BYTES);             // [T]
+    float* s_dt = s_g + T;                                                  // [T]
+    TIn* s_b = (TIn*)(smem + Cfg::X_BYTES + Cfg::ST_BYTES + Cfg::GD_BYTES);  // [T][SS]
+
+    const int nC = L / T;
+    const int nhb = H / NH;
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int hb = id % nhb;
+    const int c = (id / nhb) % nC;
+    const int b = id / (nhb * nC);
+    const int h_first = hb * NH;
+    const int g = h_first / (H / ngroups);  // NH divides the heads per group
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int t0 = c * T;
+    const size_t xrow = (size_t)H * P;
+    const size_t grow = (size_t)ngroups * S;
+    const TIn* cg = Cm + (((size_t)b * L + t0) * ngroups + g) * S;
+    const TIn* bg = Bm + (((size_t)b * L + t0) * ngroups + g) * S;
+    const int its[2] = {wave, Cfg::NIT - 1 - wave};
+
+    // ---- per-head staging: global -> registers (prefetch) -> LDS ----------------------
+    Vec16 px[Cfg::NXV], pst[Cfg::NSV];
+    float pg = 0.f, pdt = 0.f;
+    auto load_head = [&](int h) {
+        const TIn* xg = x + (((size_t)b * L + t0) * H + h) * P;
+#pragma unroll
+        for (int i = 0; i < Cfg::NXV; ++i) {
+            const int v = tid + i * NTHR;
+            const int r = v / (P / VE), col = (v % (P / VE)) * VE;
+            px[i] = *(const Vec16*)(xg + (size_t)r * xrow + col);
+        }
+        const TS* sg = states + (((size_t)b * H + h) * nC + c) * (size_t)(P * S);
+#pragma unroll
+        for (int i = 0; i < Cfg::NSV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v < P * S / VES) pst[i] = *(const Vec16*)(sg + (size_t)v * VES);
+        }
+        if (tid < T) {
+            const size_t o = ((size_t)b * H + h) * L + t0 + tid;
+            pg = G[o];
+            pdt = dt_t[o];
+        }
+    };
+    auto store_head = [&]() {
+#pragma unroll
+        for (int i = 0; i < Cfg::NXV; ++i) {
+            const int v = tid + i * NTHR;
+            const int r = v / (P / VE), col = (v % (P / VE)) * VE;
+            *(Vec16*)(s_x + r * XS + col) = px[i];
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::NSV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v < P * S / VES) {
+                const int r = v / (S / VES), col = (v % (S / VES)) * VES;
+                *(Vec16*)(s_st + r * SS + col) = pst[i];
+            }
+        }
+        if (tid < T) {
+            s_g[tid] = pg;
+            s_dt[tid] = pdt;
+        }
+    };
+
+    // ---- prologue: C rows (registers), B rows (LDS), first head -----------------------
+    Frag<TIn> cf[2][NKS];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int s0 = ks * 32 + g4 * 8;
+            load8(cf[q][ks], cg + (size_t)(its[q] * 16 + l16) * grow + s0, s0 < S);
+        }
+    if constexpr (Cfg::B_IN_LDS) {
+        Vec16 pb[Cfg::NBV];
+#pragma unroll
+        for (int i = 0; i < Cfg::NBV; ++i) {
+            const int v = tid + i * NTHR;
+            const int r = v / (S / VE), col = (v % (S / VE)) * VE;
+            pb[i] = *(const Vec16*)(bg + (size_t)r * grow + col);
+        }
+#pragma unroll
+        for (int i = 0; i < Cfg::NBV; ++i) {
+            const int v = tid + i * NTHR;
+            const int r = v / (S / VE), col = (v % (S / VE)) * VE;
+            *(Vec16*)(s_b + r * SS + col) = pb[i];
+        }
+    }
+    load_head(h_first);
+    store_head();
+    __syncthreads();
+
+    for (int hh = 0; hh < NH; ++hh) {
+        const int h = h_first + hh;
+        if (hh + 1 < NH) load_head(h + 1);  // in flight while this head computes
+
+        f32x4 yacc[2][NPT];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) yacc[q][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // 1. carried state: C_i . S_c over dstate, then row scale 2^{G_i}
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int s0 = ks * 32 + g4 * 8;
+                StateFrag<TIn, TS> hf;
+                hf.load(s_st + (pt * 16 + l16) * SS + s0, s0 < S);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    mma(yacc[q][pt], cf[q][ks], hf.hi);
+                    if constexpr (StateFrag<TIn, TS>::kSplit) mma(yacc[q][pt], cf[q][ks], hf.lo);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float sc = exp2_fast(s_g[its[q] * 16 + 4 * g4 + r]);
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) yacc[q][pt][r] *= sc;
+            }
+
+        // 2. within the chunk, two 16-column tiles (32 tokens) per step
+        const int itmax = its[1];
+        for (int kp = 0; 2 * kp <= itmax; ++kp) {
+            // S^T tiles (rows j of the two column tiles, columns i of both row tiles);
+            // one B fragment is live at a time and feeds both row tiles
+            f32x4 st[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) st[q][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int jt = 2 * kp + jj;
+                if (jt > itmax) continue;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int s0 = ks * 32 + g4 * 8;
+                    Frag<TIn> bfr;
+                    if constexpr (Cfg::B_IN_LDS)
+                        load8(bfr, s_b + (jt * 16 + l16) * SS + s0, s0 < S);
+                    else
+                        load8(bfr, bg + (size_t)(jt * 16 + l16) * grow + s0, s0 < S);
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        if (jt <= its[q]) mma(st[q][jj], bfr, cf[q][ks]);
+                }
+            }
+            // x fragments: slot (g4, v) carries token j = 32kp + 16(v/4) + 4 g4 + v%4,
+            // matching the rows the S^T accumulator holds in each lane
+            Frag<TIn> xf[NPT];
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const int j = 32 * kp + 16 * (v >> 2) + 4 * g4 + (v & 3);
+                    xf[pt].v[v] = s_x[j * XS + pt * 16 + l16];
+                }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int it = its[q];
+                if (it < 2 * kp) continue;
+                const int i = it * 16 + l16;
+                const float gi = s_g[i];
+                Frag<TIn> wf;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = (2 * kp + jj) * 16 + 4 * g4 + r;
+                        const float e = exp2_fast(gi - s_g[j]) * s_dt[j];
+                        wf.v[jj * 4 + r] = from_f32<TIn>((i >= j) ? st[q][jj][r] * e : 0.f);
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) mma(yacc[q][pt], wf, xf[pt]);
+            }
+        }
+
+        // 3. skip term and store
+        const float dh = Dv ? Dv[h] : 0.f;
+        float* yb = y + (((size_t)b * L + t0) * H + h) * P;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = its[q] * 16 + 4 * g4 + r;
+                    const int p = pt * 16 + l16;
+                    yb[(size_t)i * xrow + p] = yacc[q][pt][r] + dh * to_f32(s_x[i * XS + p]);
+                }
+
+        __syncthreads();  // every wave is done with this head's LDS copies
+        if (hh + 1 < NH) {
+            store_head();
+            __syncthreads();
+        }
+    }
+}
+
+// Heads per workgroup: the largest of 8, 5, 4, 2, 1 that divides the heads of a group
+// while leaving at least two workgroup rounds of 8 waves per CU on 256 CUs.
+inline int heads_per_block(const Dims& d) {
+    const int hpg = d.nheads / d.ngroups;
+    const long waves_per_wg = d.chunk / 32;
+    const long units = (long)d.batch * d.nchunks() * d.nheads;
+    for (int nh : {8, 5, 4, 2}) {
+        if (hpg % nh) continue;
+        if ((units / nh) * waves_per_wg >= 256L * 16) return nh;
+    }
+    return 1;
+}
+
+template <typename TIn, typename TS, int P, int S, int T>
+hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G,
+                   const float* dt_t, const void* states, const float* D, float* y,
+                   const Dims& d, hipStream_t stream) {
+    using Cfg = OutCfg<TIn, TS, P, S, T>;
+    auto kern = chunk_out_kernel<TIn, TS, P, S, T>;
+    if (Cfg::LDS_BYTES > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)Cfg::LDS_BYTES);
+        if (e != hipSuccess) return e;
+    }
+    const int nh = heads_per_block(d);
+    const int nblocks = d.batch * d.nchunks() * (d.nheads / nh);
+    kern<<<nblocks, 2 * T, Cfg::LDS_BYTES, stream>>>((const TIn*)x, (const TIn*)Bm,
+                                                     (const TIn*)Cm, G, dt_t,
+                                                     (const TS*)states, D, y, d.seqlen,
+                                                     d.nheads, d.ngroups, nh);
+    return hipGetLastError();
+}
+
+template <typename TIn, typename TS, int P, int S>
+hipError_t out_by_t(const void* x, const void* Bm, const void* Cm, const float* G,
+                    const float* dt_t, const void* st, const float* D, float* y, const Dims& d,
+                    hipStream_t s) {
+    switch (d.chunk) {
+        case 64: return run_out<TIn, TS, P, S, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 128: return run_out<TIn, TS, P, S, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 256: return run_out<TIn, TS, P, S, 256>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename TIn, typename TS, int P>
+hipError_t out_by_s(const void* x, const void* Bm, const void* Cm, const float* G,
+                    const float* dt_t, const void* st, const float* D, float* y, const Dims& d,
+                    hipStream_t s) {
+    switch (d.dstate) {
+        case 16: return out_by_t<TIn, TS, P, 16>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 32: return out_by_t<TIn, TS, P, 32>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 64: return out_by_t<TIn, TS, P, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 128: return out_by_t<TIn, TS, P, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 256: return out_by_t<TIn, TS, P, 256>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename TIn, typename TS>
+hipError_t out_by_p(const void* x, const void* Bm, const void* Cm, const float* G,
+                    const float* dt_t, const void* st, const float* D, float* y, const Dims& d,
+                    hipStream_t s) {
+    switch (d.headdim) {
+        case 16: return out_by_s<TIn, TS, 16>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 32: return out_by_s<TIn, TS, 32>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 64: return out_by_s<TIn, TS, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 128: return out_by_s<TIn, TS, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ssd

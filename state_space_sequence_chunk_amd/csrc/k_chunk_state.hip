@@ -43,7 +43,7 @@ struct StateCfg {
 template <typename TIn, int P, int S>
 __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict__ x,
                                                           const TIn* __restrict__ Bm,
-                                                          const float* __restrict__ G,
+                                                          const float* __restrict__ A,
                                                           const float* __restrict__ dt_t,
                                                           float* __restrict__ dS, int L, int H,
                                                           int ngroups, int T) {
@@ -63,12 +63,24 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
     const int t0 = c * T;
     const size_t bh = (size_t)b * H + h;
 
-    // w_j = dt_j * 2^{G_last - G_j}: the decay from token j to the end of the chunk.
+    // w_j = dt_j * 2^{log2(e) * sum_{k=j+1}^{T-1} A dt_k}: the decay from token j to the end
+    // of the chunk (the page's G_last - G_j). It is summed from the chunk's end backwards
+    // (thread tid holds token T-1-tid), so its rounding error is relative to the small
+    // exponents that dominate the state rather than to the chunk's whole cumulative decay.
     {
-        const float* Gc = G + bh * L + t0;
+        __shared__ float s_tot[4];
         const float* dc = dt_t + bh * L + t0;
-        const float glast = Gc[T - 1];
-        for (int t = tid; t < T; t += 256) s_w[t] = dc[t] * exp2_fast(glast - Gc[t]);
+        const float ah = A[h];
+        const int t = T - 1 - tid;
+        const float dtv = tid < T ? dc[t] : 0.f;
+        const float a = ah * dtv;
+        const float incl = wave_inclusive_scan(a);
+        const float excl = wave_shift_up1(incl);
+        if (lane == 63) s_tot[wave] = incl;
+        __syncthreads();
+        float off = 0.f;
+        for (int w2 = 0; w2 < wave; ++w2) off += s_tot[w2];
+        if (tid < T) s_w[t] = dtv * exp2_fast((off + excl) * kLog2e);
     }
 
     const TIn* xg = x + (((size_t)b * L + t0) * H + h) * P;
@@ -192,43 +204,43 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
 }
 
 template <typename TIn, int P, int S>
-static hipError_t run_state(const void* x, const void* Bm, const float* G, const float* dt_t,
+static hipError_t run_state(const void* x, const void* Bm, const float* A, const float* dt_t,
                             float* dS, const Dims& d, hipStream_t stream) {
     const int nblocks = d.batch * d.nchunks() * d.nheads;
     chunk_state_kernel<TIn, P, S><<<nblocks, 256, 0, stream>>>(
-        (const TIn*)x, (const TIn*)Bm, G, dt_t, dS, d.seqlen, d.nheads, d.ngroups, d.chunk);
+        (const TIn*)x, (const TIn*)Bm, A, dt_t, dS, d.seqlen, d.nheads, d.ngroups, d.chunk);
     return hipGetLastError();
 }
 
 template <typename TIn, int P>
-static hipError_t state_by_s(const void* x, const void* Bm, const float* G, const float* dt_t,
+static hipError_t state_by_s(const void* x, const void* Bm, const float* A, const float* dt_t,
                              float* dS, const Dims& d, hipStream_t st) {
     switch (d.dstate) {
-        case 16: return run_state<TIn, P, 16>(x, Bm, G, dt_t, dS, d, st);
-        case 32: return run_state<TIn, P, 32>(x, Bm, G, dt_t, dS, d, st);
-        case 64: return run_state<TIn, P, 64>(x, Bm, G, dt_t, dS, d, st);
-        case 128: return run_state<TIn, P, 128>(x, Bm, G, dt_t, dS, d, st);
-        case 256: return run_state<TIn, P, 256>(x, Bm, G, dt_t, dS, d, st);
+        case 16: return run_state<TIn, P, 16>(x, Bm, A, dt_t, dS, d, st);
+        case 32: return run_state<TIn, P, 32>(x, Bm, A, dt_t, dS, d, st);
+        case 64: return run_state<TIn, P, 64>(x, Bm, A, dt_t, dS, d, st);
+        case 128: return run_state<TIn, P, 128>(x, Bm, A, dt_t, dS, d, st);
+        case 256: return run_state<TIn, P, 256>(x, Bm, A, dt_t, dS, d, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename TIn>
-static hipError_t state_by_p(const void* x, const void* Bm, const float* G, const float* dt_t,
+static hipError_t state_by_p(const void* x, const void* Bm, const float* A, const float* dt_t,
                              float* dS, const Dims& d, hipStream_t st) {
     switch (d.headdim) {
-        case 16: return state_by_s<TIn, 16>(x, Bm, G, dt_t, dS, d, st);
-        case 32: return state_by_s<TIn, 32>(x, Bm, G, dt_t, dS, d, st);
-        case 64: return state_by_s<TIn, 64>(x, Bm, G, dt_t, dS, d, st);
-        case 128: return state_by_s<TIn, 128>(x, Bm, G, dt_t, dS, d, st);
+        case 16: return state_by_s<TIn, 16>(x, Bm, A, dt_t, dS, d, st);
+        case 32: return state_by_s<TIn, 32>(x, Bm, A, dt_t, dS, d, st);
+        case 64: return state_by_s<TIn, 64>(x, Bm, A, dt_t, dS, d, st);
+        case 128: return state_by_s<TIn, 128>(x, Bm, A, dt_t, dS, d, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_chunk_state(int in_dtype, const void* x, const void* Bm, const float* G,
+hipError_t launch_chunk_state(int in_dtype, const void* x, const void* Bm, const float* A,
                               const float* dt_t, float* dS, const Dims& d, hipStream_t stream) {
-    if (in_dtype == kBF16) return state_by_p<bf16>(x, Bm, G, dt_t, dS, d, stream);
-    return state_by_p<float>(x, Bm, G, dt_t, dS, d, stream);
+    if (in_dtype == kBF16) return state_by_p<bf16>(x, Bm, A, dt_t, dS, d, stream);
+    return state_by_p<float>(x, Bm, A, dt_t, dS, d, stream);
 }
 
 }  // namespace ssd

@@ -55,8 +55,7 @@ __global__ __launch_bounds__(256) void cumsum_kernel(const TIn* __restrict__ dt,
         }
         const float incl = wave_inclusive_scan(run);
         // exclusive prefix = inclusive prefix of the previous lane (DPP wave_shr:1)
-        const float excl =
-            __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(incl), 0x138, 0xf, 0xf, false));
+        const float excl = wave_shift_up1(incl);
         const size_t base = ((size_t)b * H + h) * L + t0 + lane * per;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {

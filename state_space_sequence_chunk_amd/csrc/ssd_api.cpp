@@ -36,6 +36,7 @@ ssd_status check_shape(const ssd_shape* s) {
     if ((s->in_dtype != SSD_F32 && s->in_dtype != SSD_BF16) ||
         (s->states_dtype != SSD_F32 && s->states_dtype != SSD_BF16))
         return SSD_ERR_DTYPE;
+    if (s->in_dtype == SSD_F32 && s->states_dtype == SSD_BF16) return SSD_ERR_UNSUPPORTED;
     if (!one_of(s->chunk, {64, 128, 256}) || !one_of(s->headdim, {16, 32, 64, 128}) ||
         !one_of(s->dstate, {16, 32, 64, 128, 256}))
         return SSD_ERR_UNSUPPORTED;
@@ -127,13 +128,14 @@ ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float*
                                          (hipStream_t)stream));
 }
 
-ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const void* B, const float* G,
-                          const float* dt_t, const float* h0, void* states, float* final_state,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A, const void* B,
+                          const float* G, const float* dt_t, const float* h0, void* states,
+                          float* final_state, void* workspace, size_t workspace_bytes,
+                          void* stream) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
-    SSD_REQUIRE(x && B && G && dt_t && states, SSD_ERR_NULL);
-    SSD_REQUIRE(aligned16(x) && aligned16(B) && aligned16(G) && aligned16(dt_t) &&
+    SSD_REQUIRE(x && A && B && G && dt_t && states, SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(A) && aligned16(B) && aligned16(G) && aligned16(dt_t) &&
                     aligned16(h0) && aligned16(states) && aligned16(final_state),
                 SSD_ERR_ALIGN);
     SSD_REQUIRE(workspace && workspace_bytes >= state_pass_ws(shape), SSD_ERR_WORKSPACE);
@@ -141,7 +143,7 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const void* B, 
     const Dims d = dims_of(shape);
     hipStream_t s = (hipStream_t)stream;
     float* dS = (float*)workspace;
-    hipError_t e = ssd::launch_chunk_state(shape->in_dtype, x, B, G, dt_t, dS, d, s);
+    hipError_t e = ssd::launch_chunk_state(shape->in_dtype, x, B, A, dt_t, dS, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
     return hip_status(ssd::launch_state_carry(shape->states_dtype, dS, G, h0, states,
                                               final_state, d, s));
@@ -184,7 +186,7 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
 
     hipError_t e = ssd::launch_cumsum(shape->in_dtype, dt, A, G, dt_t, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
-    e = ssd::launch_chunk_state(shape->in_dtype, x, B, G, dt_t, dS, d, s);
+    e = ssd::launch_chunk_state(shape->in_dtype, x, B, A, dt_t, dS, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
     e = ssd::launch_state_carry(shape->states_dtype, dS, G, h0, states, final_state, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;

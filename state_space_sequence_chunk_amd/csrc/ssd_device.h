@@ -75,6 +75,12 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
     return __int_as_float(x);
 }
 
+// Value of the previous lane (lane 0 gets 0): turns an inclusive scan into an exclusive one
+// without a subtraction (DPP wave_shr:1).
+__device__ __forceinline__ float wave_shift_up1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, false));
+}
+
 // 16-byte vector type for cooperative global<->LDS copies.
 typedef uint32_t Vec16 __attribute__((ext_vector_type(4)));
 

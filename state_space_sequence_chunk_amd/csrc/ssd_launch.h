@@ -18,7 +18,7 @@ struct Dims {
 hipError_t launch_cumsum(int in_dtype, const void* dt, const float* A, float* G, float* dt_t,
                          const Dims& d, hipStream_t stream);
 
-hipError_t launch_chunk_state(int in_dtype, const void* x, const void* Bm, const float* G,
+hipError_t launch_chunk_state(int in_dtype, const void* x, const void* Bm, const float* A,
                               const float* dt_t, float* dstate_chunks, const Dims& d,
                               hipStream_t stream);
 

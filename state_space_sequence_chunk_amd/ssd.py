@@ -61,7 +61,7 @@ def load_library():
     lib.ssd_forward_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
     lib.ssd_state_pass_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
     lib.ssd_chunk_cumsum.argtypes = [sp, vp, vp, vp, vp, vp]
-    lib.ssd_state_pass.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_state_pass.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_chunk_out.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in EXPORTS[1:]:
@@ -139,9 +139,9 @@ def ssd_chunk_cumsum(shape, dt, A, G, dt_t=None, stream=None):
                                            _stream(stream)), "ssd_chunk_cumsum")
 
 
-def ssd_state_pass(shape, x, B, G, dt_t, h0, states, final_state, workspace, stream=None):
+def ssd_state_pass(shape, x, A, B, G, dt_t, h0, states, final_state, workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().ssd_state_pass(ctypes.byref(shape), _p(x), _p(B), _p(G), _p(dt_t),
+    _check(load_library().ssd_state_pass(ctypes.byref(shape), _p(x), _p(A), _p(B), _p(G), _p(dt_t),
                                          _p(h0), _p(states), _p(final_state), _p(workspace),
                                          nbytes, _stream(stream)), "ssd_state_pass")
 

@@ -105,8 +105,9 @@ def test_stage_entry_points_reject_before_launch():
     assert lib.ssd_chunk_cumsum(ctypes.byref(s), None, f, f, f, None) == 1
     assert lib.ssd_chunk_cumsum(ctypes.byref(s), f, f, _v(FAKE + 8), f, None) == 6
     need = ssd.state_pass_workspace_bytes(s)
-    assert lib.ssd_state_pass(ctypes.byref(s), f, f, f, f, None, None, None, f, need, None) == 1
-    assert lib.ssd_state_pass(ctypes.byref(s), f, f, f, f, None, f, None, f, need - 16, None) == 5
+    assert lib.ssd_state_pass(ctypes.byref(s), f, f, f, f, f, None, None, None, f, need, None) == 1
+    assert lib.ssd_state_pass(ctypes.byref(s), f, None, f, f, f, None, f, None, f, need, None) == 1
+    assert lib.ssd_state_pass(ctypes.byref(s), f, f, f, f, f, None, f, None, f, need - 16, None) == 5
     assert lib.ssd_chunk_out(ctypes.byref(s), f, f, f, f, f, None, None, f, None) == 1
     assert lib.ssd_chunk_out(ctypes.byref(s), f, f, f, f, f, f, _v(FAKE + 2), f, None) == 6
 

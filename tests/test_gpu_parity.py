@@ -69,19 +69,30 @@ def test_state_pass_stage(name, states):
     states_t = torch.empty((b, H, nC, P, S), dtype=st_dt, device="cuda")
     fin = torch.empty((b, H, P, S), dtype=torch.float32, device="cuda")
     ws = torch.empty(ssd.state_pass_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
-    ssd.ssd_state_pass(sh, d["x"], d["B"], G, dt_t, d["h0"], states_t, fin, ws)
+    ssd.ssd_state_pass(sh, d["x"], d["A"], d["B"], G, dt_t, d["h0"], states_t, fin, ws)
     torch.cuda.synchronize()
     ref = oracle_forward(cpu, emit_every=w.chunk)
-    tol = TOL["bf16"] if st_dt == torch.bfloat16 else TOL[w.dtype]
     e_fin = max_rel_rms(fin, ref["final"])
     _print(f"{name}/{states}: final max/rms {e_fin:.2e}")
     assert e_fin <= TOL[w.dtype]
     # chunk 0 is h0 itself (or zeros); compare the states that carry information
     s_ref = ref["states"]
-    if np.any(s_ref):
-        e_st = max_rel_rms(states_t.float(), s_ref)
+    if not np.any(s_ref):
+        return
+    got = np64(states_t)
+    if st_dt == torch.bfloat16:
+        # Stored in bf16: rounding to nearest even alone moves each value by up to 2^-9 of
+        # itself, so the bound is elementwise: 2^-8 |ref| (rounding, with margin) plus
+        # 1e-3 rms(ref) for the fp32 arithmetic before the rounding.
+        r = float(np.sqrt(np.mean(s_ref * s_ref)))
+        excess = np.abs(got - s_ref) - (2.0 ** -8 * np.abs(s_ref) + 1e-3 * r)
+        _print(f"{name}/{states}: bf16 states, worst excess over the rounding bound "
+               f"{excess.max() / r:.2e} rms")
+        assert excess.max() <= 0.0
+    else:
+        e_st = max_rel_rms(got, s_ref)
         _print(f"{name}/{states}: chunk-initial states max/rms {e_st:.2e}")
-        assert e_st <= tol
+        assert e_st <= TOL[w.dtype]
 
 
 # --- stage 3 --------------------------------------------------------------------------
