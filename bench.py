@@ -88,6 +88,23 @@ def cpu_baseline(w, cpu, budget_s=15.0):
                       f"{cores} threads, scaled to the whole workload's tokens"}
 
 
+def measure_copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Achievable HBM bandwidth for context: a device-to-device copy of 1 GiB
+    (2 GiB of traffic per copy), timed with HIP events."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +112,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="2.7b-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (3 times); "
+                         "used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
@@ -107,8 +127,17 @@ def main():
     from state_space_sequence_chunk_amd import inputs as gen
     from state_space_sequence_chunk_amd import ssd
 
-    w = gen.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 3}), flush=True)
+        return
+    copy_gbps = measure_copy_bandwidth(torch)
+    w = gen.WORKLOADS[args.workload]
     cpu = gen.make_inputs(w)
     d = {k: (None if v is None else v.cuda().contiguous()) for k, v in cpu.items()}
     B, L, H, P, S, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk
@@ -206,6 +235,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "ms_per_step_ssd_forward": ms_forward,
+        "copy_GBps": copy_gbps,
         "wall_ms_per_step": wall / K * 1e3,
     }
     if not args.no_cpu_baseline:

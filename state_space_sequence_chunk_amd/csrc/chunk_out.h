@@ -72,16 +72,17 @@ template <typename TIn, typename TS, int P, int S, int T>
 struct OutCfg {
     static constexpr int NW = T / 32, NTHR = 2 * T, NIT = T / 16;
     static constexpr int NPT = P / 16, NKS = (S + 31) / 32;
-    static constexpr int XS = P + 8;  // LDS row stride of x (elements)
-    static constexpr int SS = S + 8;  // LDS row stride of the state and of B (elements)
+    static constexpr int XS = col_stride<TIn>(P);   // x rows (read by columns)
+    static constexpr int SS = row_stride<TS>(S);    // state rows (read by rows)
+    static constexpr int BS = row_stride<TIn>(S);   // B rows (read by rows)
     static constexpr int VE = 16 / (int)sizeof(TIn), VES = 16 / (int)sizeof(TS);
     static constexpr int NXV = T * P / VE / NTHR;                       // x vectors / thread
     static constexpr int NSV = (P * S / VES + NTHR - 1) / NTHR;         // state vectors / thread
     static constexpr int NBV = T * S / VE / NTHR;                       // B vectors / thread
     static constexpr size_t X_BYTES = (size_t)T * XS * sizeof(TIn);
     static constexpr size_t ST_BYTES = (size_t)P * SS * sizeof(TS);
-    static constexpr size_t GD_BYTES = 2 * (size_t)T * sizeof(float);
-    static constexpr size_t B_BYTES = (size_t)T * SS * sizeof(TIn);
+    static constexpr size_t GD_BYTES = 3 * (size_t)T * sizeof(float);  // G, dt, u
+    static constexpr size_t B_BYTES = (size_t)T * BS * sizeof(TIn);
     static constexpr bool B_IN_LDS = X_BYTES + ST_BYTES + GD_BYTES + B_BYTES <= 163840;
     static constexpr size_t LDS_BYTES = X_BYTES + ST_BYTES + GD_BYTES + (B_IN_LDS ? B_BYTES : 0);
 };
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const float* __restrict__ G, const float* __restrict__ dt_t, const TS* __restrict__ states,
     const float* __restrict__ Dv, float* __restrict__ y, int L, int H, int ngroups, int NH) {
     using Cfg = OutCfg<TIn, TS, P, S, T>;
-    constexpr int NPT = Cfg::NPT, NKS = Cfg::NKS, XS = Cfg::XS, SS = Cfg::SS;
+    constexpr int NPT = Cfg::NPT, NKS = Cfg::NKS, XS = Cfg::XS, SS = Cfg::SS, BS = Cfg::BS;
     constexpr int VE = Cfg::VE, VES = Cfg::VES, NTHR = Cfg::NTHR;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -100,7 +101,8 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     TS* s_st = (TS*)(smem + Cfg::X_BYTES);                                  // [P][SS]
     float* s_g = (float*)(smem + Cfg::X_BYTES + Cfg::ST_BYTES);             // [T]
     float* s_dt = s_g + T;                                                  // [T]
-    TIn* s_b = (TIn*)(smem + Cfg::X_BYTES + Cfg::ST_BYTES + Cfg::GD_BYTES);  // [T][SS]
+    float* s_u = s_dt + T;                                                  // [T]
+    TIn* s_b = (TIn*)(smem + Cfg::X_BYTES + Cfg::ST_BYTES + Cfg::GD_BYTES);  // [T][BS]
 
     const int nC = L / T;
     const int nhb = H / NH;
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
 
     // ---- per-head staging: global -> registers (prefetch) -> LDS ----------------------
     Vec16 px[Cfg::NXV], pst[Cfg::NSV];
-    float pg = 0.f, pdt = 0.f;
+    float pg = 0.f, pdt = 0.f, pge = 0.f;
     auto load_head = [&](int h) {
         const TIn* xg = x + (((size_t)b * L + t0) * H + h) * P;
 #pragma unroll
@@ -137,9 +139,10 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             if (v < P * S / VES) pst[i] = *(const Vec16*)(sg + (size_t)v * VES);
         }
         if (tid < T) {
-            const size_t o = ((size_t)b * H + h) * L + t0 + tid;
-            pg = G[o];
-            pdt = dt_t[o];
+            const size_t o = ((size_t)b * H + h) * L + t0;
+            pg = G[o + tid];
+            pdt = dt_t[o + tid];
+            pge = G[o + (tid | 15)];  // G at the last token of this token's 16-token tile
         }
     };
     auto store_head = [&]() {
@@ -160,6 +163,9 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         if (tid < T) {
             s_g[tid] = pg;
             s_dt[tid] = pdt;
+            // u_j = dt_j 2^{G_e - G_j}, e = last token of j's tile: the decay from j to the
+            // end of its tile (<= 1), shared by every row tile below it
+            s_u[tid] = pdt * exp2_fast(pge - pg);
         }
     };
 
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         for (int i = 0; i < Cfg::NBV; ++i) {
             const int v = tid + i * NTHR;
             const int r = v / (S / VE), col = (v % (S / VE)) * VE;
-            *(Vec16*)(s_b + r * SS + col) = pb[i];
+            *(Vec16*)(s_b + r * BS + col) = pb[i];
         }
     }
     load_head(h_first);
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
                     const int s0 = ks * 32 + g4 * 8;
                     Frag<TIn> bfr;
                     if constexpr (Cfg::B_IN_LDS)
-                        load8(bfr, s_b + (jt * 16 + l16) * SS + s0, s0 < S);
+                        load8(bfr, s_b + (jt * 16 + l16) * BS + s0, s0 < S);
                     else
                         load8(bfr, bg + (size_t)(jt * 16 + l16) * grow + s0, s0 < S);
 #pragma unroll
@@ -256,12 +262,19 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             // matching the rows the S^T accumulator holds in each lane
             Frag<TIn> xf[NPT];
 #pragma unroll
-            for (int pt = 0; pt < NPT; ++pt)
+            for (int pt = 0; pt < NPT; ++pt) {
+                if constexpr (sizeof(TIn) == 2) {
+                    const bf16x4 lo4 = lds_col4(s_x, XS, 32 * kp + 4 * g4, pt * 16, lane);
+                    const bf16x4 hi4 = lds_col4(s_x, XS, 32 * kp + 16 + 4 * g4, pt * 16, lane);
+                    xf[pt].v = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else {
 #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    const int j = 32 * kp + 16 * (v >> 2) + 4 * g4 + (v & 3);
-                    xf[pt].v[v] = s_x[j * XS + pt * 16 + l16];
+                    for (int v = 0; v < 8; ++v) {
+                        const int j = 32 * kp + 16 * (v >> 2) + 4 * g4 + (v & 3);
+                        xf[pt].v[v] = s_x[j * XS + pt * 16 + l16];
+                    }
                 }
+            }
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int it = its[q];
@@ -271,11 +284,26 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
                 Frag<TIn> wf;
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
+                    const int jt = 2 * kp + jj;
+                    const int j0 = jt * 16 + 4 * g4;  // this lane's four rows j0 .. j0+3
+                    if (jt < it) {
+                        // every i is past the tile's last token e: decay = 2^{G_i - G_e} u_j
+                        const float v = exp2_fast(gi - s_g[jt * 16 + 15]);
+                        const f32x4 u = *(const f32x4*)(s_u + j0);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = (2 * kp + jj) * 16 + 4 * g4 + r;
-                        const float e = exp2_fast(gi - s_g[j]) * s_dt[j];
-                        wf.v[jj * 4 + r] = from_f32<TIn>((i >= j) ? st[q][jj][r] * e : 0.f);
+                        for (int r = 0; r < 4; ++r) wf.v[jj * 4 + r] = from_f32<TIn>(st[q][jj][r] * (v * u[r]));
+                    } else if (jt == it) {
+                        // diagonal tile: exact decay, causal mask by selection
+                        const f32x4 gj = *(const f32x4*)(s_g + j0);
+                        const f32x4 dj = *(const f32x4*)(s_dt + j0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float e = exp2_fast(gi - gj[r]) * dj[r];
+                            wf.v[jj * 4 + r] = from_f32<TIn>((i >= j0 + r) ? st[q][jj][r] * e : 0.f);
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) wf.v[jj * 4 + r] = from_f32<TIn>(0.f);
                     }
                 }
 #pragma unroll

@@ -18,15 +18,16 @@
 // w_j x_j[p] is formed in fp32; for bf16 inputs it is split into a bf16 high part and
 // a bf16 remainder, each multiplied by the exact bf16 B (two MFMAs), which keeps the
 // product at ~16 significant bits instead of bf16's 8. fp32 inputs use fp32 MFMA.
-// Slot (g, v) of a fragment carries token 4*v + g of the 32-token step, which keeps
-// the four slot groups' LDS reads on disjoint banks.
+// Slot (g, v) of a fragment carries token 16*(v/4) + 4*g + v%4 of the 32-token step:
+// four consecutive rows per half, which is what one gfx950 transposing LDS read
+// (ds_read_b64_tr_b16) delivers from the row-major tiles, so a bf16 fragment costs two
+// LDS instructions instead of eight 2-byte reads.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-constexpr int kTK = 64;   // tokens per LDS block
-constexpr int kPad = 16;  // LDS row padding in elements
+constexpr int kTK = 64;  // tokens per LDS block
 
 template <typename TIn, int P, int S>
 struct StateCfg {
@@ -35,7 +36,7 @@ struct StateCfg {
     static constexpr int MPT = NPT >= 4 ? NPT / 4 : 1;                   // p-tiles per wave
     static constexpr int MST = NPT >= 4 ? NST : (NST + WPP - 1) / WPP;   // s-tiles per wave
     static constexpr int VE = 16 / (int)sizeof(TIn);                     // elements per 16 B
-    static constexpr int XS = P + kPad, BS = S + kPad;                   // LDS row strides
+    static constexpr int XS = col_stride<TIn>(P), BS = col_stride<TIn>(S);  // LDS row strides
     static constexpr int XVEC = kTK * P / VE, BVEC = kTK * S / VE;
     static constexpr int XPT = (XVEC + 255) / 256, BPT = (BVEC + 255) / 256;
 };
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
                                                           float* __restrict__ dS, int L, int H,
                                                           int ngroups, int T) {
     using Cfg = StateCfg<TIn, P, S>;
-    __shared__ float s_w[256];
+    __shared__ __attribute__((aligned(16))) float s_w[256];
     __shared__ __attribute__((aligned(16))) TIn s_x[kTK * Cfg::XS];
     __shared__ __attribute__((aligned(16))) TIn s_b[kTK * Cfg::BS];
 
@@ -141,24 +142,45 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
         if (kb + 1 < nKB) SSD_GLOAD(kb + 1)
 #pragma unroll
         for (int ks = 0; ks < kTK / 32; ++ks) {
+            const int r_lo = ks * 32 + 4 * g4, r_hi = r_lo + 16;  // rows of items 0-3, 4-7
             Frag<TIn> bf[Cfg::MST];
 #pragma unroll
             for (int m = 0; m < Cfg::MST; ++m) {
                 const int st = st_w + st_step * m;
                 if (st < Cfg::NST) {
+                    if constexpr (sizeof(TIn) == 2) {
+                        const bf16x4 a = lds_col4(s_b, Cfg::BS, r_lo, st * 16, lane);
+                        const bf16x4 c = lds_col4(s_b, Cfg::BS, r_hi, st * 16, lane);
+                        bf[m].v = __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
+                    } else {
 #pragma unroll
-                    for (int v = 0; v < 8; ++v)
-                        bf[m].v[v] = s_b[(ks * 32 + 4 * v + g4) * Cfg::BS + st * 16 + l16];
+                        for (int v = 0; v < 8; ++v)
+                            bf[m].v[v] = s_b[((v < 4 ? r_lo : r_hi) + (v & 3)) * Cfg::BS +
+                                             st * 16 + l16];
+                    }
                 }
             }
+            const f32x4 w_lo = *(const f32x4*)(s_w + kb * kTK + r_lo);
+            const f32x4 w_hi = *(const f32x4*)(s_w + kb * kTK + r_hi);
 #pragma unroll
             for (int n = 0; n < Cfg::MPT; ++n) {
                 const int pt = pt_w + pt_step * n;
                 float xw[8];
+                if constexpr (sizeof(TIn) == 2) {
+                    const bf16x4 a = lds_col4(s_x, Cfg::XS, r_lo, pt * 16, lane);
+                    const bf16x4 c = lds_col4(s_x, Cfg::XS, r_hi, pt * 16, lane);
 #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    const int r = ks * 32 + 4 * v + g4;
-                    xw[v] = to_f32(s_x[r * Cfg::XS + pt * 16 + l16]) * s_w[kb * kTK + r];
+                    for (int v = 0; v < 4; ++v) {
+                        xw[v] = to_f32(a[v]) * w_lo[v];
+                        xw[v + 4] = to_f32(c[v]) * w_hi[v];
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) {
+                        const int r = (v < 4 ? r_lo : r_hi) + (v & 3);
+                        xw[v] = to_f32(s_x[r * Cfg::XS + pt * 16 + l16]) *
+                                (v < 4 ? w_lo[v & 3] : w_hi[v & 3]);
+                    }
                 }
                 if constexpr (sizeof(TIn) == 2) {
                     Frag<bf16> hi, lo;

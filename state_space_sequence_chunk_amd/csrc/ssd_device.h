@@ -81,6 +81,33 @@ __device__ __forceinline__ float wave_shift_up1(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, false));
 }
 
+// LDS row strides (in elements) chosen against bank conflicts on 64 four-byte banks.
+//  - col_stride: for ds_read_b64_tr_b16 column reads, where the 32 lanes served together
+//    read 8 consecutive rows x 32 bytes: the row stride in words must be an odd multiple
+//    of 8 so those rows land on disjoint 8-bank windows (fp32 tiles, read one element per
+//    lane from rows 4 apart, need a stride of 4 mod 16 words instead).
+//  - row_stride: for 16-byte row reads by 16 lanes of 16 different rows: stride = 4 mod 8
+//    words spreads the rows over disjoint 4-bank windows.
+template <typename T> constexpr int col_stride(int n) {
+    return sizeof(T) == 2 ? (n == 16 ? 16 : n + 16) : n + 4;
+}
+template <typename T> constexpr int row_stride(int n) { return sizeof(T) == 2 ? n + 8 : n + 4; }
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Column read through the gfx950 transposing LDS load (ds_read_b64_tr_b16). Within each
+// group of 16 lanes, lane s supplies the address of 4 consecutive elements and lane j
+// receives element (j & 3) from lanes (j >> 2) + 4k, k = 0..3. Pointing lane s at row
+// r0 + (s >> 2), column c0 + 4 (s & 3) of a row-major matrix therefore hands lane j the
+// column c0 + j of rows r0 .. r0 + 3. r0 may differ between the four 16-lane groups.
+// `base` must be the start of a __shared__ array; ld is its row stride in elements.
+__device__ __forceinline__ bf16x4 lds_col4(const bf16* base, int ld, int r0, int c0, int lane) {
+    const int s = lane & 15;
+    const bf16* p = base + (r0 + (s >> 2)) * ld + c0 + 4 * (s & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(__attribute__((address_space(3))) bf16*)p);
+}
+
 // 16-byte vector type for cooperative global<->LDS copies.
 typedef uint32_t Vec16 __attribute__((ext_vector_type(4)));
 
