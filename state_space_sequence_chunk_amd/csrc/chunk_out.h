@@ -12,16 +12,22 @@
 // --------------
 // One workgroup of T/32 waves handles one (batch, chunk) and a block of NH heads of one
 // B/C group, one head after another:
-//  - B's chunk rows are staged once in LDS (when they fit next to the per-head buffers)
-//    and C's rows of each wave's two 16-row tiles stay in VGPRs; both serve all NH heads.
-//  - Per head, x's chunk rows, the chunk-initial state, G and dt sit in LDS; the next
-//    head's copies are loaded into registers while the current head computes and are
-//    written to LDS after it, so HBM reads overlap the matrix work.
-//  - Wave w owns row tiles w and T/16-1-w, which splits the causal triangle evenly.
-//    For each pair of 16-column tiles it forms S^T = B_j C_i^T on the matrix core
-//    (K = dstate). In that accumulator layout each lane holds one row i and four j's per
-//    tile -- exactly the A-operand layout of y += W x -- so decay, dt_j and the mask are
-//    applied in registers and W is rounded once to the input dtype and used directly.
+//  - Wave w owns row tiles w and T/16-1-w, which splits the causal triangle evenly; C's
+//    rows of those tiles stay in VGPRs for the whole workgroup.
+//  - The interaction tiles S^T = B_j C_i^T (16 x 16, j-tile <= i-tile, K = dstate) do not
+//    depend on the head. When they fit, the workgroup computes them once (B staged in LDS
+//    when it fits too, else read from L2) and keeps them in LDS in the accumulator layout
+//    (each lane reads back its own four values with one 8- or 16-byte load), so every head
+//    reuses them; otherwise each head recomputes them.
+//  - Per head, x's chunk rows, the chunk-initial state, G, dt and u_j = dt_j 2^{G_e - G_j}
+//    (e = last token of j's 16-token tile) sit in LDS; the next head's copies are loaded
+//    into registers while the current head computes and are written to LDS after it, so
+//    HBM reads overlap the matrix work.
+//  - In the S^T accumulator layout each lane holds one row i and four j's per tile --
+//    exactly the A-operand layout of y += W x -- so the decay (2^{G_i - G_e} u_j off the
+//    diagonal, exact with the causal mask on it) is applied in registers and W is rounded
+//    once to the input dtype and used directly; x's token-axis fragments come from the
+//    gfx950 transposing LDS read.
 //  - The carried-state term C_i . S_c (K = dstate) is scaled per row by 2^{G_i}; D x_i
 //    is added and y is written in fp32.
 // The page's operand swap for Blackwell's tensor memory does not apply: gfx950 MFMA takes
@@ -72,6 +78,7 @@ template <typename TIn, typename TS, int P, int S, int T>
 struct OutCfg {
     static constexpr int NW = T / 32, NTHR = 2 * T, NIT = T / 16;
     static constexpr int NPT = P / 16, NKS = (S + 31) / 32;
+    static constexpr int NTILE = NIT * (NIT + 1) / 2;  // lower-triangular 16 x 16 tiles
     static constexpr int XS = col_stride<TIn>(P);   // x rows (read by columns)
     static constexpr int SS = row_stride<TS>(S);    // state rows (read by rows)
     static constexpr int BS = row_stride<TIn>(S);   // B rows (read by rows)
@@ -82,9 +89,21 @@ struct OutCfg {
     static constexpr size_t X_BYTES = (size_t)T * XS * sizeof(TIn);
     static constexpr size_t ST_BYTES = (size_t)P * SS * sizeof(TS);
     static constexpr size_t GD_BYTES = 3 * (size_t)T * sizeof(float);  // G, dt, u
+    static constexpr size_t HEAD_BYTES = X_BYTES + ST_BYTES + GD_BYTES;  // per-head region
     static constexpr size_t B_BYTES = (size_t)T * BS * sizeof(TIn);
-    static constexpr bool B_IN_LDS = X_BYTES + ST_BYTES + GD_BYTES + B_BYTES <= 163840;
-    static constexpr size_t LDS_BYTES = X_BYTES + ST_BYTES + GD_BYTES + (B_IN_LDS ? B_BYTES : 0);
+    static constexpr size_t TILE_BYTES = (size_t)NTILE * 256 * sizeof(TIn);
+    static constexpr size_t LDS_MAX = 163840;
+    // interaction tiles shared by the heads of a workgroup
+    static constexpr bool SHARED = HEAD_BYTES + TILE_BYTES <= LDS_MAX;
+    // B staged in LDS: in SHARED mode only while the tiles are built (over the per-head
+    // region), otherwise next to the per-head region for the whole kernel
+    static constexpr bool B_IN_LDS =
+        SHARED ? (B_BYTES > HEAD_BYTES ? B_BYTES : HEAD_BYTES) + TILE_BYTES <= LDS_MAX
+               : HEAD_BYTES + B_BYTES <= LDS_MAX;
+    static constexpr size_t REGION0 =
+        SHARED ? (B_IN_LDS && B_BYTES > HEAD_BYTES ? B_BYTES : HEAD_BYTES) : HEAD_BYTES;
+    static constexpr size_t LDS_BYTES =
+        SHARED ? REGION0 + TILE_BYTES : HEAD_BYTES + (B_IN_LDS ? B_BYTES : 0);
 };
 
 template <typename TIn, typename TS, int P, int S, int T>
@@ -102,7 +121,9 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     float* s_g = (float*)(smem + Cfg::X_BYTES + Cfg::ST_BYTES);             // [T]
     float* s_dt = s_g + T;                                                  // [T]
     float* s_u = s_dt + T;                                                  // [T]
-    TIn* s_b = (TIn*)(smem + Cfg::X_BYTES + Cfg::ST_BYTES + Cfg::GD_BYTES);  // [T][BS]
+    // B rows: over the per-head region (SHARED, prologue only) or after it
+    TIn* s_b = (TIn*)(smem + (Cfg::SHARED ? 0 : Cfg::HEAD_BYTES));         // [T][BS]
+    TIn* s_tiles = (TIn*)(smem + Cfg::REGION0);                            // [NTILE][64][4]
 
     const int nC = L / T;
     const int nhb = H / NH;
@@ -193,6 +214,38 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             *(Vec16*)(s_b + r * BS + col) = pb[i];
         }
     }
+    // B rows of j-tile jt as the A operand of S^T = B_j C_i^T (lane: row j, 8 dstate values)
+    auto load_bfrag = [&](Frag<TIn>& f, int jt, int ks) {
+        const int s0 = ks * 32 + g4 * 8;
+        if constexpr (Cfg::B_IN_LDS)
+            load8(f, s_b + (jt * 16 + l16) * BS + s0, s0 < S);
+        else
+            load8(f, bg + (size_t)(jt * 16 + l16) * grow + s0, s0 < S);
+    };
+    if constexpr (Cfg::SHARED) {
+        // build this wave's interaction tiles once for all heads of the workgroup
+        if constexpr (Cfg::B_IN_LDS) __syncthreads();
+        const int itmax = its[1];
+        for (int jt = 0; jt <= itmax; ++jt) {
+            f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                Frag<TIn> bfr;
+                load_bfrag(bfr, jt, ks);
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    if (jt <= its[q]) mma(st[q], bfr, cf[q][ks]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (jt > its[q]) continue;
+                TIn* dst = s_tiles + ((size_t)(its[q] * (its[q] + 1) / 2 + jt) * 64 + lane) * 4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[r] = from_f32<TIn>(st[q][r]);
+            }
+        }
+        __syncthreads();  // tiles written; the B rows (if staged) may now be overwritten
+    }
     load_head(h_first);
     store_head();
     __syncthreads();
@@ -234,28 +287,43 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         // 2. within the chunk, two 16-column tiles (32 tokens) per step
         const int itmax = its[1];
         for (int kp = 0; 2 * kp <= itmax; ++kp) {
-            // S^T tiles (rows j of the two column tiles, columns i of both row tiles);
-            // one B fragment is live at a time and feeds both row tiles
+            // S^T tiles (rows j of the two column tiles, columns i of both row tiles)
             f32x4 st[2][2];
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) st[q][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (Cfg::SHARED) {
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int jt = 2 * kp + jj;
-                if (jt > itmax) continue;
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int s0 = ks * 32 + g4 * 8;
-                    Frag<TIn> bfr;
-                    if constexpr (Cfg::B_IN_LDS)
-                        load8(bfr, s_b + (jt * 16 + l16) * BS + s0, s0 < S);
-                    else
-                        load8(bfr, bg + (size_t)(jt * 16 + l16) * grow + s0, s0 < S);
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int jt = 2 * kp + jj;
+                        if (jt > its[q]) continue;
+                        const TIn* src =
+                            s_tiles + ((size_t)(its[q] * (its[q] + 1) / 2 + jt) * 64 + lane) * 4;
+                        if constexpr (sizeof(TIn) == 2) {
+                            const bf16x4 t4 = *(const bf16x4*)src;
 #pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        if (jt <= its[q]) mma(st[q][jj], bfr, cf[q][ks]);
+                            for (int r = 0; r < 4; ++r) st[q][jj][r] = to_f32(t4[r]);
+                        } else {
+                            st[q][jj] = *(const f32x4*)src;
+                        }
+                    }
+            } else {
+                // one B fragment is live at a time and feeds both row tiles
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int jt = 2 * kp + jj;
+                    if (jt > itmax) continue;
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        Frag<TIn> bfr;
+                        load_bfrag(bfr, jt, ks);
+#pragma unroll
+                        for (int q = 0; q < 2; ++q)
+                            if (jt <= its[q]) mma(st[q][jj], bfr, cf[q][ks]);
+                    }
                 }
             }
             // x fragments: slot (g4, v) carries token j = 32kp + 16(v/4) + 4 g4 + v%4,
