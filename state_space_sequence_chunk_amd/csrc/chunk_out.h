@@ -91,7 +91,8 @@ struct OutCfg {
     static constexpr size_t GD_BYTES = 3 * (size_t)T * sizeof(float);  // G, dt, u
     static constexpr size_t HEAD_BYTES = X_BYTES + ST_BYTES + GD_BYTES;  // per-head region
     static constexpr size_t B_BYTES = (size_t)T * BS * sizeof(TIn);
-    static constexpr size_t TILE_BYTES = (size_t)NTILE * 256 * sizeof(TIn);
+    // the tiles plus one all-zero tile that stands in for tiles above the diagonal
+    static constexpr size_t TILE_BYTES = (size_t)(NTILE + 1) * 256 * sizeof(TIn);
     static constexpr size_t LDS_MAX = 163840;
     // interaction tiles shared by the heads of a workgroup
     static constexpr bool SHARED = HEAD_BYTES + TILE_BYTES <= LDS_MAX;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     float* s_u = s_dt + T;                                                  // [T]
     // B rows: over the per-head region (SHARED, prologue only) or after it
     TIn* s_b = (TIn*)(smem + (Cfg::SHARED ? 0 : Cfg::HEAD_BYTES));         // [T][BS]
-    TIn* s_tiles = (TIn*)(smem + Cfg::REGION0);                            // [NTILE][64][4]
+    TIn* s_tiles = (TIn*)(smem + Cfg::REGION0);                            // [NTILE+1][64][4]
 
     const int nC = L / T;
     const int nhb = H / NH;
@@ -133,37 +134,47 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const int b = id / (nhb * nC);
     const int h_first = hb * NH;
     const int g = h_first / (H / ngroups);  // NH divides the heads per group
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T;
-    const size_t xrow = (size_t)H * P;
+    const int HP = H * P;
     const size_t grow = (size_t)ngroups * S;
     const TIn* cg = Cm + (((size_t)b * L + t0) * ngroups + g) * S;
     const TIn* bg = Bm + (((size_t)b * L + t0) * ngroups + g) * S;
     const int its[2] = {wave, Cfg::NIT - 1 - wave};
 
+    // buffer descriptors over this chunk's rows of x and y (all heads), the states and the
+    // per-(batch, head) decay rows; per-head offsets go in the uniform offset operand
+    const BufRsrc rx = make_rsrc(x + ((size_t)b * L + t0) * HP, (uint32_t)(T * HP * sizeof(TIn)));
+    const BufRsrc ry = make_rsrc(y + ((size_t)b * L + t0) * HP, (uint32_t)(T * HP * sizeof(float)));
+    const BufRsrc rst = make_rsrc(states + (size_t)b * H * nC * P * S,
+                                  (uint32_t)((size_t)H * nC * P * S * sizeof(TS)));
+    const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
+    const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
+
     // ---- per-head staging: global -> registers (prefetch) -> LDS ----------------------
     Vec16 px[Cfg::NXV], pst[Cfg::NSV];
     float pg = 0.f, pdt = 0.f, pge = 0.f;
     auto load_head = [&](int h) {
-        const TIn* xg = x + (((size_t)b * L + t0) * H + h) * P;
 #pragma unroll
         for (int i = 0; i < Cfg::NXV; ++i) {
             const int v = tid + i * NTHR;
             const int r = v / (P / VE), col = (v % (P / VE)) * VE;
-            px[i] = *(const Vec16*)(xg + (size_t)r * xrow + col);
+            px[i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(TIn)),
+                               (uint32_t)(h * P * sizeof(TIn)));
         }
-        const TS* sg = states + (((size_t)b * H + h) * nC + c) * (size_t)(P * S);
+        const uint32_t st_off = (uint32_t)(((size_t)h * nC + c) * P * S * sizeof(TS));
 #pragma unroll
         for (int i = 0; i < Cfg::NSV; ++i) {
             const int v = tid + i * NTHR;
-            if (v < P * S / VES) pst[i] = *(const Vec16*)(sg + (size_t)v * VES);
+            if (v < P * S / VES) pst[i] = buf_load16(rst, (uint32_t)(v * 16), st_off);
         }
         if (tid < T) {
-            const size_t o = ((size_t)b * H + h) * L + t0;
-            pg = G[o + tid];
-            pdt = dt_t[o + tid];
-            pge = G[o + (tid | 15)];  // G at the last token of this token's 16-token tile
+            const uint32_t o = (uint32_t)(((size_t)h * L + t0) * sizeof(float));
+            pg = buf_load_f32(rg, tid * 4, o);
+            pdt = buf_load_f32(rdt, tid * 4, o);
+            pge = buf_load_f32(rg, (tid | 15) * 4, o);  // G at the last token of the tile
         }
     };
     auto store_head = [&]() {
@@ -190,7 +201,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         }
     };
 
-    // ---- prologue: C rows (registers), B rows (LDS), first head -----------------------
+    // ---- prologue: C rows (registers), interaction tiles (LDS), first head ------------
     Frag<TIn> cf[2][NKS];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -222,6 +233,10 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         else
             load8(f, bg + (size_t)(jt * 16 + l16) * grow + s0, s0 < S);
     };
+    auto tile_ptr = [&](int q, int jt) {  // this lane's 4 values of tile (its[q], jt)
+        const int k = jt <= its[q] ? its[q] * (its[q] + 1) / 2 + jt : Cfg::NTILE;
+        return s_tiles + ((size_t)k * 64 + lane) * 4;
+    };
     if constexpr (Cfg::SHARED) {
         // build this wave's interaction tiles once for all heads of the workgroup
         if constexpr (Cfg::B_IN_LDS) __syncthreads();
@@ -239,16 +254,29 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 if (jt > its[q]) continue;
-                TIn* dst = s_tiles + ((size_t)(its[q] * (its[q] + 1) / 2 + jt) * 64 + lane) * 4;
+                TIn* dst = tile_ptr(q, jt);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[r] = from_f32<TIn>(st[q][r]);
             }
+        }
+        if (wave == 0) {
+            TIn* z = s_tiles + ((size_t)Cfg::NTILE * 64 + lane) * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[r] = from_f32<TIn>(0.f);
         }
         __syncthreads();  // tiles written; the B rows (if staged) may now be overwritten
     }
     load_head(h_first);
     store_head();
     __syncthreads();
+
+    // y offsets (bytes) of this lane's 8 rows within the chunk, for column l16 of head 0
+    uint32_t yoff[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            yoff[q][r] = (uint32_t)(((its[q] * 16 + 4 * g4 + r) * HP + l16) * sizeof(float));
 
     for (int hh = 0; hh < NH; ++hh) {
         const int h = h_first + hh;
@@ -275,33 +303,31 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
                 }
             }
         }
+        float gi[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < 2; ++q) {
+            gi[q] = s_g[its[q] * 16 + l16];
+            const f32x4 g4v = *(const f32x4*)(s_g + its[q] * 16 + 4 * g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float sc = exp2_fast(s_g[its[q] * 16 + 4 * g4 + r]);
+                const float sc = exp2_fast(g4v[r]);
 #pragma unroll
                 for (int pt = 0; pt < NPT; ++pt) yacc[q][pt][r] *= sc;
             }
+        }
 
         // 2. within the chunk, two 16-column tiles (32 tokens) per step
         const int itmax = its[1];
         for (int kp = 0; 2 * kp <= itmax; ++kp) {
-            // S^T tiles (rows j of the two column tiles, columns i of both row tiles)
+            // S^T tiles (rows j of the two column tiles, columns i of both row tiles);
+            // tiles above the diagonal read as zeros
             f32x4 st[2][2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) st[q][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (Cfg::SHARED) {
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
 #pragma unroll
                     for (int jj = 0; jj < 2; ++jj) {
-                        const int jt = 2 * kp + jj;
-                        if (jt > its[q]) continue;
-                        const TIn* src =
-                            s_tiles + ((size_t)(its[q] * (its[q] + 1) / 2 + jt) * 64 + lane) * 4;
+                        const TIn* src = tile_ptr(q, 2 * kp + jj);
                         if constexpr (sizeof(TIn) == 2) {
                             const bf16x4 t4 = *(const bf16x4*)src;
 #pragma unroll
@@ -311,6 +337,10 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
                         }
                     }
             } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) st[q][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
                 // one B fragment is live at a time and feeds both row tiles
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
@@ -347,51 +377,63 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             for (int q = 0; q < 2; ++q) {
                 const int it = its[q];
                 if (it < 2 * kp) continue;
-                const int i = it * 16 + l16;
-                const float gi = s_g[i];
-                Frag<TIn> wf;
+                float w[8];
+                // off the diagonal every i is past the tile's last token e:
+                // decay = 2^{G_i - G_e} u_j. Above the diagonal the tile is zero and the
+                // clamped exponent keeps the factor finite.
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     const int jt = 2 * kp + jj;
-                    const int j0 = jt * 16 + 4 * g4;  // this lane's four rows j0 .. j0+3
-                    if (jt < it) {
-                        // every i is past the tile's last token e: decay = 2^{G_i - G_e} u_j
-                        const float v = exp2_fast(gi - s_g[jt * 16 + 15]);
-                        const f32x4 u = *(const f32x4*)(s_u + j0);
+                    const float v = exp2_fast(fminf(gi[q] - s_g[jt * 16 + 15], 0.f));
+                    const f32x4 u = *(const f32x4*)(s_u + jt * 16 + 4 * g4);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) wf.v[jj * 4 + r] = from_f32<TIn>(st[q][jj][r] * (v * u[r]));
-                    } else if (jt == it) {
-                        // diagonal tile: exact decay, causal mask by selection
-                        const f32x4 gj = *(const f32x4*)(s_g + j0);
-                        const f32x4 dj = *(const f32x4*)(s_dt + j0);
+                    for (int r = 0; r < 4; ++r) w[jj * 4 + r] = st[q][jj][r] * (v * u[r]);
+                }
+                if ((it >> 1) == kp) {
+                    // the diagonal tile: exact decay with the causal mask, by selection
+                    const int jj = it & 1;
+                    const int i = it * 16 + l16;
+                    const int j0 = it * 16 + 4 * g4;
+                    const f32x4 gj = *(const f32x4*)(s_g + j0);
+                    const f32x4 dj = *(const f32x4*)(s_dt + j0);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float e = exp2_fast(gi - gj[r]) * dj[r];
-                            wf.v[jj * 4 + r] = from_f32<TIn>((i >= j0 + r) ? st[q][jj][r] * e : 0.f);
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) wf.v[jj * 4 + r] = from_f32<TIn>(0.f);
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = exp2_fast(gi[q] - gj[r]) * dj[r];
+                        const float d = (i >= j0 + r) ? st[q][jj][r] * e : 0.f;
+                        if (jj == 0) w[r] = d;
+                        else w[4 + r] = d;
                     }
                 }
+                Frag<TIn> wf;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) wf.v[v] = from_f32<TIn>(w[v]);
 #pragma unroll
                 for (int pt = 0; pt < NPT; ++pt) mma(yacc[q][pt], wf, xf[pt]);
             }
         }
 
-        // 3. skip term and store
+        // 3. skip term and store (x of this lane's rows i by a column read)
         const float dh = Dv ? Dv[h] : 0.f;
-        float* yb = y + (((size_t)b * L + t0) * H + h) * P;
+        const uint32_t yh = (uint32_t)(h * P * sizeof(float));
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int pt = 0; pt < NPT; ++pt)
+            for (int pt = 0; pt < NPT; ++pt) {
+                float xi[4];
+                if constexpr (sizeof(TIn) == 2) {
+                    const bf16x4 x4 = lds_col4(s_x, XS, its[q] * 16 + 4 * g4, pt * 16, lane);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = its[q] * 16 + 4 * g4 + r;
-                    const int p = pt * 16 + l16;
-                    yb[(size_t)i * xrow + p] = yacc[q][pt][r] + dh * to_f32(s_x[i * XS + p]);
+                    for (int r = 0; r < 4; ++r) xi[r] = to_f32(x4[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        xi[r] = s_x[(its[q] * 16 + 4 * g4 + r) * XS + pt * 16 + l16];
                 }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    buf_store_f32(yacc[q][pt][r] + dh * xi[r], ry,
+                                  yoff[q][r] + pt * 16 * (uint32_t)sizeof(float), yh);
+            }
 
         __syncthreads();  // every wave is done with this head's LDS copies
         if (hh + 1 < NH) {

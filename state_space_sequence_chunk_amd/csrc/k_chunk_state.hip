@@ -59,7 +59,8 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
     const int c = (id / H) % nC;
     const int b = id / (H * nC);
     const int g = h / (H / ngroups);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T;
     const size_t bh = (size_t)b * H + h;

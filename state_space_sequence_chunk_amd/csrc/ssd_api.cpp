@@ -40,12 +40,17 @@ ssd_status check_shape(const ssd_shape* s) {
     if (!one_of(s->chunk, {64, 128, 256}) || !one_of(s->headdim, {16, 32, 64, 128}) ||
         !one_of(s->dstate, {16, 32, 64, 128, 256}))
         return SSD_ERR_UNSUPPORTED;
-    // Every element count handed to a kernel must fit in 31 bits of workgroup ids and
-    // in the index arithmetic; reject sizes beyond that rather than overflow.
-    const double states = (double)s->batch * s->nheads * (s->seqlen / s->chunk) * s->headdim *
-                          s->dstate;
+    // Element counts handed to a kernel must fit the 31-bit index arithmetic, and the
+    // per-batch extents the kernels address through buffer descriptors (32-bit byte
+    // counts and offsets) must stay below 2 GiB; reject larger sizes rather than overflow.
+    const double per_batch_states = (double)s->nheads * (s->seqlen / s->chunk) * s->headdim *
+                                    s->dstate * 4.0;
+    const double states = per_batch_states / 4.0 * (double)s->batch;
     const double xs = (double)s->batch * s->seqlen * s->nheads * s->headdim;
-    if (states > 2.0e9 || xs > 2.0e9) return SSD_ERR_UNSUPPORTED;
+    const double per_batch_decay = (double)s->nheads * s->seqlen * 4.0;
+    if (states > 2.0e9 || xs > 2.0e9 || per_batch_states >= 2147483648.0 ||
+        per_batch_decay >= 2147483648.0)
+        return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 

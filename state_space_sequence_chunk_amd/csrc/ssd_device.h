@@ -108,8 +108,29 @@ __device__ __forceinline__ bf16x4 lds_col4(const bf16* base, int ld, int r0, int
         (lds_bf16x4*)(__attribute__((address_space(3))) bf16*)p);
 }
 
+// Buffer-resource addressing: a 128-bit descriptor (base in SGPRs, size in bytes) plus a
+// 32-bit per-lane offset and a 32-bit uniform offset, so loads and stores need no 64-bit
+// per-lane address arithmetic. Accesses at or beyond `bytes` are dropped (stores) or
+// return zero (loads) by the hardware range check. Word 3 = 0x00020000 is the raw 32-bit
+// data format of the gfx9 family.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// The b32 buffer builtins move raw 32-bit patterns (integers); floats are bit-cast.
+__device__ __forceinline__ void buf_store_f32(float v, BufRsrc r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+
 // 16-byte vector type for cooperative global<->LDS copies.
 typedef uint32_t Vec16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Vec16 buf_load16(BufRsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ float buf_load_f32(BufRsrc r, uint32_t voff, uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
 
 // Map a linear workgroup id so that consecutive logical ids run on the same XCD:
 // hardware hands workgroups to the 8 XCDs round-robin, so logical id
