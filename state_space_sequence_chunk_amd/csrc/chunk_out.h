@@ -34,6 +34,8 @@
 // both operands from VGPRs.
 #pragma once
 
+#include <algorithm>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -237,6 +239,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         const int k = jt <= its[q] ? its[q] * (its[q] + 1) / 2 + jt : Cfg::NTILE;
         return s_tiles + ((size_t)k * 64 + lane) * 4;
     };
+    load_head(h_first);  // in flight while the tiles are built
     if constexpr (Cfg::SHARED) {
         // build this wave's interaction tiles once for all heads of the workgroup
         if constexpr (Cfg::B_IN_LDS) __syncthreads();
@@ -266,7 +269,6 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         }
         __syncthreads();  // tiles written; the B rows (if staged) may now be overwritten
     }
-    load_head(h_first);
     store_head();
     __syncthreads();
 
@@ -443,17 +445,20 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     }
 }
 
-// Heads per workgroup: the largest of 8, 5, 4, 2, 1 that divides the heads of a group
-// while leaving at least two workgroup rounds of 8 waves per CU on 256 CUs.
-inline int heads_per_block(const Dims& d) {
+// Heads per workgroup. Each workgroup pays a fixed prologue (C rows, B rows, the
+// interaction tiles), so it should serve as many heads as possible -- but the grid must
+// still cover every CU with as many resident workgroups as fit. Pick the largest divisor
+// of the heads per group whose grid still gives every CU its resident workgroups.
+inline int heads_per_block(const Dims& d, size_t lds_bytes) {
     const int hpg = d.nheads / d.ngroups;
-    const long waves_per_wg = d.chunk / 32;
     const long units = (long)d.batch * d.nchunks() * d.nheads;
-    for (int nh : {8, 5, 4, 2}) {
-        if (hpg % nh) continue;
-        if ((units / nh) * waves_per_wg >= 256L * 16) return nh;
-    }
-    return 1;
+    const long per_cu = std::max<long>(1, std::min<long>(163840 / (long)std::max<size_t>(lds_bytes, 1),
+                                                         32 / (d.chunk / 32)));
+    const long want = 256L * per_cu;  // workgroups that fill 256 CUs once
+    int best = 1;
+    for (int nh = 1; nh <= hpg; ++nh)
+        if (hpg % nh == 0 && units / nh >= want) best = nh;
+    return best;
 }
 
 template <typename TIn, typename TS, int P, int S, int T>
@@ -468,7 +473,7 @@ hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G
                                            (int)Cfg::LDS_BYTES);
         if (e != hipSuccess) return e;
     }
-    const int nh = heads_per_block(d);
+    const int nh = heads_per_block(d, Cfg::LDS_BYTES);
     const int nblocks = d.batch * d.nchunks() * (d.nheads / nh);
     kern<<<nblocks, 2 * T, Cfg::LDS_BYTES, stream>>>((const TIn*)x, (const TIn*)Bm,
                                                      (const TIn*)Cm, G, dt_t,
