@@ -392,18 +392,24 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
                     for (int r = 0; r < 4; ++r) w[jj * 4 + r] = st[q][jj][r] * (v * u[r]);
                 }
                 if ((it >> 1) == kp) {
-                    // the diagonal tile: exact decay with the causal mask, by selection
-                    const int jj = it & 1;
+                    // the diagonal tile (the first of the pair when it is even): exact decay
+                    // with the causal mask, by selection
+                    const bool lo = (it & 1) == 0;
                     const int i = it * 16 + l16;
                     const int j0 = it * 16 + 4 * g4;
                     const f32x4 gj = *(const f32x4*)(s_g + j0);
                     const f32x4 dj = *(const f32x4*)(s_dt + j0);
+                    f32x4 e4;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float e = exp2_fast(gi[q] - gj[r]) * dj[r];
-                        const float d = (i >= j0 + r) ? st[q][jj][r] * e : 0.f;
-                        if (jj == 0) w[r] = d;
-                        else w[4 + r] = d;
+                    for (int r = 0; r < 4; ++r) e4[r] = exp2_fast(gi[q] - gj[r]) * dj[r];
+                    if (lo) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            w[r] = (i >= j0 + r) ? st[q][0][r] * e4[r] : 0.f;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            w[4 + r] = (i >= j0 + r) ? st[q][1][r] * e4[r] : 0.f;
                     }
                 }
                 Frag<TIn> wf;
