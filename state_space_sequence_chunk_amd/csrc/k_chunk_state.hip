@@ -1,4 +1,5 @@
-// Stage 2a: each chunk's own contribution to the state that leaves it.
+// Stage 2a: each chunk's own contribution to the state that leaves it (one workgroup per
+// (batch, chunk, head); the multi-head form in chunk_state_mh.h is preferred when it fits).
 //
 // Page "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA CUDA
 // Tile", section "Mamba-2 architecture" (the log-space jump formula) and section
@@ -260,9 +261,21 @@ static hipError_t state_by_p(const void* x, const void* Bm, const float* A, cons
     return hipErrorInvalidValue;
 }
 
+bool launch_chunk_state_mh_bf16(const void*, const void*, const float*, const float*, float*,
+                                const Dims&, hipStream_t, hipError_t*);
+bool launch_chunk_state_mh_f32(const void*, const void*, const float*, const float*, float*,
+                               const Dims&, hipStream_t, hipError_t*);
+
+// The multi-head form (B rows staged once per workgroup, x double-buffered per head) is
+// used whenever its LDS plan fits; otherwise one workgroup per (batch, chunk, head).
 hipError_t launch_chunk_state(int in_dtype, const void* x, const void* Bm, const float* A,
                               const float* dt_t, float* dS, const Dims& d, hipStream_t stream) {
-    if (in_dtype == kBF16) return state_by_p<bf16>(x, Bm, A, dt_t, dS, d, stream);
+    hipError_t err = hipSuccess;
+    if (in_dtype == kBF16) {
+        if (launch_chunk_state_mh_bf16(x, Bm, A, dt_t, dS, d, stream, &err)) return err;
+        return state_by_p<bf16>(x, Bm, A, dt_t, dS, d, stream);
+    }
+    if (launch_chunk_state_mh_f32(x, Bm, A, dt_t, dS, d, stream, &err)) return err;
     return state_by_p<float>(x, Bm, A, dt_t, dS, d, stream);
 }
 
