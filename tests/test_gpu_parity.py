@@ -52,6 +52,27 @@ def test_cumsum_stage(name):
     assert torch.equal(dt_t.cpu(), cpu["dt"].float().permute(0, 2, 1))
 
 
+# Head counts that take the kernel's other load paths: bf16 with heads not a multiple of
+# 8 and fp32 with heads not a multiple of 4 (element loads), and enough chunks with many
+# heads that a block holds the maximum 56 heads and the last block only 16.
+@pytest.mark.parametrize("dtype,batch,seqlen,nheads,chunk", [
+    ("bf16", 2, 256, 12, 64), ("fp32", 1, 512, 6, 128), ("fp32", 2, 1024, 24, 256),
+    ("bf16", 1, 16384, 72, 64)])
+def test_cumsum_head_blocks(dtype, batch, seqlen, nheads, chunk):
+    w = gen.Workload("cumsum-shape", batch, seqlen, nheads, 16, 16, 1, chunk, dtype, False, 77)
+    cpu, d = make(w)
+    sh = ssd.shape_of(d["x"], d["B"], chunk)
+    G = torch.empty((batch, nheads, seqlen), dtype=torch.float32, device="cuda")
+    dt_t = torch.empty_like(G)
+    ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dt_t)
+    torch.cuda.synchronize()
+    ref = oracle.chunk_cumsum_log2(cpu["dt"], cpu["A"], chunk)
+    err = np.abs(np64(G) - ref) / (1.0 + np.abs(ref))
+    _print(f"{dtype} b{batch} L{seqlen} H{nheads} T{chunk}: max |dG|/(1+|G|) = {err.max():.2e}")
+    assert err.max() < 1e-5
+    assert torch.equal(dt_t.cpu(), cpu["dt"].float().permute(0, 2, 1))
+
+
 # --- stage 2 --------------------------------------------------------------------------
 @pytest.mark.parametrize("states", ["same", "fp32"])
 @pytest.mark.parametrize("name", list(SMALL))
