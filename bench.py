@@ -3,16 +3,20 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step is one pass of the whole forward pass (cumulative decay, chunk states, carry,
-chunk output) over one batch of seeded synthetic input already resident in HBM. The
-timed steps call the C ABI's three stage entry points in order on one stream with HIP
-events between them, which gives each stage's duration over the timed region; the
-one-call ssd_forward path is timed the same way for comparison. Prints one JSON line.
+chunk output) over one batch of seeded synthetic input already resident in HBM, made by
+one call of the C ABI's ssd_forward. The timed region is K such steps on one stream,
+bracketed by device synchronisation and timed with HIP events; `value` is tokens per
+second over it. A second region runs the same K steps through the three stage entry
+points with HIP events between them on the launch stream, which gives each stage's
+average duration for the roofline figures. Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -49,6 +53,34 @@ def algorithmic(w):
         "chunk_out": B * nC * H * (2.0 * T * T * S + 2.0 * T * S * P + 2.0 * T * T * P),
     }
     return by, fl
+
+
+# Sources of the chunk-output kernel; the HBM traffic measured with rocprofv3 counters
+# is reported only while they are unchanged since the counters were taken.
+CHUNK_OUT_SOURCES = ("chunk_out.h", "k_chunk_out.cpp", "k_chunk_out_bf16.hip",
+                     "k_chunk_out_bf16_f32.hip", "k_chunk_out_f32.hip", "ssd_device.h")
+
+
+def sources_sha256(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "state_space_sequence_chunk_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per chunk_out launch from the committed counter summary, or None when
+    there is none for this workload or the kernel changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"chunk_out_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_h = re.search(r"^sources_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != sources_sha256(CHUNK_OUT_SOURCES):
+        return None
+    return int(m_b.group(1))
 
 
 def cpu_baseline(w, cpu, budget_s=15.0):
@@ -115,7 +147,12 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (3 times); "
                          "used to calibrate the HBM byte counters")
+    ap.add_argument("--sources-sha256", action="store_true",
+                    help="print the hash of the chunk-output kernel sources and exit")
     args = ap.parse_args()
+    if args.sources_sha256:
+        print(sources_sha256(CHUNK_OUT_SOURCES))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
               "layout of this path is a design note, not a measured configuration.",
@@ -167,35 +204,39 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    def forward_step():
         fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], stream)
+
+    for _ in range(args.warmup):
+        forward_step()
+        step()
     torch.cuda.synchronize()
 
+    # timed region: K one-call forward steps
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        forward_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / K
+
+    # per-stage region: the same K steps through the stage entry points, events between
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
     for k in range(K):
         step(evs[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    span_ms = evs[0][0].elapsed_time(evs[-1][3])
     stage_ms = {"cumsum": 0.0, "state_pass": 0.0, "chunk_out": 0.0}
     for e in evs:
         stage_ms["cumsum"] += e[0].elapsed_time(e[1]) / K
         stage_ms["state_pass"] += e[1].elapsed_time(e[2]) / K
         stage_ms["chunk_out"] += e[2].elapsed_time(e[3]) / K
-    ms_per_step = span_ms / K
-
-    # the one-call entry point, same kernels, timed the same way
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(K):
-        fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_forward = e0.elapsed_time(e1) / K
+    ms_staged = evs[0][0].elapsed_time(evs[-1][3]) / K
 
     by, fl = algorithmic(w)
     kernels = {
@@ -214,7 +255,8 @@ def main():
     co["eff_mfma_frac"] = co["eff_TFLOPs"] / peak_tf
     dom = "chunk_out"
     roofline = {"bound": "hbm", "achieved": kernels[dom]["GBps"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": kernels[dom]["GBps"] / HBM_PEAK_GBS, "traffic": None,
+                "unit": "GB/s", "frac": kernels[dom]["GBps"] / HBM_PEAK_GBS,
+                "traffic": measured_traffic(w.name),
                 "kernel": "chunk_out_kernel",
                 "bytes_per_launch": kernels[dom]["bytes"]}
 
@@ -234,7 +276,7 @@ def main():
         "config": w.describe(),
         "roofline": roofline,
         "kernels": kernels,
-        "ms_per_step_ssd_forward": ms_forward,
+        "ms_per_step_staged": ms_staged,
         "copy_GBps": copy_gbps,
         "wall_ms_per_step": wall / K * 1e3,
     }
