@@ -137,6 +137,41 @@ def measure_copy_bandwidth(torch, nbytes=1 << 30, reps=10):
     return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
+def time_decode(torch, ssd, d, state, stream, steps=32, replays=8):
+    """Average duration of one recurrent decode step on the workload's final state (all
+    batches and heads, one token): `steps` launches captured in a HIP graph and replayed,
+    so the figure is device time rather than Python launch time. The state is updated in
+    place at every step. Algorithmic bytes: the fp32 state read and written, plus the
+    token's x, dt, B, C and y."""
+    x, dt, Bm, Cm = d["x"][:, 0].contiguous(), d["dt"][:, 0].contiguous(), \
+        d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous()
+    st = state.clone()
+    b, H, P = x.shape
+    y = torch.empty((b, H, P), dtype=torch.float32, device=x.device)
+    sh = ssd.make_shape(b, 1, H, P, Bm.shape[2], Bm.shape[1], 1, x.dtype, torch.float32)
+    for _ in range(3):
+        ssd.ssd_decode_step(sh, x, dt, d["A"], Bm, Cm, d["D"], st, y, stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream()
+        for _ in range(steps):
+            ssd.ssd_decode_step(sh, x, dt, d["A"], Bm, Cm, d["D"], st, y, cs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (steps * replays)
+    e = x.element_size()
+    nbytes = (2 * st.numel() * 4 + x.numel() * e + dt.numel() * e + 2 * Bm.numel() * e
+              + y.numel() * 4)
+    return {"ms": ms, "bytes": nbytes, "graph_steps": steps * replays}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +273,11 @@ def main():
         stage_ms["chunk_out"] += e[2].elapsed_time(e[3]) / K
     ms_staged = evs[0][0].elapsed_time(evs[-1][3]) / K
 
+    try:
+        decode = time_decode(torch, ssd, d, fin, stream)
+    except Exception as exc:  # reported, never silently replaced
+        decode = {"error": f"{type(exc).__name__}: {exc}"}
+
     by, fl = algorithmic(w)
     kernels = {
         "cumsum": {"ms": stage_ms["cumsum"], "bytes": by["cumsum"]},
@@ -246,7 +286,10 @@ def main():
         "chunk_out": {"ms": stage_ms["chunk_out"], "bytes": by["chunk_out"],
                       "flops_per_head_dense": fl["chunk_out"]},
     }
+    kernels["decode_step"] = decode
     for k, v in kernels.items():
+        if "ms" not in v:
+            continue
         v["GBps"] = v["bytes"] / (v["ms"] * 1e-3) / 1e9
         v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
     co = kernels["chunk_out"]

@@ -134,6 +134,30 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
                        float* final_state, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * Recurrent decode step (section "Mamba-2 architecture": the recurrent form, which takes
+ * one token at a time with a state of fixed size, the form the page names for sequential
+ * inference). For each batch b and head h (g = h / (nheads/ngroups)), on the fp32 state
+ * that ssd_forward returns as its final state:
+ *     state[b,h] <- exp(A[h] dt[b,h]) state[b,h] + dt[b,h] x[b,h]^T (outer) B[b,g]
+ *     y[b,h]      = state[b,h] . C[b,g] + D[h] x[b,h]      (reads the updated state)
+ * so a prompt prefilled by ssd_forward (final_state) continues here token by token, and
+ * a sequence split at any token gives the same result as one pass.
+ * Shape: seqlen must be 1 (else SSD_ERR_SHAPE); chunk and states_dtype are not used.
+ * Layouts (the [batch, 1, ...] slices of the forward pass's layouts):
+ *     x        [batch, nheads, headdim]          in_dtype
+ *     dt       [batch, nheads]                   in_dtype
+ *     B, C     [batch, ngroups, dstate]          in_dtype
+ *     A, D     [nheads]                          fp32 (D may be NULL)
+ *     state    [batch, nheads, headdim, dstate]  fp32, read and updated in place
+ *     y        [batch, nheads, headdim]          fp32
+ * state must not alias any other argument. Errors and execution as for the other entry
+ * points (validation before any launch; asynchronous on `stream`).
+ */
+ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, float* state, float* y,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,20 @@ ssd_status check_shape(const ssd_shape* s) {
     return SSD_OK;
 }
 
+// Shape check of the decode step: one token, the forward pass's head, group and dtype
+// rules; chunk and states_dtype are not used.
+ssd_status check_decode_shape(const ssd_shape* s) {
+    if (!s) return SSD_ERR_NULL;
+    if (s->batch < 1 || s->seqlen != 1 || s->nheads < 1 || s->headdim < 1 || s->dstate < 1 ||
+        s->ngroups < 1 || s->nheads % s->ngroups != 0)
+        return SSD_ERR_SHAPE;
+    if (s->in_dtype != SSD_F32 && s->in_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (!one_of(s->headdim, {16, 32, 64, 128}) || !one_of(s->dstate, {16, 32, 64, 128, 256}))
+        return SSD_ERR_UNSUPPORTED;
+    if ((double)s->batch * s->nheads * s->headdim * s->dstate > 2.0e9) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
 Dims dims_of(const ssd_shape* s) {
     Dims d;
     d.batch = (int)s->batch;
@@ -197,6 +211,19 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
     if (e != hipSuccess) return SSD_ERR_HIP;
     return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype, x, B, C, G,
                                             dt_t, states, D, y, d, s));
+}
+
+ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, float* state, float* y,
+                           void* stream) {
+    ssd_status st = check_decode_shape(shape);
+    if (st != SSD_OK) return st;
+    SSD_REQUIRE(x && dt && A && B && C && state && y, SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(dt) && aligned16(A) && aligned16(B) && aligned16(C) &&
+                    aligned16(D) && aligned16(state) && aligned16(y),
+                SSD_ERR_ALIGN);
+    return hip_status(ssd::launch_decode(shape->in_dtype, x, dt, A, B, C, D, state, y,
+                                         dims_of(shape), (hipStream_t)stream));
 }
 
 }  // extern "C"

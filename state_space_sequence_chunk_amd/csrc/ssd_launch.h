@@ -26,6 +26,11 @@ hipError_t launch_state_carry(int states_dtype, const float* dstate_chunks, cons
                               const float* h0, void* states, float* final_state, const Dims& d,
                               hipStream_t stream);
 
+// One recurrent step on a carried fp32 state (in place), y for that token.
+hipError_t launch_decode(int in_dtype, const void* x, const void* dt, const float* A,
+                         const void* Bm, const void* Cm, const float* D, float* state, float* y,
+                         const Dims& d, hipStream_t stream);
+
 hipError_t launch_chunk_out(int in_dtype, int states_dtype, const void* x, const void* Bm,
                             const void* Cm, const float* G, const float* dt_t, const void* states,
                             const float* D, float* y, const Dims& d, hipStream_t stream);

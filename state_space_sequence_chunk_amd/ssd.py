@@ -22,7 +22,7 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE"
 # Entry points declared in include/ssd.h.
 EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_bytes",
            "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
-           "ssd_chunk_out", "ssd_forward")
+           "ssd_chunk_out", "ssd_forward", "ssd_decode_step")
 
 
 class SSDError(RuntimeError):
@@ -64,6 +64,7 @@ def load_library():
     lib.ssd_state_pass.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_chunk_out.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -157,6 +158,23 @@ def ssd_forward(shape, x, dt, A, B, C, D, h0, y, final_state, workspace, stream=
     _check(load_library().ssd_forward(ctypes.byref(shape), _p(x), _p(dt), _p(A), _p(B), _p(C),
                                       _p(D), _p(h0), _p(y), _p(final_state), _p(workspace),
                                       nbytes, _stream(stream)), "ssd_forward")
+
+
+def ssd_decode_step(shape, x, dt, A, B, C, D, state, y, stream=None):
+    _check(load_library().ssd_decode_step(ctypes.byref(shape), _p(x), _p(dt), _p(A), _p(B),
+                                          _p(C), _p(D), _p(state), _p(y), _stream(stream)),
+           "ssd_decode_step")
+
+
+def decode_step(x, dt, A, B, C, D, state, *, stream=None):
+    """One token for every (batch, head): x [b, h, P], dt [b, h], B/C [b, g, S]; `state`
+    (fp32 [b, h, P, S], e.g. ssd_forward's final state) is updated in place. Returns y
+    (fp32 [b, h, P])."""
+    b, H, P = x.shape
+    sh = make_shape(b, 1, H, P, B.shape[2], B.shape[1], 1, x.dtype, torch.float32)
+    y = torch.empty((b, H, P), dtype=torch.float32, device=x.device)
+    ssd_decode_step(sh, x, dt, A, B, C, D, state, y, stream)
+    return y
 
 
 class Forward:

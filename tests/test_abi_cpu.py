@@ -112,6 +112,30 @@ def test_stage_entry_points_reject_before_launch():
     assert lib.ssd_chunk_out(ctypes.byref(s), f, f, f, f, f, f, _v(FAKE + 2), f, None) == 6
 
 
+def test_decode_step_rejects_before_launch():
+    lib = ssd.load_library()
+    f = _v(FAKE)
+    args = [f] * 8  # x dt A B C D state y
+    ok = shape(seqlen=1)
+    # a valid call would launch: only the rejecting cases are called here
+    assert lib.ssd_decode_step(ctypes.byref(shape()), *args, None) == 2  # seqlen != 1
+    assert lib.ssd_decode_step(ctypes.byref(shape(seqlen=1, ngroups=3)), *args, None) == 2
+    assert lib.ssd_decode_step(ctypes.byref(shape(seqlen=1, in_dtype=9)), *args, None) == 3
+    assert lib.ssd_decode_step(ctypes.byref(shape(seqlen=1, headdim=48)), *args, None) == 4
+    assert lib.ssd_decode_step(ctypes.byref(shape(seqlen=1, dstate=512)), *args, None) == 4
+    bad = list(args)
+    bad[6] = None  # state
+    assert lib.ssd_decode_step(ctypes.byref(ok), *bad, None) == 1
+    bad = list(args)
+    bad[5] = None  # D is optional: still fails later on the misaligned y only
+    bad[7] = _v(FAKE + 4)
+    assert lib.ssd_decode_step(ctypes.byref(ok), *bad, None) == 6
+    assert lib.ssd_decode_step(None, *args, None) == 1
+    # chunk and states_dtype are not used by the decode step
+    assert lib.ssd_decode_step(ctypes.byref(shape(seqlen=1, chunk=7, states_dtype=5)),
+                               *[None] * 8, None) == 1
+
+
 def test_status_strings():
     lib = ssd.load_library()
     for code in range(8):
