@@ -22,7 +22,14 @@
  *        G, dt_t  [batch, nheads, seqlen]                 fp32 (head-major, tokens fastest)
  *        states   [batch, nheads, nchunks, headdim, dstate]   states_dtype
  *        y        [batch, seqlen, nheads, headdim]        fp32
- *    with nchunks = seqlen / chunk.
+ *    with nchunks = ceil(seqlen / chunk).
+ *  - Lengths: any seqlen >= 0. A last chunk shorter than `chunk` is processed as if it
+ *    were padded with zero tokens (dt = 0, x = B = C = 0), which is the page's own padding
+ *    (section "Kernel 1: Computing cumulative sums") and leaves the result of every real
+ *    token unchanged; only the real tokens' outputs are written. seqlen = 0 is an empty
+ *    sequence: nothing is read or written except final_state, which receives h0 (zeros
+ *    when h0 is NULL); the tensors with a seqlen extent (and a zero-byte workspace) may
+ *    then be NULL.
  *  - Ownership: the caller allocates and frees every buffer, including the workspace.
  *    The library never allocates device memory, keeps no pointer after returning and
  *    holds no global state, so concurrent calls on different buffers are safe.
@@ -33,8 +40,7 @@
  *    invalid call returns a non-zero ssd_status and touches no memory. A failed launch
  *    returns SSD_ERR_HIP. No call aborts the process or throws.
  *  - Supported sizes: chunk in {64, 128, 256}; headdim in {16, 32, 64, 128};
- *    dstate in {16, 32, 64, 128, 256}; seqlen a positive multiple of chunk;
- *    nheads a multiple of ngroups; in_dtype and states_dtype in {SSD_F32, SSD_BF16},
+ *    dstate in {16, 32, 64, 128, 256}; nheads a multiple of ngroups; in_dtype and states_dtype in {SSD_F32, SSD_BF16},
  *    except fp32 inputs with bf16 states (SSD_ERR_UNSUPPORTED: it would only lose the
  *    precision the fp32 inputs ask for).
  */
@@ -51,7 +57,7 @@ extern "C" {
 typedef enum ssd_status {
     SSD_OK = 0,
     SSD_ERR_NULL = 1,        /* a required pointer is NULL */
-    SSD_ERR_SHAPE = 2,       /* a size < 1, nheads % ngroups != 0, or seqlen % chunk != 0 */
+    SSD_ERR_SHAPE = 2,       /* a size < 1 (seqlen < 0), or nheads % ngroups != 0 */
     SSD_ERR_DTYPE = 3,       /* a dtype code that is neither SSD_F32 nor SSD_BF16 */
     SSD_ERR_UNSUPPORTED = 4, /* chunk, headdim, dstate or dtype pair outside the supported sets */
     SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
@@ -97,7 +103,7 @@ ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float*
  * The state entering chunk c+1 is
  *     S_{c+1} = 2^{G_last} S_c + sum_{j in chunk c} dt_j 2^{G_last - G_j} x_j^T (outer) B_j
  * (stored P x S), starting from S_0 = h0 (zeros when h0 is NULL); G_last is G at the
- * chunk's last token, and the exponent G_last - G_j = log2(e) * sum_{k=j+1}^{last} A dt_k
+ * chunk's last (real) token, and the exponent G_last - G_j = log2(e) * sum_{k=j+1}^{last} A dt_k
  * is summed from the chunk's end (hence A is an input), which keeps its rounding error
  * relative to the exponents that dominate the state.
  * Outputs: states[b,h,c] = S_c for every chunk c (states_dtype), and, when final_state

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     TIn* s_b = (TIn*)(smem + (Cfg::SHARED ? 0 : Cfg::HEAD_BYTES));         // [T][BS]
     TIn* s_tiles = (TIn*)(smem + Cfg::REGION0);                            // [NTILE+1][64][4]
 
-    const int nC = L / T;
+    const int nC = (L + T - 1) / T;
     const int nhb = H / NH;
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int hb = id % nhb;
@@ -140,6 +140,9 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T;
+    // real tokens of this chunk; a partial last chunk is computed as if padded with zero
+    // tokens (dt = 0 keeps G at its last real value), and its padded rows are not stored
+    const int rows = min(T, L - t0);
     const int HP = H * P;
     const size_t grow = (size_t)ngroups * S;
     const TIn* cg = Cm + (((size_t)b * L + t0) * ngroups + g) * S;
@@ -148,8 +151,10 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
 
     // buffer descriptors over this chunk's rows of x and y (all heads), the states and the
     // per-(batch, head) decay rows; per-head offsets go in the uniform offset operand
-    const BufRsrc rx = make_rsrc(x + ((size_t)b * L + t0) * HP, (uint32_t)(T * HP * sizeof(TIn)));
-    const BufRsrc ry = make_rsrc(y + ((size_t)b * L + t0) * HP, (uint32_t)(T * HP * sizeof(float)));
+    // (x and y rows past the real tokens lie outside these descriptors: loads return zeros
+    // and stores are dropped)
+    const BufRsrc rx = make_rsrc(x + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(TIn)));
+    const BufRsrc ry = make_rsrc(y + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(float)));
     const BufRsrc rst = make_rsrc(states + (size_t)b * H * nC * P * S,
                                   (uint32_t)((size_t)H * nC * P * S * sizeof(TS)));
     const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
@@ -174,9 +179,9 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         }
         if (tid < T) {
             const uint32_t o = (uint32_t)(((size_t)h * L + t0) * sizeof(float));
-            pg = buf_load_f32(rg, tid * 4, o);
-            pdt = buf_load_f32(rdt, tid * 4, o);
-            pge = buf_load_f32(rg, (tid | 15) * 4, o);  // G at the last token of the tile
+            pg = buf_load_f32(rg, min(tid, rows - 1) * 4, o);
+            pdt = tid < rows ? buf_load_f32(rdt, tid * 4, o) : 0.f;
+            pge = buf_load_f32(rg, min(tid | 15, rows - 1) * 4, o);  // G at the tile's last token
         }
     };
     auto store_head = [&]() {
@@ -210,7 +215,8 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int s0 = ks * 32 + g4 * 8;
-            load8(cf[q][ks], cg + (size_t)(its[q] * 16 + l16) * grow + s0, s0 < S);
+            load8(cf[q][ks], cg + (size_t)(its[q] * 16 + l16) * grow + s0,
+                  s0 < S && its[q] * 16 + l16 < rows);
         }
     if constexpr (Cfg::B_IN_LDS) {
         Vec16 pb[Cfg::NBV];
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         for (int i = 0; i < Cfg::NBV; ++i) {
             const int v = tid + i * NTHR;
             const int r = v / (S / VE), col = (v % (S / VE)) * VE;
-            pb[i] = *(const Vec16*)(bg + (size_t)r * grow + col);
+            pb[i] = r < rows ? *(const Vec16*)(bg + (size_t)r * grow + col) : Vec16{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int i = 0; i < Cfg::NBV; ++i) {
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         if constexpr (Cfg::B_IN_LDS)
             load8(f, s_b + (jt * 16 + l16) * BS + s0, s0 < S);
         else
-            load8(f, bg + (size_t)(jt * 16 + l16) * grow + s0, s0 < S);
+            load8(f, bg + (size_t)(jt * 16 + l16) * grow + s0, s0 < S && jt * 16 + l16 < rows);
     };
     auto tile_ptr = [&](int q, int jt) {  // this lane's 4 values of tile (its[q], jt)
         const int k = jt <= its[q] ? its[q] * (its[q] + 1) / 2 + jt : Cfg::NTILE;

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(512) void chunk_state_mh_kernel(
         return (float*)(smem + Cfg::B_BYTES + k * (Cfg::X_BYTES + Cfg::W_BYTES) + Cfg::X_BYTES);
     };
 
-    const int nC = L / T;
+    const int nC = (L + T - 1) / T;
     const int nhb = H / NH;
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int hb = id % nhb;
@@ -70,12 +70,14 @@ __global__ __launch_bounds__(512) void chunk_state_mh_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T;
+    const int rows = min(T, L - t0);  // real tokens of this chunk; the rest count as zeros
     const int HP = H * P;
     const int pt = wave / Cfg::WPT;          // this wave's p-tile
     const int st0 = wave % Cfg::WPT;         // first s-tile; stride WPT
     const bool active = pt < Cfg::NPT;
 
-    const BufRsrc rx = make_rsrc(x + ((size_t)b * L + t0) * HP, (uint32_t)(T * HP * sizeof(TIn)));
+    // x rows past the chunk's real tokens lie outside the descriptor and load as zeros
+    const BufRsrc rx = make_rsrc(x + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(TIn)));
     const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
     const BufRsrc rds = make_rsrc(dS + (size_t)b * H * nC * P * S,
                                   (uint32_t)((size_t)H * nC * P * S * sizeof(float)));
@@ -96,7 +98,10 @@ __global__ __launch_bounds__(512) void chunk_state_mh_kernel(
         if (wave == 0) {  // wave 0 scans the head's decay; lane holds tokens T-1-(PER*lane+k)
             const uint32_t o = (uint32_t)(((size_t)h * L + t0) * sizeof(float));
 #pragma unroll
-            for (int k = 0; k < PER; ++k) pdt[k] = buf_load_f32(rdt, (T - 1 - (PER * lane + k)) * 4, o);
+            for (int k = 0; k < PER; ++k) {
+                const int t = T - 1 - (PER * lane + k);
+                pdt[k] = t < rows ? buf_load_f32(rdt, t * 4, o) : 0.f;
+            }
         }
     };
     auto store_head = [&](int h, int kb) {
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(512) void chunk_state_mh_kernel(
             const int v = tid + i * NTHR;
             if (v < T * S / VE) {
                 const int r = v / (S / VE), col = (v % (S / VE)) * VE;
-                pb[i] = *(const Vec16*)(bg + (size_t)r * grow + col);
+                pb[i] = r < rows ? *(const Vec16*)(bg + (size_t)r * grow + col) : Vec16{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
     __shared__ __attribute__((aligned(16))) TIn s_x[kTK * Cfg::XS];
     __shared__ __attribute__((aligned(16))) TIn s_b[kTK * Cfg::BS];
 
-    const int nC = L / T;
+    const int nC = (L + T - 1) / T;
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int h = id % H;
     const int c = (id / H) % nC;
@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T;
+    const int rows = min(T, L - t0);  // real tokens of this chunk; the rest count as zeros
     const size_t bh = (size_t)b * H + h;
 
     // w_j = dt_j * 2^{log2(e) * sum_{k=j+1}^{T-1} A dt_k}: the decay from token j to the end
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
         const float* dc = dt_t + bh * L + t0;
         const float ah = A[h];
         const int t = T - 1 - tid;
-        const float dtv = tid < T ? dc[t] : 0.f;
+        const float dtv = tid < T && t < rows ? dc[t] : 0.f;
         const float a = ah * dtv;
         const float incl = wave_inclusive_scan(a);
         const float excl = wave_shift_up1(incl);
@@ -97,14 +98,18 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(const TIn* __restrict_
             const int v = tid + i * 256;                                                  \
             if (v < Cfg::XVEC) {                                                          \
                 const int r = v / (P / Cfg::VE), col = (v % (P / Cfg::VE)) * Cfg::VE;     \
-                xr[i] = *(const Vec16*)(xg + (size_t)((kb) * kTK + r) * xrow + col);      \
+                const int tr = (kb) * kTK + r;                                            \
+                xr[i] = tr < rows ? *(const Vec16*)(xg + (size_t)tr * xrow + col)         \
+                                  : Vec16{0u, 0u, 0u, 0u};                                \
             }                                                                             \
         }                                                                                 \
         _Pragma("unroll") for (int i = 0; i < Cfg::BPT; ++i) {                            \
             const int v = tid + i * 256;                                                  \
             if (v < Cfg::BVEC) {                                                          \
                 const int r = v / (S / Cfg::VE), col = (v % (S / Cfg::VE)) * Cfg::VE;     \
-                br[i] = *(const Vec16*)(bg + (size_t)((kb) * kTK + r) * brow + col);      \
+                const int tr = (kb) * kTK + r;                                            \
+                br[i] = tr < rows ? *(const Vec16*)(bg + (size_t)tr * brow + col)         \
+                                  : Vec16{0u, 0u, 0u, 0u};                                \
             }                                                                             \
         }                                                                                 \
     }

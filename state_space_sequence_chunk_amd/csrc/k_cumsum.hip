@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kCumsumThreads) void cumsum_kernel(
     const int h0 = blockIdx.y * hb;
     const int nh = min(hb, H - h0);
     const int t0 = c * T;
+    const int rows = min(T, L - t0);  // real tokens; a partial last chunk is zero-padded
     const int groups = nh / VW;  // vectors per token row (nh % VW == 0 by the host plan)
     const int nvec = T * groups;
     const TIn* src = dt + ((size_t)b * L + t0) * H + h0;
@@ -66,7 +67,8 @@ __global__ __launch_bounds__(kCumsumThreads) void cumsum_kernel(
                 const int e = base + k * kCumsumThreads;
                 if (e < nvec) {
                     const int t = e / groups, gi = e - t * groups;
-                    v[k] = *(const Vec16*)(src + (size_t)t * H + gi * VW);
+                    v[k] = t < rows ? *(const Vec16*)(src + (size_t)t * H + gi * VW)
+                                    : Vec16{0u, 0u, 0u, 0u};
                 }
             }
 #pragma unroll
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(kCumsumThreads) void cumsum_kernel(
                 const int e = base + k * kCumsumThreads;
                 if (e < nvec) {
                     const int t = e / groups;
-                    v[k] = to_f32(src[(size_t)t * H + (e - t * groups)]);
+                    v[k] = t < rows ? to_f32(src[(size_t)t * H + (e - t * groups)]) : 0.f;
                 }
             }
 #pragma unroll
@@ -121,7 +123,16 @@ __global__ __launch_bounds__(kCumsumThreads) void cumsum_kernel(
 #pragma unroll
         for (int k = 0; k < PER; ++k) g[k] = (excl + part[k]) * kLog2e;
         const size_t o = ((size_t)b * H + h) * L + t0 + lane * PER;
-        if constexpr (PER == 4) {
+        if (rows < T || (L & 3) != 0) {
+            // partial chunk, or rows not 16-byte aligned: element stores of the real tokens
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                if (lane * PER + k < rows) {
+                    G[o + k] = g[k];
+                    if (dt_t) dt_t[o + k] = d[k];
+                }
+            }
+        } else if constexpr (PER == 4) {
             *(float4*)(G + o) = make_float4(g[0], g[1], g[2], g[3]);
             if (dt_t) *(float4*)(dt_t + o) = make_float4(d[0], d[1], d[2], d[3]);
         } else if constexpr (PER == 2) {

@@ -35,7 +35,10 @@ __global__ __launch_bounds__(64) void state_carry_kernel(const float* __restrict
     const int e = (blockIdx.x % per_bh) * 256 + threadIdx.x * 4;
     f32x4 hv = f32x4{0.f, 0.f, 0.f, 0.f};
     if (h0) hv = *(const f32x4*)(h0 + bh * PS + e);
-    const float* gl = G + bh * L + (T - 1);  // G at each chunk's last token: gl[c * T]
+    // G at each chunk's last token (the last real one in a partial last chunk, where the
+    // zero-padded tokens would leave G unchanged)
+    const float* gr = G + bh * L;
+    auto g_last = [&](int c) { return gr[min((c + 1) * T, L) - 1]; };
     const float* src = dS + bh * nC * (size_t)PS + e;
     TS* dst = states + bh * nC * (size_t)PS + e;
     constexpr int U = 8;
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(64) void state_carry_kernel(const float* __restrict
         for (int u = 0; u < U; ++u) {
             if (c0 + u < nC) {
                 d[u] = *(const f32x4*)(src + (size_t)(c0 + u) * PS);
-                dec[u] = exp2_fast(gl[(size_t)(c0 + u) * T]);
+                dec[u] = exp2_fast(g_last(c0 + u));
             }
         }
 #pragma unroll
@@ -58,6 +61,19 @@ __global__ __launch_bounds__(64) void state_carry_kernel(const float* __restrict
         }
     }
     if (fin) *(f32x4*)(fin + bh * PS + e) = hv;
+}
+
+// The state after an empty sequence: final = h0 (zeros without h0), 4 floats per thread.
+__global__ __launch_bounds__(256) void state_init_kernel(const float* __restrict__ h0,
+                                                         float* __restrict__ fin, size_t n4) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4) *(f32x4*)(fin + 4 * i) = h0 ? *(const f32x4*)(h0 + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+hipError_t launch_state_init(const float* h0, float* fin, const Dims& d, hipStream_t stream) {
+    const size_t n4 = (size_t)d.batch * d.nheads * d.headdim * d.dstate / 4;
+    state_init_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, stream>>>(h0, fin, n4);
+    return hipGetLastError();
 }
 
 hipError_t launch_state_carry(int states_dtype, const float* dS, const float* G,

@@ -26,13 +26,15 @@ bool one_of(int64_t v, std::initializer_list<int64_t> set) {
 
 size_t esize(int32_t dt) { return dt == SSD_BF16 ? 2 : 4; }
 
+// Chunks of the sequence (the last may be partial; none for an empty sequence).
+int64_t nchunks_of(const ssd_shape* s) { return (s->seqlen + s->chunk - 1) / s->chunk; }
+
 ssd_status check_shape(const ssd_shape* s) {
     if (!s) return SSD_ERR_NULL;
-    if (s->batch < 1 || s->seqlen < 1 || s->nheads < 1 || s->headdim < 1 || s->dstate < 1 ||
+    if (s->batch < 1 || s->seqlen < 0 || s->nheads < 1 || s->headdim < 1 || s->dstate < 1 ||
         s->ngroups < 1 || s->chunk < 1)
         return SSD_ERR_SHAPE;
     if (s->nheads % s->ngroups != 0) return SSD_ERR_SHAPE;
-    if (s->seqlen % s->chunk != 0) return SSD_ERR_SHAPE;
     if ((s->in_dtype != SSD_F32 && s->in_dtype != SSD_BF16) ||
         (s->states_dtype != SSD_F32 && s->states_dtype != SSD_BF16))
         return SSD_ERR_DTYPE;
@@ -43,7 +45,7 @@ ssd_status check_shape(const ssd_shape* s) {
     // Element counts handed to a kernel must fit the 31-bit index arithmetic, and the
     // per-batch extents the kernels address through buffer descriptors (32-bit byte
     // counts and offsets) must stay below 2 GiB; reject larger sizes rather than overflow.
-    const double per_batch_states = (double)s->nheads * (s->seqlen / s->chunk) * s->headdim *
+    const double per_batch_states = (double)s->nheads * nchunks_of(s) * s->headdim *
                                     s->dstate * 4.0;
     const double states = per_batch_states / 4.0 * (double)s->batch;
     const double xs = (double)s->batch * s->seqlen * s->nheads * s->headdim;
@@ -84,7 +86,7 @@ size_t decay_bytes(const ssd_shape* s) {  // one [batch, nheads, seqlen] fp32 ar
     return round_up((size_t)s->batch * s->nheads * s->seqlen * sizeof(float));
 }
 size_t chunk_states_elems(const ssd_shape* s) {
-    return (size_t)s->batch * s->nheads * (s->seqlen / s->chunk) * s->headdim * s->dstate;
+    return (size_t)s->batch * s->nheads * nchunks_of(s) * s->headdim * s->dstate;
 }
 size_t state_pass_ws(const ssd_shape* s) {  // per-chunk state increments, fp32
     return round_up(chunk_states_elems(s) * sizeof(float));
@@ -109,7 +111,7 @@ const char* ssd_status_string(int status) {
     switch (status) {
         case SSD_OK: return "ok";
         case SSD_ERR_NULL: return "a required pointer is NULL";
-        case SSD_ERR_SHAPE: return "invalid sizes (a size < 1, nheads % ngroups != 0 or seqlen % chunk != 0)";
+        case SSD_ERR_SHAPE: return "invalid sizes (a size < 1, seqlen < 0 or nheads % ngroups != 0)";
         case SSD_ERR_DTYPE: return "unknown dtype code";
         case SSD_ERR_UNSUPPORTED: return "chunk, headdim or dstate outside the supported sets";
         case SSD_ERR_WORKSPACE: return "workspace missing or too small";
@@ -141,8 +143,10 @@ ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float*
                             float* dt_t, void* stream) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
-    SSD_REQUIRE(dt && A && G, SSD_ERR_NULL);
+    const bool empty = shape->seqlen == 0;  // nothing to compute
+    SSD_REQUIRE(A && (empty || (dt && G)), SSD_ERR_NULL);
     SSD_REQUIRE(aligned16(dt) && aligned16(A) && aligned16(G) && aligned16(dt_t), SSD_ERR_ALIGN);
+    if (empty) return SSD_OK;
     return hip_status(ssd::launch_cumsum(shape->in_dtype, dt, A, G, dt_t, dims_of(shape),
                                          (hipStream_t)stream));
 }
@@ -153,14 +157,17 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
                           void* stream) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
-    SSD_REQUIRE(x && A && B && G && dt_t && states, SSD_ERR_NULL);
+    const bool empty = shape->seqlen == 0;  // only the final state (= h0) is written
+    SSD_REQUIRE(A && (empty || (x && B && G && dt_t && states)), SSD_ERR_NULL);
     SSD_REQUIRE(aligned16(x) && aligned16(A) && aligned16(B) && aligned16(G) && aligned16(dt_t) &&
                     aligned16(h0) && aligned16(states) && aligned16(final_state),
                 SSD_ERR_ALIGN);
-    SSD_REQUIRE(workspace && workspace_bytes >= state_pass_ws(shape), SSD_ERR_WORKSPACE);
+    const size_t need = state_pass_ws(shape);
+    SSD_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), SSD_ERR_WORKSPACE);
     SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
     const Dims d = dims_of(shape);
     hipStream_t s = (hipStream_t)stream;
+    if (empty) return final_state ? hip_status(ssd::launch_state_init(h0, final_state, d, s)) : SSD_OK;
     float* dS = (float*)workspace;
     hipError_t e = ssd::launch_chunk_state(shape->in_dtype, x, B, A, dt_t, dS, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
@@ -173,6 +180,7 @@ ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, c
                          float* y, void* stream) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
+    if (shape->seqlen == 0) return SSD_OK;  // empty sequence: no output rows
     SSD_REQUIRE(x && B && C && G && dt_t && states && y, SSD_ERR_NULL);
     SSD_REQUIRE(aligned16(x) && aligned16(B) && aligned16(C) && aligned16(G) &&
                     aligned16(dt_t) && aligned16(states) && aligned16(D) && aligned16(y),
@@ -188,15 +196,18 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
                        void* stream) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
-    SSD_REQUIRE(x && dt && A && B && C && y, SSD_ERR_NULL);
+    const bool empty = shape->seqlen == 0;  // only the final state (= h0) is written
+    SSD_REQUIRE(A && (empty || (x && dt && B && C && y)), SSD_ERR_NULL);
     SSD_REQUIRE(aligned16(x) && aligned16(dt) && aligned16(A) && aligned16(B) && aligned16(C) &&
                     aligned16(D) && aligned16(h0) && aligned16(y) && aligned16(final_state),
                 SSD_ERR_ALIGN);
-    SSD_REQUIRE(workspace && workspace_bytes >= forward_ws(shape), SSD_ERR_WORKSPACE);
+    const size_t need = forward_ws(shape);
+    SSD_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), SSD_ERR_WORKSPACE);
     SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
 
     const Dims d = dims_of(shape);
     hipStream_t s = (hipStream_t)stream;
+    if (empty) return final_state ? hip_status(ssd::launch_state_init(h0, final_state, d, s)) : SSD_OK;
     char* w = (char*)workspace;
     float* G = (float*)w;
     float* dt_t = (float*)(w + decay_bytes(shape));

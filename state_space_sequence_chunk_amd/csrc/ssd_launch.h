@@ -12,7 +12,8 @@ enum { kF32 = 0, kBF16 = 1 };
 
 struct Dims {
     int batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
-    int nchunks() const { return seqlen / chunk; }
+    // chunks of the sequence; the last one holds seqlen - (nchunks - 1) * chunk tokens
+    int nchunks() const { return (seqlen + chunk - 1) / chunk; }
 };
 
 hipError_t launch_cumsum(int in_dtype, const void* dt, const float* A, float* G, float* dt_t,
@@ -25,6 +26,10 @@ hipError_t launch_chunk_state(int in_dtype, const void* x, const void* Bm, const
 hipError_t launch_state_carry(int states_dtype, const float* dstate_chunks, const float* G,
                               const float* h0, void* states, float* final_state, const Dims& d,
                               hipStream_t stream);
+
+// final_state = h0 (zeros when h0 is NULL): the state after an empty sequence.
+hipError_t launch_state_init(const float* h0, float* final_state, const Dims& d,
+                             hipStream_t stream);
 
 // One recurrent step on a carried fp32 state (in place), y for that token.
 hipError_t launch_decode(int in_dtype, const void* x, const void* dt, const float* A,

@@ -45,8 +45,9 @@ def shape(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     ({}, 0),
-    (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(nheads=0), 2), (dict(ngroups=3), 2),
-    (dict(seqlen=500), 2), (dict(chunk=96, seqlen=576), 4), (dict(chunk=32, seqlen=512), 4),
+    (dict(batch=0), 2), (dict(seqlen=-1), 2), (dict(nheads=0), 2), (dict(ngroups=3), 2),
+    (dict(seqlen=0), 0), (dict(seqlen=500), 0), (dict(seqlen=1), 0),
+    (dict(chunk=96, seqlen=576), 4), (dict(chunk=32, seqlen=512), 4), (dict(chunk=0), 2),
     (dict(headdim=48), 4), (dict(dstate=96), 4), (dict(dstate=512), 4),
     (dict(in_dtype=7), 3), (dict(states_dtype=5), 3),
     (dict(headdim=16, dstate=16, chunk=64, in_dtype=ssd.SSD_F32), 0),
@@ -63,7 +64,37 @@ def test_workspace_sizes():
     dec = 2 * 8 * 512 * 4
     assert ssd.forward_workspace_bytes(s) == 2 * dec + elems * 4 + elems * 2
     with pytest.raises(ssd.SSDError):
-        ssd.forward_workspace_bytes(shape(seqlen=100))
+        ssd.forward_workspace_bytes(shape(ngroups=3))
+
+
+def _round256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_sizes_ragged_and_empty():
+    # 300 tokens in chunks of 256: two chunks, the second holding 44 real tokens
+    s = shape(seqlen=300, states_dtype=ssd.SSD_F32)
+    elems = 2 * 8 * 2 * 64 * 128
+    assert ssd.state_pass_workspace_bytes(s) == elems * 4
+    dec = _round256(2 * 8 * 300 * 4)
+    assert ssd.forward_workspace_bytes(s) == 2 * dec + elems * 4 + elems * 4
+    e = shape(seqlen=0)
+    assert ssd.state_pass_workspace_bytes(e) == 0 and ssd.forward_workspace_bytes(e) == 0
+
+
+def test_empty_sequence_host_paths():
+    # nothing to compute and no final state wanted: success with no launch and NULL tensors
+    lib = ssd.load_library()
+    e = shape(seqlen=0)
+    f = _v(FAKE)
+    assert lib.ssd_chunk_cumsum(ctypes.byref(e), None, f, None, None, None) == 0
+    assert lib.ssd_chunk_out(ctypes.byref(e), *[None] * 8, None) == 0
+    assert lib.ssd_forward(ctypes.byref(e), None, None, f, None, None, None, None, None, None,
+                           None, 0, None) == 0
+    assert lib.ssd_state_pass(ctypes.byref(e), None, f, None, None, None, None, None, None,
+                              None, 0, None) == 0
+    # A is still required
+    assert lib.ssd_forward(ctypes.byref(e), *[None] * 10, 0, None) == 1
 
 
 def test_null_shape_and_null_out_pointer():
@@ -94,7 +125,7 @@ def test_forward_rejects_before_launch():
     assert lib.ssd_forward(ctypes.byref(s), *args, _v(FAKE), need - 1, None) == 5
     assert lib.ssd_forward(ctypes.byref(s), *args, None, need, None) == 5
     # invalid shape wins over everything else
-    s2 = shape(seqlen=100)
+    s2 = shape(ngroups=3)
     assert lib.ssd_forward(ctypes.byref(s2), *args, _v(FAKE), need, None) == 2
 
 
