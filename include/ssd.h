@@ -21,7 +21,7 @@
  *        h0,final [batch, nheads, headdim, dstate]        fp32 (state stored P x S)
  *        G, dt_t  [batch, nheads, seqlen]                 fp32 (head-major, tokens fastest)
  *        states   [batch, nheads, nchunks, headdim, dstate]   states_dtype
- *        y        [batch, seqlen, nheads, headdim]        fp32
+ *        y        [batch, seqlen, nheads, headdim]        out_dtype (fp32 by default)
  *    with nchunks = ceil(seqlen / chunk).
  *  - Lengths: any seqlen >= 0. A last chunk shorter than `chunk` is processed as if it
  *    were padded with zero tokens (dt = 0, x = B = C = 0), which is the page's own padding
@@ -74,6 +74,10 @@ typedef struct ssd_shape {
     int32_t in_dtype;     /* dtype of x, dt, B, C */
     int32_t states_dtype; /* dtype of the chunk-initial states (ssd_state_pass output,
                              ssd_chunk_out input, and the forward pass's internal copy) */
+    int32_t out_dtype;    /* dtype of y: SSD_F32 (the default to use), or SSD_BF16 for
+                             bf16 inputs and bf16 states only. bf16 y is a throughput
+                             option: rounding y alone costs ~3e-2 of max|y| / rms(y) */
+    int32_t reserved;     /* set to 0 */
 } ssd_shape;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -122,21 +126,21 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
  *     y_i = 2^{G_i} C_i^T S_c + sum_{j <= i} 2^{G_i - G_j} (C_i . B_j) dt_j x_j + D[h] x_i
  * The causal mask keeps the diagonal (y_t reads the state after token t). The
  * interaction matrix C B^T never leaves the chip; decays of masked pairs are selected
- * away, never multiplied, so their overflow cannot reach y. y is written in fp32.
+ * away, never multiplied, so their overflow cannot reach y. y is written in out_dtype.
  * D may be NULL (no skip term).
  */
 ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, const void* C,
                          const float* G, const float* dt_t, const void* states, const float* D,
-                         float* y, void* stream);
+                         void* y, void* stream);
 
 /*
- * The whole forward pass: stage 1, stage 2, stage 3 on one stream. Returns y (fp32) and,
+ * The whole forward pass: stage 1, stage 2, stage 3 on one stream. Returns y (out_dtype) and,
  * when final_state is not NULL, the state after the last token (fp32), which may be fed
  * back as the next call's h0 (section "Kernel 2: fwd_pass_state", after the chunk loop).
  * h0 and D may be NULL. The workspace must hold ssd_forward_workspace_bytes bytes.
  */
 ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, const float* A,
-                       const void* B, const void* C, const float* D, const float* h0, float* y,
+                       const void* B, const void* C, const float* D, const float* h0, void* y,
                        float* final_state, void* workspace, size_t workspace_bytes,
                        void* stream);
 
@@ -149,7 +153,8 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
  *     y[b,h]      = state[b,h] . C[b,g] + D[h] x[b,h]      (reads the updated state)
  * so a prompt prefilled by ssd_forward (final_state) continues here token by token, and
  * a sequence split at any token gives the same result as one pass.
- * Shape: seqlen must be 1 (else SSD_ERR_SHAPE); chunk and states_dtype are not used.
+ * Shape: seqlen must be 1 (else SSD_ERR_SHAPE); chunk, states_dtype and out_dtype are not
+ * used (the state and y are fp32).
  * Layouts (the [batch, 1, ...] slices of the forward pass's layouts):
  *     x        [batch, nheads, headdim]          in_dtype
  *     dt       [batch, nheads]                   in_dtype

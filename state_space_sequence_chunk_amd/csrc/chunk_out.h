@@ -109,11 +109,20 @@ struct OutCfg {
         SHARED ? REGION0 + TILE_BYTES : HEAD_BYTES + (B_IN_LDS ? B_BYTES : 0);
 };
 
-template <typename TIn, typename TS, int P, int S, int T>
+// y element store through a buffer descriptor: fp32, or bf16 rounded to nearest even.
+__device__ __forceinline__ void store_y(float v, float*, BufRsrc r, uint32_t voff, uint32_t soff) {
+    buf_store_f32(v, r, voff, soff);
+}
+__device__ __forceinline__ void store_y(float v, bf16*, BufRsrc r, uint32_t voff, uint32_t soff) {
+    const bf16 b = from_f32<bf16>(v);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b), r, voff, soff, 0);
+}
+
+template <typename TIn, typename TS, typename TY, int P, int S, int T>
 __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ Bm, const TIn* __restrict__ Cm,
     const float* __restrict__ G, const float* __restrict__ dt_t, const TS* __restrict__ states,
-    const float* __restrict__ Dv, float* __restrict__ y, int L, int H, int ngroups, int NH) {
+    const float* __restrict__ Dv, TY* __restrict__ y, int L, int H, int ngroups, int NH) {
     using Cfg = OutCfg<TIn, TS, P, S, T>;
     constexpr int NPT = Cfg::NPT, NKS = Cfg::NKS, XS = Cfg::XS, SS = Cfg::SS, BS = Cfg::BS;
     constexpr int VE = Cfg::VE, VES = Cfg::VES, NTHR = Cfg::NTHR;
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     // (x and y rows past the real tokens lie outside these descriptors: loads return zeros
     // and stores are dropped)
     const BufRsrc rx = make_rsrc(x + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(TIn)));
-    const BufRsrc ry = make_rsrc(y + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(float)));
+    const BufRsrc ry = make_rsrc(y + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(TY)));
     const BufRsrc rst = make_rsrc(states + (size_t)b * H * nC * P * S,
                                   (uint32_t)((size_t)H * nC * P * S * sizeof(TS)));
     const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            yoff[q][r] = (uint32_t)(((its[q] * 16 + 4 * g4 + r) * HP + l16) * sizeof(float));
+            yoff[q][r] = (uint32_t)(((its[q] * 16 + 4 * g4 + r) * HP + l16) * sizeof(TY));
 
     for (int hh = 0; hh < NH; ++hh) {
         const int h = h_first + hh;
@@ -428,7 +437,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
 
         // 3. skip term and store (x of this lane's rows i by a column read)
         const float dh = Dv ? Dv[h] : 0.f;
-        const uint32_t yh = (uint32_t)(h * P * sizeof(float));
+        const uint32_t yh = (uint32_t)(h * P * sizeof(TY));
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -445,8 +454,8 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    buf_store_f32(yacc[q][pt][r] + dh * xi[r], ry,
-                                  yoff[q][r] + pt * 16 * (uint32_t)sizeof(float), yh);
+                    store_y(yacc[q][pt][r] + dh * xi[r], y, ry,
+                            yoff[q][r] + pt * 16 * (uint32_t)sizeof(TY), yh);
             }
 
         __syncthreads();  // every wave is done with this head's LDS copies
@@ -473,12 +482,12 @@ inline int heads_per_block(const Dims& d, size_t lds_bytes) {
     return best;
 }
 
-template <typename TIn, typename TS, int P, int S, int T>
+template <typename TIn, typename TS, typename TY, int P, int S, int T>
 hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G,
-                   const float* dt_t, const void* states, const float* D, float* y,
+                   const float* dt_t, const void* states, const float* D, void* y,
                    const Dims& d, hipStream_t stream) {
     using Cfg = OutCfg<TIn, TS, P, S, T>;
-    auto kern = chunk_out_kernel<TIn, TS, P, S, T>;
+    auto kern = chunk_out_kernel<TIn, TS, TY, P, S, T>;
     if (Cfg::LDS_BYTES > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -489,46 +498,46 @@ hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G
     const int nblocks = d.batch * d.nchunks() * (d.nheads / nh);
     kern<<<nblocks, 2 * T, Cfg::LDS_BYTES, stream>>>((const TIn*)x, (const TIn*)Bm,
                                                      (const TIn*)Cm, G, dt_t,
-                                                     (const TS*)states, D, y, d.seqlen,
+                                                     (const TS*)states, D, (TY*)y, d.seqlen,
                                                      d.nheads, d.ngroups, nh);
     return hipGetLastError();
 }
 
-template <typename TIn, typename TS, int P, int S>
+template <typename TIn, typename TS, typename TY, int P, int S>
 hipError_t out_by_t(const void* x, const void* Bm, const void* Cm, const float* G,
-                    const float* dt_t, const void* st, const float* D, float* y, const Dims& d,
+                    const float* dt_t, const void* st, const float* D, void* y, const Dims& d,
                     hipStream_t s) {
     switch (d.chunk) {
-        case 64: return run_out<TIn, TS, P, S, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 128: return run_out<TIn, TS, P, S, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 256: return run_out<TIn, TS, P, S, 256>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 64: return run_out<TIn, TS, TY, P, S, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 128: return run_out<TIn, TS, TY, P, S, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 256: return run_out<TIn, TS, TY, P, S, 256>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <typename TIn, typename TS, int P>
+template <typename TIn, typename TS, typename TY, int P>
 hipError_t out_by_s(const void* x, const void* Bm, const void* Cm, const float* G,
-                    const float* dt_t, const void* st, const float* D, float* y, const Dims& d,
+                    const float* dt_t, const void* st, const float* D, void* y, const Dims& d,
                     hipStream_t s) {
     switch (d.dstate) {
-        case 16: return out_by_t<TIn, TS, P, 16>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 32: return out_by_t<TIn, TS, P, 32>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 64: return out_by_t<TIn, TS, P, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 128: return out_by_t<TIn, TS, P, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 256: return out_by_t<TIn, TS, P, 256>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 16: return out_by_t<TIn, TS, TY, P, 16>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 32: return out_by_t<TIn, TS, TY, P, 32>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 64: return out_by_t<TIn, TS, TY, P, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 128: return out_by_t<TIn, TS, TY, P, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 256: return out_by_t<TIn, TS, TY, P, 256>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <typename TIn, typename TS>
+template <typename TIn, typename TS, typename TY>
 hipError_t out_by_p(const void* x, const void* Bm, const void* Cm, const float* G,
-                    const float* dt_t, const void* st, const float* D, float* y, const Dims& d,
+                    const float* dt_t, const void* st, const float* D, void* y, const Dims& d,
                     hipStream_t s) {
     switch (d.headdim) {
-        case 16: return out_by_s<TIn, TS, 16>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 32: return out_by_s<TIn, TS, 32>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 64: return out_by_s<TIn, TS, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
-        case 128: return out_by_s<TIn, TS, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 16: return out_by_s<TIn, TS, TY, 16>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 32: return out_by_s<TIn, TS, TY, 32>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 64: return out_by_s<TIn, TS, TY, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
+        case 128: return out_by_s<TIn, TS, TY, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
     }
     return hipErrorInvalidValue;
 }

@@ -4,9 +4,9 @@
 namespace ssd {
 
 hipError_t launch_chunk_out_bf16(const void* x, const void* Bm, const void* Cm, const float* G,
-                             const float* dt_t, const void* states, const float* D, float* y,
+                             const float* dt_t, const void* states, const float* D, void* y,
                              const Dims& d, hipStream_t s) {
-    return out_by_p<bf16, bf16>(x, Bm, Cm, G, dt_t, states, D, y, d, s);
+    return out_by_p<bf16, bf16, float>(x, Bm, Cm, G, dt_t, states, D, y, d, s);
 }
 
 }  // namespace ssd

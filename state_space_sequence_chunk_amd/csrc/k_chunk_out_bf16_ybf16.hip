@@ -1,0 +1,13 @@
+// Stage 3 kernel instances for inputs bf16, chunk-initial states bf16 and y bf16 (template in
+// chunk_out.h).
+#include "chunk_out.h"
+
+namespace ssd {
+
+hipError_t launch_chunk_out_bf16_ybf16(const void* x, const void* Bm, const void* Cm, const float* G,
+                             const float* dt_t, const void* states, const float* D, void* y,
+                             const Dims& d, hipStream_t s) {
+    return out_by_p<bf16, bf16, bf16>(x, Bm, Cm, G, dt_t, states, D, y, d, s);
+}
+
+}  // namespace ssd

@@ -36,9 +36,13 @@ ssd_status check_shape(const ssd_shape* s) {
         return SSD_ERR_SHAPE;
     if (s->nheads % s->ngroups != 0) return SSD_ERR_SHAPE;
     if ((s->in_dtype != SSD_F32 && s->in_dtype != SSD_BF16) ||
-        (s->states_dtype != SSD_F32 && s->states_dtype != SSD_BF16))
+        (s->states_dtype != SSD_F32 && s->states_dtype != SSD_BF16) ||
+        (s->out_dtype != SSD_F32 && s->out_dtype != SSD_BF16))
         return SSD_ERR_DTYPE;
     if (s->in_dtype == SSD_F32 && s->states_dtype == SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    // bf16 y is built for the all-bf16 path only
+    if (s->out_dtype == SSD_BF16 && (s->in_dtype != SSD_BF16 || s->states_dtype != SSD_BF16))
+        return SSD_ERR_UNSUPPORTED;
     if (!one_of(s->chunk, {64, 128, 256}) || !one_of(s->headdim, {16, 32, 64, 128}) ||
         !one_of(s->dstate, {16, 32, 64, 128, 256}))
         return SSD_ERR_UNSUPPORTED;
@@ -177,7 +181,7 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
 
 ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, const void* C,
                          const float* G, const float* dt_t, const void* states, const float* D,
-                         float* y, void* stream) {
+                         void* y, void* stream) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
     if (shape->seqlen == 0) return SSD_OK;  // empty sequence: no output rows
@@ -185,13 +189,14 @@ ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, c
     SSD_REQUIRE(aligned16(x) && aligned16(B) && aligned16(C) && aligned16(G) &&
                     aligned16(dt_t) && aligned16(states) && aligned16(D) && aligned16(y),
                 SSD_ERR_ALIGN);
-    return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype, x, B, C, G,
+    return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype,
+                                            shape->out_dtype, x, B, C, G,
                                             dt_t, states, D, y, dims_of(shape),
                                             (hipStream_t)stream));
 }
 
 ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, const float* A,
-                       const void* B, const void* C, const float* D, const float* h0, float* y,
+                       const void* B, const void* C, const float* D, const float* h0, void* y,
                        float* final_state, void* workspace, size_t workspace_bytes,
                        void* stream) {
     ssd_status st = check_shape(shape);
@@ -220,7 +225,8 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
     if (e != hipSuccess) return SSD_ERR_HIP;
     e = ssd::launch_state_carry(shape->states_dtype, dS, G, h0, states, final_state, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
-    return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype, x, B, C, G,
+    return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype,
+                                            shape->out_dtype, x, B, C, G,
                                             dt_t, states, D, y, d, s));
 }
 

@@ -36,8 +36,9 @@ hipError_t launch_decode(int in_dtype, const void* x, const void* dt, const floa
                          const void* Bm, const void* Cm, const float* D, float* state, float* y,
                          const Dims& d, hipStream_t stream);
 
-hipError_t launch_chunk_out(int in_dtype, int states_dtype, const void* x, const void* Bm,
-                            const void* Cm, const float* G, const float* dt_t, const void* states,
-                            const float* D, float* y, const Dims& d, hipStream_t stream);
+hipError_t launch_chunk_out(int in_dtype, int states_dtype, int out_dtype, const void* x,
+                            const void* Bm, const void* Cm, const float* G, const float* dt_t,
+                            const void* states, const float* D, void* y, const Dims& d,
+                            hipStream_t stream);
 
 }  // namespace ssd

@@ -36,7 +36,8 @@ class ssd_shape(ctypes.Structure):
                 ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
-                ("states_dtype", ctypes.c_int32)]
+                ("states_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -85,22 +86,26 @@ def dtype_code(dt: torch.dtype) -> int:
     raise ValueError(f"unsupported dtype {dt}")
 
 
+def _code(dt):
+    return dt if isinstance(dt, int) else dtype_code(dt)
+
+
 def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, in_dtype,
-               states_dtype=None) -> ssd_shape:
-    ind = in_dtype if isinstance(in_dtype, int) else dtype_code(in_dtype)
-    if states_dtype is None:
-        std = ind
-    else:
-        std = states_dtype if isinstance(states_dtype, int) else dtype_code(states_dtype)
+               states_dtype=None, out_dtype=None) -> ssd_shape:
+    """Shape struct; states default to the input dtype, y to fp32."""
+    ind = _code(in_dtype)
+    std = ind if states_dtype is None else _code(states_dtype)
+    outd = SSD_F32 if out_dtype is None else _code(out_dtype)
     return ssd_shape(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate),
-                     int(ngroups), int(chunk), ind, std)
+                     int(ngroups), int(chunk), ind, std, outd, 0)
 
 
-def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int, states_dtype=None) -> ssd_shape:
+def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int, states_dtype=None,
+             out_dtype=None) -> ssd_shape:
     """Shape struct from x [b, L, h, P] and B [b, L, g, S]."""
     b, L, H, P = x.shape
     G, S = B.shape[2], B.shape[3]
-    return make_shape(b, L, H, P, S, G, chunk, x.dtype, states_dtype)
+    return make_shape(b, L, H, P, S, G, chunk, x.dtype, states_dtype, out_dtype)
 
 
 def _p(t):
@@ -183,12 +188,13 @@ class Forward:
     torch supplies the device memory; the call itself is one C-ABI invocation.
     """
 
-    def __init__(self, x, B, chunk, states_dtype=None, device=None):
-        self.shape = shape_of(x, B, chunk, states_dtype)
+    def __init__(self, x, B, chunk, states_dtype=None, device=None, out_dtype=None):
+        self.shape = shape_of(x, B, chunk, states_dtype, out_dtype)
         dev = device or x.device
         b, L, H, P = x.shape
         S = B.shape[3]
-        self.y = torch.empty((b, L, H, P), dtype=torch.float32, device=dev)
+        ydt = torch.bfloat16 if self.shape.out_dtype == SSD_BF16 else torch.float32
+        self.y = torch.empty((b, L, H, P), dtype=ydt, device=dev)
         self.final = torch.empty((b, H, P, S), dtype=torch.float32, device=dev)
         self.workspace = torch.empty(forward_workspace_bytes(self.shape), dtype=torch.uint8,
                                      device=dev)
@@ -199,7 +205,9 @@ class Forward:
         return self.y, self.final
 
 
-def forward(x, dt, A, B, C, D=None, h0=None, *, chunk, states_dtype=None, stream=None):
-    """One-shot forward pass; returns (y fp32 [b, L, h, P], final state fp32 [b, h, P, S])."""
-    f = Forward(x, B, chunk, states_dtype)
+def forward(x, dt, A, B, C, D=None, h0=None, *, chunk, states_dtype=None, out_dtype=None,
+            stream=None):
+    """One-shot forward pass; returns (y [b, L, h, P] in out_dtype (fp32 by default),
+    final state fp32 [b, h, P, S])."""
+    f = Forward(x, B, chunk, states_dtype, out_dtype=out_dtype)
     return f(x, dt, A, B, C, D, h0, stream)

@@ -36,9 +36,15 @@ def test_library_exports_every_declared_symbol():
     assert sorted(ssd.EXPORTS) == names
 
 
+def test_shape_struct_matches_header():
+    # seven int64 sizes, then in_dtype, states_dtype, out_dtype, reserved (int32)
+    assert ctypes.sizeof(ssd.ssd_shape) == 7 * 8 + 4 * 4
+    assert ssd.ssd_shape.out_dtype.offset == 7 * 8 + 2 * 4
+
+
 def shape(**kw):
     base = dict(batch=2, seqlen=512, nheads=8, headdim=64, dstate=128, ngroups=2, chunk=256,
-                in_dtype=ssd.SSD_BF16, states_dtype=None)
+                in_dtype=ssd.SSD_BF16, states_dtype=None, out_dtype=None)
     base.update(kw)
     return ssd.make_shape(**base)
 
@@ -51,6 +57,9 @@ def shape(**kw):
     (dict(headdim=48), 4), (dict(dstate=96), 4), (dict(dstate=512), 4),
     (dict(in_dtype=7), 3), (dict(states_dtype=5), 3),
     (dict(headdim=16, dstate=16, chunk=64, in_dtype=ssd.SSD_F32), 0),
+    (dict(out_dtype=ssd.SSD_BF16), 0), (dict(out_dtype=7), 3),
+    (dict(out_dtype=ssd.SSD_BF16, states_dtype=ssd.SSD_F32), 4),
+    (dict(out_dtype=ssd.SSD_BF16, in_dtype=ssd.SSD_F32, states_dtype=ssd.SSD_F32), 4),
 ])
 def test_validate_shape(kw, code):
     assert ssd.validate_shape(shape(**kw)) == code

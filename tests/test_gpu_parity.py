@@ -277,3 +277,23 @@ def test_error_status_raises():
     _, d = make(w)
     with pytest.raises(ssd.SSDError):
         ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=96)
+
+
+# --- bf16 y (throughput option) ---------------------------------------------------------
+@pytest.mark.parametrize("name", ["small-bf16", "2.7b-bf16", "long-bf16"])
+def test_bf16_y_is_fp32_y_rounded(name):
+    w = SMALL[name]
+    cpu, d = make(w)
+    y32, f32 = gpu_forward(w, d)
+    y16, f16 = ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
+                           out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16
+    # the same fp32 value, rounded once to nearest even; the final state is unaffected
+    assert torch.equal(y16, y32.to(torch.bfloat16)) and torch.equal(f16, f32)
+    ref = oracle_forward(cpu)
+    e_max = max_rel_rms(np64(y16), ref["y"])
+    e_rms = rms_rel(np64(y16), ref["y"])
+    _print(f"{name}: bf16 y max/rms {e_max:.2e} rms-rel {e_rms:.2e} (fp32 y bound 2e-2 not claimed)")
+    assert e_rms <= 5e-3
+
