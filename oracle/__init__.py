@@ -16,14 +16,20 @@ Contents
 ``chunk_cumsum_log2``  the per-chunk cumulative decay in base-2 log space (same page,
                        section "Kernel 1: Computing cumulative sums"): the inclusive sum
                        of A*dt from the chunk's first token, times log2(e).
+``forward64``          the recurrence with float64 inputs (``ssd_oracle_grad.c``), used
+                       by the finite-difference checks of the gradients.
+``backward``           fp64 reverse-mode gradients of the recurrence with respect to x,
+                       dt, A, B, C, D and h0 (``ssd_oracle_grad.c``).
 
 Everything computes in float64 from float32-representable inputs (bf16 and fp32 input
 values are exact in float32).
 """
 from .ssd_oracle import (  # noqa: F401
+    backward,
     build,
     chunk_cumsum_log2,
     forward,
+    forward64,
     forward_pairs,
     library_path,
 )

@@ -14,6 +14,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
+_SRC_GRAD = os.path.join(_HERE, "ssd_oracle_grad.c")
 _OUT_DIR = os.path.join(_HERE, "_build")
 _LIB = os.path.join(_OUT_DIR, "libssd_oracle.so")
 
@@ -26,21 +27,26 @@ def library_path() -> str:
 
 def build(force: bool = True) -> str:
     """Compile the C oracle with gcc (plain -O2, IEEE semantics, no fast-math)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+    if not force and not _stale():
         return _LIB
     os.makedirs(_OUT_DIR, exist_ok=True)
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
-           "-std=c99", "-Wall", "-o", tmp, _SRC, "-lm", "-lpthread"]
+           "-std=c99", "-Wall", "-o", tmp, _SRC, _SRC_GRAD, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
 
 
+def _stale() -> bool:
+    return not os.path.exists(_LIB) or any(
+        os.path.getmtime(_LIB) < os.path.getmtime(src) for src in (_SRC, _SRC_GRAD))
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if _stale():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         f = lib.ssd_oracle_forward
@@ -48,6 +54,12 @@ def _load():
         vp = ctypes.c_void_p
         f.argtypes = [i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp,
                       ctypes.c_int]
+        f.restype = ctypes.c_int
+        f = lib.ssd_oracle_forward_f64
+        f.argtypes = [i64] * 6 + [vp] * 9 + [ctypes.c_int]
+        f.restype = ctypes.c_int
+        f = lib.ssd_oracle_backward
+        f.argtypes = [i64] * 6 + [vp] * 16 + [ctypes.c_int]
         f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -181,3 +193,55 @@ def chunk_cumsum_log2(dt, A, chunk):
             run = run + a[:, t, :]
             G[:, :, t] = run * log2e
     return G
+
+
+# --- gradients (ssd_oracle_grad.c) ----------------------------------------------------
+def _np64(a):
+    """float64 numpy copy of an array-like; torch tensors (any device) are widened."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().double().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def forward64(x, dt, A, B, C, D=None, h0=None, *, nthreads=None):
+    """The recurrence with float64 inputs (values used as given, no rounding to float32),
+    for finite differences. Returns {"y": [b, L, h, P], "final": [b, h, P, S]}."""
+    x, dt, A, B, C, D, h0 = (_np64(v) for v in (x, dt, A, B, C, D, h0))
+    bsz, L, H, P = x.shape
+    G, S = B.shape[2], B.shape[3]
+    y = np.empty((bsz, L, H, P), np.float64)
+    fin = np.empty((bsz, H, P, S), np.float64)
+    rc = _load().ssd_oracle_forward_f64(bsz, L, H, P, S, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                        _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(fin),
+                                        nthreads or _default_threads())
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_forward_f64 failed ({rc})")
+    return {"y": y, "final": fin}
+
+
+def backward(x, dt, A, B, C, D, h0, dy, dfinal=None, *, nthreads=None):
+    """Gradients of sum(dy * y) + sum(dfinal * final) with respect to every input, in
+    float64 (reverse-mode through the token recurrence; see ssd_oracle_grad.c).
+    Returns dx, ddt, dA [h], dB, dC [b, L, g, S], dD [h] and dh0 [b, h, P, S]; dA and dD
+    are summed over the batch here."""
+    x, dt, A, B, C, D, h0, dy, dfinal = (_np64(v) for v in (x, dt, A, B, C, D, h0, dy, dfinal))
+    bsz, L, H, P = x.shape
+    G, S = B.shape[2], B.shape[3]
+    dx = np.empty_like(x)
+    ddt = np.empty_like(dt)
+    dB = np.empty_like(B)
+    dC = np.empty_like(C)
+    dA_bh = np.empty((bsz, H), np.float64)
+    dD_bh = np.empty((bsz, H), np.float64)
+    dh0 = np.empty((bsz, H, P, S), np.float64)
+    rc = _load().ssd_oracle_backward(bsz, L, H, P, S, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(h0), _ptr(dy), _ptr(dfinal),
+                                     _ptr(dx), _ptr(ddt), _ptr(dA_bh), _ptr(dB), _ptr(dC),
+                                     _ptr(dD_bh), _ptr(dh0), nthreads or _default_threads())
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_backward failed ({rc})")
+    return {"dx": dx, "ddt": ddt, "dA": dA_bh.sum(axis=0), "dB": dB, "dC": dC,
+            "dD": dD_bh.sum(axis=0), "dh0": dh0}
+
