@@ -169,6 +169,31 @@ ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const void* dt
                            const void* B, const void* C, const float* D, float* state, float* y,
                            void* stream);
 
+/*
+ * Backward pass: the gradients of sum(dy * y) + sum(dfinal * final_state) with respect to
+ * every input of ssd_forward, i.e. reverse-mode differentiation of the recurrence of
+ * section "Mamba-2 architecture" (the page publishes no backward; this is the chain rule
+ * applied to its forward definition). With Lam_t = dL/dH_t:
+ *     Lam_t = dy_t (outer) C_t + exp(A dt_{t+1}) Lam_{t+1}
+ *     dx_t = D dy_t + dt_t Lam_t B_t,  dB_t = dt_t Lam_t^T x_t (summed over the group's
+ *     heads),  dC_t = H_t^T dy_t (summed likewise),  dD = sum dy . x,  dh0 = dL/dH_{-1},
+ *     ddt_t = x_t . Lam_t B_t + A dL/da_t,  dA = sum_t dt_t dL/da_t  (a_t = A dt_t).
+ * The forward quantities it needs (cumulative decay, chunk-initial states, final state)
+ * are recomputed here. All arithmetic is fp32; states_dtype and out_dtype are not used.
+ * Inputs: x, dt, B, C in in_dtype and A, D, h0 as for ssd_forward (D and h0 may be NULL);
+ * dy [batch, seqlen, nheads, headdim] fp32; dfinal [batch, nheads, headdim, dstate] fp32
+ * or NULL (zero). Outputs, all fp32, written in full: dx (x's layout), ddt (dt's layout),
+ * dA [nheads], dB and dC (B's layout), dD [nheads] (may be NULL), dh0 (h0's layout, may be
+ * NULL). The workspace must hold ssd_backward_workspace_bytes bytes. seqlen = 0: dh0 =
+ * dfinal (zeros without), dA = dD = 0, and the seqlen-sized tensors may be NULL.
+ */
+ssd_status ssd_backward_workspace_bytes(const ssd_shape* shape, size_t* bytes);
+ssd_status ssd_backward(const ssd_shape* shape, const void* x, const void* dt, const float* A,
+                        const void* B, const void* C, const float* D, const float* h0,
+                        const float* dy, const float* dfinal, float* dx, float* ddt, float* dA,
+                        float* dB, float* dC, float* dD, float* dh0, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,202 @@
+// Backward pass: orchestration and the kernels that do not depend on the state shape
+// (reverse carry over chunks, the per-(batch, head) suffix sum, the sums over heads).
+// The per-chunk kernels are templates in backward.h, instantiated per input dtype in
+// k_backward_bf16.hip and k_backward_f32.hip.
+#include "backward.h"
+
+namespace ssd {
+
+hipError_t launch_bwd_chunks_bf16(const BwdArgs& a, int batch, int P, int S, bool f, bool r,
+                                  bool v, hipStream_t st);
+hipError_t launch_bwd_chunks_f32(const BwdArgs& a, int batch, int P, int S, bool f, bool r,
+                                 bool v, hipStream_t st);
+
+// ---- reverse carry over chunks: R_c (gradient at chunk c's end), dh0 -------------------
+// In place over the per-chunk sums: reads dR_c, stores R_c, then R <- 2^{G_last} R + dR_c.
+__global__ __launch_bounds__(64) void bwd_carry_kernel(float* __restrict__ R,
+                                                        const float* __restrict__ G,
+                                                        const float* __restrict__ dfinal,
+                                                        float* __restrict__ dh0, int L, int T,
+                                                        int nC, int PS) {
+    const int per_bh = PS / 256;
+    const size_t bh = blockIdx.x / per_bh;
+    const int e = (blockIdx.x % per_bh) * 256 + threadIdx.x * 4;
+    f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (dfinal) r = *(const f32x4*)(dfinal + bh * PS + e);
+    const float* gr = G + bh * L;
+    float* base = R + bh * nC * (size_t)PS + e;
+    for (int c = nC - 1; c >= 0; --c) {
+        float* p = base + (size_t)c * PS;
+        const f32x4 d = *(const f32x4*)p;
+        *(f32x4*)p = r;
+        const float dec = exp2_fast(gr[min((c + 1) * T, L) - 1]);
+        r = dec * r + d;
+    }
+    if (dh0) *(f32x4*)(dh0 + bh * PS + e) = r;
+}
+
+// ---- per (batch, head): the suffix sum for the log-decay gradient, ddt, dA and dD -------
+// da_t = sum_{t' >= t} (q_t' - dt_t' v_t') + <dfinal, final>; 256 threads, each a
+// contiguous run of tokens, combined with a block-wide scan of the run totals.
+__global__ __launch_bounds__(256) void bwd_scan_kernel(
+    const float* __restrict__ q, const float* __restrict__ v, const float* __restrict__ dyx,
+    const float* __restrict__ dt_t, const float* __restrict__ A, const float* __restrict__ dfinal,
+    const float* __restrict__ fin, float* __restrict__ ddt, float* __restrict__ dA_bh,
+    float* __restrict__ dD_bh, int L, int H, int PS) {
+    __shared__ float s_tot[256];
+    __shared__ float s_red[3][256];
+    const int bh = blockIdx.x, h = bh % H, b = bh / H;
+    const int tid = threadIdx.x;
+    // <dfinal, final>
+    float cst = 0.f;
+    if (dfinal)
+        for (int i = tid; i < PS; i += 256) cst += dfinal[(size_t)bh * PS + i] * fin[(size_t)bh * PS + i];
+    s_red[0][tid] = cst;
+    // this thread's run of tokens
+    const int per = (L + 255) / 256;
+    const int ta = min(tid * per, L), tz = min(ta + per, L);
+    const size_t o = (size_t)bh * L;
+    float run = 0.f;
+    for (int t = ta; t < tz; ++t) run += q[o + t] - dt_t[o + t] * v[o + t];
+    s_tot[tid] = run;
+    __syncthreads();
+    if (tid == 0) {
+        float c = 0.f;
+        for (int i = 0; i < 256; ++i) c += s_red[0][i];
+        s_red[1][0] = c;
+        // suffix sums of the run totals: s_tot[i] <- sum_{j > i} tot_j
+        float acc = 0.f;
+        for (int i = 255; i >= 0; --i) {
+            const float tt = s_tot[i];
+            s_tot[i] = acc;
+            acc += tt;
+        }
+    }
+    __syncthreads();
+    const float ah = A[h];
+    float suffix = s_tot[tid] + s_red[1][0];
+    float pa = 0.f, pd = 0.f;
+    for (int t = tz - 1; t >= ta; --t) {
+        suffix += q[o + t] - dt_t[o + t] * v[o + t];
+        ddt[((size_t)b * L + t) * H + h] = v[o + t] + ah * suffix;
+        pa += dt_t[o + t] * suffix;
+        pd += dyx[o + t];
+    }
+    __syncthreads();
+    s_red[0][tid] = pa;
+    s_red[2][tid] = pd;
+    __syncthreads();
+    if (tid == 0) {
+        float sa = 0.f, sd = 0.f;
+        for (int i = 0; i < 256; ++i) {
+            sa += s_red[0][i];
+            sd += s_red[2][i];
+        }
+        dA_bh[bh] = sa;
+        dD_bh[bh] = sd;
+    }
+}
+
+// ---- sums over the heads of each group (dB, dC) and over the batch (dA, dD) ------------
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ dBh,
+                                                         const float* __restrict__ dCh,
+                                                         float* __restrict__ dB,
+                                                         float* __restrict__ dC, size_t nBG,
+                                                         int hpg, int S) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // over [B, L, G, S]
+    if (i >= nBG) return;
+    const size_t s = i % S, blg = i / S;
+    float sb = 0.f, sc = 0.f;
+    for (int k = 0; k < hpg; ++k) {
+        const size_t j = (blg * hpg + k) * S + s;
+        sb += dBh[j];
+        sc += dCh[j];
+    }
+    dB[i] = sb;
+    dC[i] = sc;
+}
+
+__global__ __launch_bounds__(256) void bwd_reduce_heads_kernel(const float* __restrict__ dA_bh,
+                                                               const float* __restrict__ dD_bh,
+                                                               float* __restrict__ dA,
+                                                               float* __restrict__ dD, int B,
+                                                               int H) {
+    const int h = blockIdx.x * 256 + threadIdx.x;
+    if (h >= H) return;
+    float sa = 0.f, sd = 0.f;
+    for (int b = 0; b < B; ++b) {
+        sa += dA_bh[(size_t)b * H + h];
+        sd += dD_bh[(size_t)b * H + h];
+    }
+    dA[h] = sa;
+    if (dD) dD[h] = sd;
+}
+
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+static hipError_t fill_zero(float* p, size_t n, hipStream_t s) {
+    if (!p || n == 0) return hipSuccess;
+    fill_zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipStream_t s) {
+    const int B = d.batch, L = d.seqlen, H = d.nheads, P = d.headdim, S = d.dstate;
+    const int G = d.ngroups, T = d.chunk, nC = d.nchunks(), PS = P * S;
+    const int hpg = H / G;
+    hipError_t e;
+    if (L == 0) {  // no tokens: final = h0, so dh0 = dfinal; nothing else moves
+        if (k.dh0) {
+            e = launch_state_init(k.dfinal, k.dh0, d, s);
+            if (e != hipSuccess) return e;
+        }
+        e = fill_zero(k.dA, H, s);
+        if (e != hipSuccess) return e;
+        return fill_zero(k.dD, H, s);
+    }
+    // forward quantities: cumulative decay, fp32 chunk-initial states, final state
+    e = launch_cumsum(in_dtype, k.dt, k.A, k.ws.G, k.ws.dt_t, d, s);
+    if (e != hipSuccess) return e;
+    e = launch_chunk_state(in_dtype, k.x, k.B, k.A, k.ws.dt_t, k.ws.R, d, s);
+    if (e != hipSuccess) return e;
+    e = launch_state_carry(kF32, k.ws.R, k.ws.G, k.h0, k.ws.Hc, k.ws.fin, d, s);
+    if (e != hipSuccess) return e;
+
+    BwdArgs a;
+    a.x = k.x; a.dt = k.dt; a.Bm = k.B; a.Cm = k.C; a.A = k.A; a.D = k.D; a.dy = k.dy;
+    a.Hc = k.ws.Hc; a.R = k.ws.R; a.dx = k.dx;
+    a.dBh = hpg == 1 ? k.dB : k.ws.dBh;
+    a.dCh = hpg == 1 ? k.dC : k.ws.dCh;
+    a.v = k.ws.v; a.q = k.ws.q; a.dyx = k.ws.dyx;
+    a.L = L; a.H = H; a.G = G; a.T = T;
+    auto chunks = [&](bool f, bool r, bool v) {
+        return in_dtype == kBF16 ? launch_bwd_chunks_bf16(a, B, P, S, f, r, v, s)
+                                 : launch_bwd_chunks_f32(a, B, P, S, f, r, v, s);
+    };
+    // forward walk (dC, q) and the per-chunk sums dR_c (over the consumed increments)
+    e = chunks(true, true, false);
+    if (e != hipSuccess) return e;
+    bwd_carry_kernel<<<B * H * (PS / 256), 64, 0, s>>>(k.ws.R, k.ws.G, k.dfinal, k.dh0, L, T, nC,
+                                                       PS);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = chunks(false, false, true);
+    if (e != hipSuccess) return e;
+    bwd_scan_kernel<<<B * H, 256, 0, s>>>(k.ws.q, k.ws.v, k.ws.dyx, k.ws.dt_t, k.A, k.dfinal,
+                                          k.ws.fin, k.ddt, k.ws.dA_bh, k.ws.dD_bh, L, H, PS);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (hpg > 1) {
+        const size_t n = (size_t)B * L * G * S;
+        bwd_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k.ws.dBh, k.ws.dCh, k.dB,
+                                                                      k.dC, n, hpg, S);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    bwd_reduce_heads_kernel<<<(H + 255) / 256, 256, 0, s>>>(k.ws.dA_bh, k.ws.dD_bh, k.dA, k.dD,
+                                                            B, H);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

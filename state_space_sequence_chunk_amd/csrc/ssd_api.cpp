@@ -100,6 +100,25 @@ size_t forward_ws(const ssd_shape* s) {  // G, dt_t, increments, chunk-initial s
            round_up(chunk_states_elems(s) * esize(s->states_dtype));
 }
 
+// Backward workspace: the forward quantities it recomputes and its per-token partials.
+struct BwdSizes {
+    size_t dec, st, fin, tok, bh, part, total;
+};
+BwdSizes bwd_sizes(const ssd_shape* s) {
+    BwdSizes z;
+    const size_t BH = (size_t)s->batch * s->nheads;
+    z.dec = round_up(BH * s->seqlen * sizeof(float));
+    z.st = round_up(chunk_states_elems(s) * sizeof(float));
+    z.fin = round_up(BH * s->headdim * s->dstate * sizeof(float));
+    z.tok = z.dec;
+    z.bh = round_up(BH * sizeof(float));
+    const bool shared = s->nheads != s->ngroups;
+    z.part = shared ? round_up((size_t)s->batch * s->seqlen * s->nheads * s->dstate * sizeof(float))
+                    : 0;
+    z.total = s->seqlen == 0 ? 0 : 2 * z.dec + 2 * z.st + z.fin + 3 * z.tok + 2 * z.bh + 2 * z.part;
+    return z;
+}
+
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
 #define SSD_REQUIRE(cond, code) \
@@ -241,6 +260,66 @@ ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const void* dt
                 SSD_ERR_ALIGN);
     return hip_status(ssd::launch_decode(shape->in_dtype, x, dt, A, B, C, D, state, y,
                                          dims_of(shape), (hipStream_t)stream));
+}
+
+// The backward pass computes in fp32 throughout: states_dtype and out_dtype are not used.
+static ssd_status check_backward_shape(const ssd_shape* shape) {
+    if (!shape) return SSD_ERR_NULL;
+    ssd_shape s = *shape;
+    s.states_dtype = SSD_F32;
+    s.out_dtype = SSD_F32;
+    return check_shape(&s);
+}
+
+ssd_status ssd_backward_workspace_bytes(const ssd_shape* shape, size_t* bytes) {
+    SSD_REQUIRE(bytes, SSD_ERR_NULL);
+    ssd_status st = check_backward_shape(shape);
+    if (st != SSD_OK) return st;
+    *bytes = bwd_sizes(shape).total;
+    return SSD_OK;
+}
+
+ssd_status ssd_backward(const ssd_shape* shape, const void* x, const void* dt, const float* A,
+                        const void* B, const void* C, const float* D, const float* h0,
+                        const float* dy, const float* dfinal, float* dx, float* ddt, float* dA,
+                        float* dB, float* dC, float* dD, float* dh0, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    ssd_status st = check_backward_shape(shape);
+    if (st != SSD_OK) return st;
+    const bool empty = shape->seqlen == 0;
+    SSD_REQUIRE(A && dA && (empty || (x && dt && B && C && dy && dx && ddt && dB && dC)),
+                SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(dt) && aligned16(A) && aligned16(B) && aligned16(C) &&
+                    aligned16(D) && aligned16(h0) && aligned16(dy) && aligned16(dfinal) &&
+                    aligned16(dx) && aligned16(ddt) && aligned16(dA) && aligned16(dB) &&
+                    aligned16(dC) && aligned16(dD) && aligned16(dh0),
+                SSD_ERR_ALIGN);
+    const BwdSizes z = bwd_sizes(shape);
+    SSD_REQUIRE(workspace_bytes >= z.total && (z.total == 0 || workspace), SSD_ERR_WORKSPACE);
+    SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
+    ssd::BwdLaunch k;
+    k.x = x; k.dt = dt; k.B = B; k.C = C; k.A = A; k.D = D; k.h0 = h0; k.dy = dy;
+    k.dfinal = dfinal; k.dx = dx; k.ddt = ddt; k.dA = dA; k.dB = dB; k.dC = dC; k.dD = dD;
+    k.dh0 = dh0;
+    char* w = (char*)workspace;
+    auto take = [&](size_t n) {
+        float* p = n ? (float*)w : nullptr;
+        w += n;
+        return p;
+    };
+    k.ws.G = take(z.dec);
+    k.ws.dt_t = take(z.dec);
+    k.ws.Hc = take(z.st);
+    k.ws.R = take(z.st);
+    k.ws.fin = take(z.fin);
+    k.ws.v = take(z.tok);
+    k.ws.q = take(z.tok);
+    k.ws.dyx = take(z.tok);
+    k.ws.dA_bh = take(z.bh);
+    k.ws.dD_bh = take(z.bh);
+    k.ws.dBh = take(z.part);
+    k.ws.dCh = take(z.part);
+    return hip_status(ssd::launch_backward(shape->in_dtype, k, dims_of(shape), (hipStream_t)stream));
 }
 
 }  // extern "C"

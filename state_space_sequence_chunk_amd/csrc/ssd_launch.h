@@ -36,6 +36,24 @@ hipError_t launch_decode(int in_dtype, const void* x, const void* dt, const floa
                          const void* Bm, const void* Cm, const float* D, float* state, float* y,
                          const Dims& d, hipStream_t stream);
 
+// Backward pass: every buffer below is the caller's (the workspace carved up on the host).
+struct BwdWorkspace {
+    float *G, *dt_t;      // [B, H, L] cumulative decay and dt (fp32)
+    float *Hc, *R;        // [B, H, nC, P, S] chunk-initial states; increments, then the
+                          // gradient arriving at each chunk's end
+    float* fin;           // [B, H, P, S] forward final state
+    float *v, *q, *dyx;   // [B, H, L] per-token scalars
+    float *dA_bh, *dD_bh; // [B, H]
+    float *dBh, *dCh;     // [B, L, H, S] per-head dB, dC (when heads share a group)
+};
+struct BwdLaunch {
+    const void *x, *dt, *B, *C;
+    const float *A, *D, *h0, *dy, *dfinal;
+    float *dx, *ddt, *dA, *dB, *dC, *dD, *dh0;
+    BwdWorkspace ws;
+};
+hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipStream_t stream);
+
 hipError_t launch_chunk_out(int in_dtype, int states_dtype, int out_dtype, const void* x,
                             const void* Bm, const void* Cm, const float* G, const float* dt_t,
                             const void* states, const float* D, void* y, const Dims& d,

@@ -100,3 +100,11 @@ def draw(batch, seqlen, nheads, headdim, dstate, ngroups, dtype, gen, *, random_
         "x": x.to(dtype), "dt": dt.to(dtype), "A": A, "B": B.to(dtype), "C": C.to(dtype),
         "D": D, "h0": h0,
     }
+
+
+def draw_cotangents(batch, seqlen, nheads, headdim, dstate, gen) -> dict:
+    """Seeded incoming gradients for the backward pass: dy [b, L, h, P] and dfinal
+    [b, h, P, S], both fp32 N(0, 1)."""
+    f32 = torch.float32
+    return {"dy": torch.randn((batch, seqlen, nheads, headdim), generator=gen, dtype=f32),
+            "dfinal": torch.randn((batch, nheads, headdim, dstate), generator=gen, dtype=f32)}

@@ -22,7 +22,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE"
 # Entry points declared in include/ssd.h.
 EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_bytes",
            "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
-           "ssd_chunk_out", "ssd_forward", "ssd_decode_step")
+           "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
+           "ssd_backward")
 
 
 class SSDError(RuntimeError):
@@ -66,6 +67,8 @@ def load_library():
     lib.ssd_chunk_out.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_backward_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
+    lib.ssd_backward.argtypes = [sp] + [vp] * 17 + [sz, vp]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -180,6 +183,39 @@ def decode_step(x, dt, A, B, C, D, state, *, stream=None):
     y = torch.empty((b, H, P), dtype=torch.float32, device=x.device)
     ssd_decode_step(sh, x, dt, A, B, C, D, state, y, stream)
     return y
+
+
+def backward_workspace_bytes(shape: ssd_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_backward_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)),
+           "ssd_backward_workspace_bytes")
+    return int(n.value)
+
+
+def ssd_backward(shape, x, dt, A, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0,
+                 workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ssd_backward(ctypes.byref(shape), _p(x), _p(dt), _p(A), _p(B), _p(C),
+                                       _p(D), _p(h0), _p(dy), _p(dfinal), _p(dx), _p(ddt),
+                                       _p(dA), _p(dB), _p(dC), _p(dD), _p(dh0), _p(workspace),
+                                       nbytes, _stream(stream)), "ssd_backward")
+
+
+def backward(x, dt, A, B, C, D, h0, dy, dfinal=None, *, chunk, stream=None):
+    """Gradients of sum(dy * y) + sum(dfinal * final) (fp32 tensors, input layouts):
+    returns dict dx, ddt, dA, dB, dC, dD, dh0."""
+    sh = shape_of(x, B, chunk)
+    b, L, H, P = x.shape
+    S = B.shape[3]
+    f32 = dict(dtype=torch.float32, device=x.device)
+    out = {"dx": torch.empty(x.shape, **f32), "ddt": torch.empty(dt.shape, **f32),
+           "dA": torch.empty(A.shape, **f32), "dB": torch.empty(B.shape, **f32),
+           "dC": torch.empty(C.shape, **f32), "dD": torch.empty((H,), **f32),
+           "dh0": torch.empty((b, H, P, S), **f32)}
+    ws = torch.empty(backward_workspace_bytes(sh), dtype=torch.uint8, device=x.device)
+    ssd_backward(sh, x, dt, A, B, C, D, h0, dy, dfinal, out["dx"], out["ddt"], out["dA"],
+                 out["dB"], out["dC"], out["dD"], out["dh0"], ws, stream)
+    return out
 
 
 class Forward:

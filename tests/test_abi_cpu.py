@@ -188,3 +188,46 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ssd, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         ssd.load_library()
+
+
+def test_backward_workspace_sizes():
+    # G, dt_t, chunk-initial states, gradients at the chunk ends, final state, three
+    # per-token scalars, two per-(batch, head) partials, and per-head dB, dC (shared groups)
+    s = shape(seqlen=300)
+    dec = _round256(2 * 8 * 300 * 4)
+    st = 2 * 8 * 2 * 64 * 128 * 4
+    fin = 2 * 8 * 64 * 128 * 4
+    part = _round256(2 * 300 * 8 * 128 * 4)
+    want = 2 * dec + 2 * st + fin + 3 * dec + 2 * 256 + 2 * part
+    assert ssd.backward_workspace_bytes(s) == want
+    # one head per group: the per-head partials are the outputs themselves
+    s1 = shape(seqlen=300, ngroups=8)
+    assert ssd.backward_workspace_bytes(s1) == want - 2 * part
+    # the backward pass ignores states_dtype and out_dtype
+    assert ssd.backward_workspace_bytes(shape(seqlen=300, in_dtype=ssd.SSD_F32,
+                                              states_dtype=ssd.SSD_BF16)) == want
+    assert ssd.backward_workspace_bytes(shape(seqlen=0)) == 0
+
+
+def test_backward_rejects_before_launch():
+    lib = ssd.load_library()
+    s = shape()
+    f = _v(FAKE)
+    need = ssd.backward_workspace_bytes(s)
+    # x dt A B C D h0 dy dfinal dx ddt dA dB dC dD dh0
+    args = [f] * 16
+    for i in (0, 1, 2, 3, 4, 7, 9, 10, 11, 12, 13):  # required pointers
+        bad = list(args)
+        bad[i] = None
+        assert lib.ssd_backward(ctypes.byref(s), *bad, f, need, None) == 1, i
+    bad = list(args)
+    bad[10] = _v(FAKE + 4)  # misaligned ddt
+    assert lib.ssd_backward(ctypes.byref(s), *bad, f, need, None) == 6
+    assert lib.ssd_backward(ctypes.byref(s), *args, f, need - 1, None) == 5
+    assert lib.ssd_backward(ctypes.byref(s), *args, None, need, None) == 5
+    assert lib.ssd_backward(ctypes.byref(shape(ngroups=3)), *args, f, need, None) == 2
+    assert lib.ssd_backward(ctypes.byref(shape(dstate=96)), *args, f, need, None) == 4
+    assert lib.ssd_backward(None, *args, f, need, None) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.ssd_backward_workspace_bytes(ctypes.byref(s), None) == 1
+    assert lib.ssd_backward_workspace_bytes(ctypes.byref(shape(in_dtype=9)), ctypes.byref(n)) == 3
