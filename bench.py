@@ -172,6 +172,40 @@ def time_decode(torch, ssd, d, state, stream, steps=32, replays=8):
     return {"ms": ms, "bytes": nbytes, "graph_steps": steps * replays}
 
 
+def time_backward(torch, ssd, gen, w, d, stream, steps, warmup):
+    """The backward pass on the same inputs with seeded N(0, 1) dy and dfinal: ms per call,
+    timed with events on the launch stream."""
+    g = torch.Generator()
+    g.manual_seed(w.seed + 1)
+    cot = gen.draw_cotangents(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, g)
+    dy, dfin = cot["dy"].cuda(), cot["dfinal"].cuda()
+    del cot
+    sh = ssd.shape_of(d["x"], d["B"], w.chunk)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = [torch.empty(d["x"].shape, **f32), torch.empty(d["dt"].shape, **f32),
+           torch.empty(d["A"].shape, **f32), torch.empty(d["B"].shape, **f32),
+           torch.empty(d["C"].shape, **f32), torch.empty((w.nheads,), **f32),
+           torch.empty(dfin.shape, **f32)]
+    ws = torch.empty(ssd.backward_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+
+    def call():
+        ssd.ssd_backward(sh, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], dy, dfin,
+                         *out, ws, stream)
+
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "steps": steps, "workspace_bytes": ws.numel()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +324,13 @@ def main():
         variants["bf16_y"] = {"value": w.tokens / (ms16 * 1e-3), "unit": "tokens/s",
                               "ms_per_step": ms16}
         del f16
+
+    # the backward pass (gradients of every input), a separate figure from the forward
+    try:
+        variants["backward"] = time_backward(torch, ssd, gen, w, d, stream,
+                                             max(1, min(K, 10)), min(args.warmup, 2))
+    except Exception as exc:  # reported, never silently replaced
+        variants["backward"] = {"error": f"{type(exc).__name__}: {exc}"}
 
     try:
         decode = time_decode(torch, ssd, d, fin, stream)
