@@ -68,6 +68,8 @@ struct BwdArgs {
     const float* A;   // [H]
     const float* D;   // [H] or null
     const float* dy;  // [B, L, H, P]
+    const float* Gc;  // [B, H, L] per-chunk cumulative log2 decay
+    const float* dtt; // [B, H, L] dt (fp32)
     const float* Hc;  // [B, H, nC, P, S] chunk-initial states (fp32)
     float* R;         // [B, H, nC, P, S] dR_c, then R_c
     float* dx;        // [B, L, H, P]

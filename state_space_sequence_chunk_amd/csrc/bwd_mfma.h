@@ -1,0 +1,528 @@
+// Backward pass on the matrix cores (bf16 inputs): the per-chunk products of the gradient
+// written as causal decayed products, one kernel template for three of them.
+//
+// Inside chunk c (tokens t, s of the chunk; G the inclusive log2 decay from the chunk's
+// start, G_e its value at the last real token; H_c the state entering the chunk and R_c
+// the gradient arriving at its end), the chain rule through the recurrence of page
+// "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA CUDA Tile",
+// section "Mamba-2 architecture", gives
+//     dC_t  = 2^{G_t} H_c^T dy_t       + sum_{s <= t} 2^{G_t - G_s} dt_s (dy_t . x_s) B_s
+//     dB_s  = dt_s [2^{G_e - G_s} R_c^T x_s + sum_{t >= s} 2^{G_t - G_s} (x_s . dy_t) C_t]
+//     dxh_s = 2^{G_e - G_s} R_c B_s    + sum_{t >= s} 2^{G_t - G_s} (B_s . C_t) dy_t
+// with dx_s = D dy_s + dt_s dxh_s. Each is
+//     out_i = scale_i Q_i . Z  +  sum_{j causal to i} 2^{+-(G_i - G_j)} w_j (Q_i . K_j) V_j
+// ("causal" is j <= i forward in time for dC, j >= i backward in time for dB and dxh):
+//     op   Q    K    V    Z (state, [N][KD])   w     scale
+//     dC   dy   x    B    H_c^T                dt    2^{G_i}
+//     dB   x    dy   C    R_c^T                1     2^{G_e - G_i}   (times dt_i after)
+//     dxh  B    C    dy   R_c                  1     2^{G_e - G_i}
+// The epilogues also form q_t = C_t . dC_t (dC op), and v_s = x_s . dxh_s, dy_s . x_s and
+// dx (dxh op), the per-token scalars of the decay gradient.
+//
+// gfx950 mapping: one workgroup of T/32 waves per (batch, chunk, head); K rows, V rows,
+// the state (bf16 high and low parts of its fp32 values) and G, dt in LDS. Wave w owns
+// row tiles w and T/16-1-w (equal causal work). For each 32-wide block of j it builds
+// the two 16x16 tiles Z^T[j][i] = K_j . Q_i on MFMA with Q's row fragments held in
+// registers; the accumulator layout of Z^T (lane: column i, four consecutive j) is the
+// A-operand layout of out += W V, so the decay, mask and w are applied in registers and
+// W is rounded once to bf16; V's token-axis fragments come from the transposing LDS read.
+// dy enters the MFMAs rounded to bf16; everything else accumulates in fp32.
+#pragma once
+
+#include <type_traits>
+
+#include "backward.h"
+
+namespace ssd {
+
+enum BwdOp { kOpC = 0, kOpB = 1, kOpX = 2 };
+
+template <int OP, int P, int S, int T>
+struct BmCfg {
+    static constexpr bool REV = OP != kOpC;
+    static constexpr int KD = OP == kOpX ? S : P;  // contraction of Q . K and of Q . Z
+    static constexpr int N = OP == kOpX ? P : S;   // output width
+    // dy (fp32) is the operand split into bf16 high and low parts: Q of dC, K of dB, V of dxh
+    static constexpr bool QSPLIT = OP == kOpC, KSPLIT = OP == kOpB, VSPLIT = OP == kOpX;
+    static constexpr int NIT = T / 16, NW = T / 32, NTHR = 64 * NW;
+    static constexpr int NKS = KD / 32, NNT = N / 16;
+    static constexpr int KS = row_stride<bf16>(KD);  // K rows and Z rows (read by rows)
+    static constexpr int VS = col_stride<bf16>(N);   // V rows (read by columns)
+    static constexpr size_t K_BYTES = (size_t)T * KS * 2;  // each part
+    static constexpr size_t V_BYTES = (size_t)T * VS * 2;  // each part
+    static constexpr size_t Z_BYTES = (size_t)N * KS * 2;  // each part
+    static constexpr size_t LDS_BYTES = K_BYTES * (KSPLIT ? 2 : 1) + V_BYTES * (VSPLIT ? 2 : 1) +
+                                        2 * Z_BYTES + 2 * (size_t)T * 4;
+    static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && N % 16 == 0;
+};
+
+// 8 consecutive values as bf16 (high part) and, for fp32 sources, the bf16 remainders
+__device__ __forceinline__ void ld8_split(const bf16* p, bf16x8& hi, bf16x8& lo) {
+    hi = *(const bf16x8*)p;
+    lo = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+__device__ __forceinline__ void ld8_split(const float* p, bf16x8& hi, bf16x8& lo) {
+    const f32x4 u = *(const f32x4*)p, w = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = (bf16)u[i];
+        hi[i + 4] = (bf16)w[i];
+        lo[i] = (bf16)(u[i] - to_f32(hi[i]));
+        lo[i + 4] = (bf16)(w[i] - to_f32(hi[i + 4]));
+    }
+}
+
+// Rows [0, NROWS) x NCOLS (a multiple of 8) of a row-major source, staged into LDS as bf16
+// (and, with SPLIT, the bf16 remainders of fp32 values): load() puts every load of the
+// calling thread in flight at once, store() converts and writes after they land. Rows at
+// or past `rows` are zero.
+template <typename TSrc, int NTHR, int NROWS, int NCOLS, bool SPLIT>
+struct Stager {
+    static constexpr int PER = NCOLS / 8, NVEC = NROWS * PER;
+    static constexpr int NV = (NVEC + NTHR - 1) / NTHR;
+    static constexpr bool F32 = sizeof(TSrc) == 4;
+    f32x4 raw[F32 ? 2 * NV : NV];
+    __device__ __forceinline__ void load(const TSrc* src, size_t sstride, int rows, int tid) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * NTHR;
+            const int r = v / PER, col = (v % PER) * 8;
+            const bool ok = v < NVEC && r < rows;
+            if constexpr (F32) {
+                raw[2 * i] = ok ? *(const f32x4*)(src + r * sstride + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+                raw[2 * i + 1] =
+                    ok ? *(const f32x4*)(src + r * sstride + col + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                raw[i] = ok ? *(const f32x4*)(src + r * sstride + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
+    __device__ __forceinline__ void store(bf16* dst, bf16* dst_lo, int dstride, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v >= NVEC) continue;
+            const int r = v / PER, col = (v % PER) * 8;
+            if constexpr (F32) {
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    hi[k] = (bf16)raw[2 * i][k];
+                    hi[k + 4] = (bf16)raw[2 * i + 1][k];
+                    lo[k] = (bf16)(raw[2 * i][k] - to_f32(hi[k]));
+                    lo[k + 4] = (bf16)(raw[2 * i + 1][k] - to_f32(hi[k + 4]));
+                }
+                *(bf16x8*)(dst + r * dstride + col) = hi;
+                if constexpr (SPLIT) *(bf16x8*)(dst_lo + r * dstride + col) = lo;
+            } else {
+                *(f32x4*)(dst + r * dstride + col) = raw[i];
+            }
+        }
+    }
+};
+
+// The state [P][S] (fp32) transposed into LDS: Z[s][p], high and low bf16 parts.
+template <int NTHR, int P, int S>
+struct StateTStager {
+    static constexpr int NVEC = P * S / 4, NV = (NVEC + NTHR - 1) / NTHR;
+    f32x4 raw[NV];
+    __device__ __forceinline__ void load(const float* src, int tid) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * NTHR;
+            raw[i] = v < NVEC ? *(const f32x4*)(src + (size_t)v * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __device__ __forceinline__ void store(bf16* zh, bf16* zl, int ks, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v >= NVEC) continue;
+            const int p = v / (S / 4), s0 = (v % (S / 4)) * 4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bf16 hi = (bf16)raw[i][k];
+                zh[(s0 + k) * ks + p] = hi;
+                zl[(s0 + k) * ks + p] = (bf16)(raw[i][k] - to_f32(hi));
+            }
+        }
+    }
+};
+
+template <int OP, int P, int S, int T>
+__global__ __launch_bounds__(2 * T) void bwd_mfma_kernel(BwdArgs a) {
+    using Cfg = BmCfg<OP, P, S, T>;
+    constexpr int N = Cfg::N, NKS = Cfg::NKS, NNT = Cfg::NNT;
+    constexpr int KS = Cfg::KS, VS = Cfg::VS, NTHR = Cfg::NTHR, NIT = Cfg::NIT;
+    constexpr bool REV = Cfg::REV, QSPLIT = Cfg::QSPLIT, KSPLIT = Cfg::KSPLIT,
+                   VSPLIT = Cfg::VSPLIT;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char* sp = smem;
+    bf16* s_k = (bf16*)sp;                               // [T][KS]
+    sp += Cfg::K_BYTES;
+    bf16* s_kl = KSPLIT ? (bf16*)sp : nullptr;           // [T][KS] low parts of K
+    sp += KSPLIT ? Cfg::K_BYTES : 0;
+    bf16* s_v = (bf16*)sp;                               // [T][VS]
+    sp += Cfg::V_BYTES;
+    bf16* s_vl = VSPLIT ? (bf16*)sp : nullptr;           // [T][VS] low parts of V
+    sp += VSPLIT ? Cfg::V_BYTES : 0;
+    bf16* s_zh = (bf16*)sp;                              // [N][KS]
+    bf16* s_zl = s_zh + N * KS;                          // [N][KS]
+    sp += 2 * Cfg::Z_BYTES;
+    float* s_g = (float*)sp;                             // [T]
+    float* s_dt = s_g + T;                               // [T]
+
+    const int L = a.L, H = a.H, NG = a.G;
+    const int nC = (L + T - 1) / T;
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = id % H, c = (id / H) % nC, b = id / (H * nC);
+    const int g = h / (H / NG);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int t0 = c * T, rows = min(T, L - t0);
+    const size_t HP = (size_t)H * P, GS = (size_t)NG * S;
+    const bf16* xr = (const bf16*)a.x + (((size_t)b * L + t0) * H + h) * P;    // stride HP
+    const float* dyr = a.dy + (((size_t)b * L + t0) * H + h) * P;             // stride HP
+    const bf16* br = (const bf16*)a.Bm + (((size_t)b * L + t0) * NG + g) * S;  // stride GS
+    const bf16* cr = (const bf16*)a.Cm + (((size_t)b * L + t0) * NG + g) * S;  // stride GS
+    const size_t bhl = ((size_t)b * H + h) * L + t0;
+    const float* zsrc = (OP == kOpC ? a.Hc : a.R) + (((size_t)b * H + h) * nC + c) * P * S;
+
+    // ---- staging: K and V rows, the state (high/low bf16), G and dt ---------------------
+    // (every load in flight before the first LDS write)
+    using KSrc = std::conditional_t<OP == kOpB, float, bf16>;
+    using VSrc = std::conditional_t<OP == kOpX, float, bf16>;
+    constexpr int KD = Cfg::KD;
+    Stager<KSrc, NTHR, T, KD, KSPLIT> stk;
+    Stager<VSrc, NTHR, T, N, VSPLIT> stv;
+    if constexpr (OP == kOpC) {
+        stk.load(xr, HP, rows, tid);
+        stv.load(br, GS, rows, tid);
+    } else if constexpr (OP == kOpB) {
+        stk.load(dyr, HP, rows, tid);
+        stv.load(cr, GS, rows, tid);
+    } else {
+        stk.load(cr, GS, rows, tid);
+        stv.load(dyr, HP, rows, tid);
+    }
+    float pg = 0.f, pdt = 0.f;
+    if (tid < T) {
+        pg = a.Gc[bhl + min(tid, rows - 1)];
+        pdt = tid < rows ? a.dtt[bhl + tid] : 0.f;
+    }
+    if constexpr (OP == kOpX) {
+        // Z[n = p][k = s] = R_c[p][s]: rows of the state as they are
+        Stager<float, NTHR, P, S, true> stz;
+        stz.load(zsrc, S, P, tid);
+        stk.store(s_k, s_kl, KS, tid);
+        stv.store(s_v, s_vl, VS, tid);
+        stz.store(s_zh, s_zl, KS, tid);
+    } else {
+        // Z[n = s][k = p] = state[p][s]: the state transposed
+        StateTStager<NTHR, P, S> stz;
+        stz.load(zsrc, tid);
+        stk.store(s_k, s_kl, KS, tid);
+        stv.store(s_v, s_vl, VS, tid);
+        stz.store(s_zh, s_zl, KS, tid);
+    }
+    if (tid < T) {
+        s_g[tid] = pg;
+        s_dt[tid] = pdt;
+    }
+    __syncthreads();
+
+    const float g_end = s_g[T - 1];  // = G at the last real token (padded rows repeat it)
+    const float dval = a.D ? a.D[h] : 0.f;
+#pragma unroll 1
+    for (int qi = 0; qi < 2; ++qi) {
+        const int it = qi == 0 ? wave : NIT - 1 - wave;  // this wave's row tiles
+        const int I0 = it * 16;
+        // Q's rows of this tile (lane: row I0 + l16, k = 32 ks + 8 g4 + v)
+        Frag<bf16> qf[NKS], ql[NKS];
+        const int qrow = I0 + l16;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int k0 = ks * 32 + g4 * 8;
+            bf16x8 hi = bf16x8{0, 0, 0, 0, 0, 0, 0, 0}, lo = hi;
+            if (qrow < rows) {
+                if constexpr (OP == kOpC) ld8_split(dyr + qrow * HP + k0, hi, lo);
+                else if constexpr (OP == kOpB) ld8_split(xr + qrow * HP + k0, hi, lo);
+                else ld8_split(br + qrow * GS + k0, hi, lo);
+            }
+            qf[ks].v = hi;
+            ql[ks].v = lo;
+        }
+        f32x4 acc[NNT];
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // carried-state term Q_i . Z, scaled per row
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) {
+                Frag<bf16> zh, zl;
+                zh.v = *(const bf16x8*)(s_zh + (nt * 16 + l16) * KS + ks * 32 + g4 * 8);
+                zl.v = *(const bf16x8*)(s_zl + (nt * 16 + l16) * KS + ks * 32 + g4 * 8);
+                mma(acc[nt], qf[ks], zh);
+                mma(acc[nt], qf[ks], zl);
+                if constexpr (QSPLIT) mma(acc[nt], ql[ks], zh);
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float gi = s_g[I0 + 4 * g4 + r];
+            const float sc = exp2_fast(REV ? g_end - gi : gi);
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) acc[nt][r] *= sc;
+        }
+        // intra-chunk term over 32-wide blocks of j
+        const float gi = s_g[qrow];
+        const int jp_lo = REV ? it / 2 : 0, jp_hi = REV ? NIT / 2 - 1 : it / 2;
+#pragma unroll 1
+        for (int jp = jp_lo; jp <= jp_hi; ++jp) {
+            const int J0 = jp * 32;
+            f32x4 zt[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int o = (J0 + jt * 16 + l16) * KS + ks * 32 + g4 * 8;
+                    Frag<bf16> kf;
+                    kf.v = *(const bf16x8*)(s_k + o);
+                    mma(zt[jt], kf, qf[ks]);
+                    if constexpr (QSPLIT) mma(zt[jt], kf, ql[ks]);
+                    if constexpr (KSPLIT) {
+                        kf.v = *(const bf16x8*)(s_kl + o);
+                        mma(zt[jt], kf, qf[ks]);
+                    }
+                }
+            // W[i][j] in the A-operand layout (row i = qrow, item 4 jt + r <-> j), split
+            // into bf16 high and low parts
+            Frag<bf16> wf, wl;
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                const f32x4 gj = *(const f32x4*)(s_g + J0 + jt * 16 + 4 * g4);
+                f32x4 wj = f32x4{1.f, 1.f, 1.f, 1.f};
+                if constexpr (!REV) wj = *(const f32x4*)(s_dt + J0 + jt * 16 + 4 * g4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = J0 + jt * 16 + 4 * g4 + r;
+                    const bool keep = REV ? j >= qrow : j <= qrow;
+                    const float e = exp2_fast(REV ? gj[r] - gi : gi - gj[r]);
+                    const float w = keep ? e * wj[r] * zt[jt][r] : 0.f;
+                    const bf16 hi = (bf16)w;
+                    wf.v[jt * 4 + r] = hi;
+                    wl.v[jt * 4 + r] = (bf16)(w - to_f32(hi));
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) {
+                Frag<bf16> vf;
+                vf.v = __builtin_shufflevector(lds_col4(s_v, VS, J0 + 4 * g4, nt * 16, lane),
+                                               lds_col4(s_v, VS, J0 + 16 + 4 * g4, nt * 16, lane),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+                mma(acc[nt], wf, vf);
+                mma(acc[nt], wl, vf);
+                if constexpr (VSPLIT) {
+                    vf.v = __builtin_shufflevector(
+                        lds_col4(s_vl, VS, J0 + 4 * g4, nt * 16, lane),
+                        lds_col4(s_vl, VS, J0 + 16 + 4 * g4, nt * 16, lane), 0, 1, 2, 3, 4, 5,
+                        6, 7);
+                    mma(acc[nt], wf, vf);
+                }
+            }
+        }
+        // ---- epilogue: element (row I0 + 4 g4 + r, column 16 nt + l16) of the tile ------
+        float red[4] = {0.f, 0.f, 0.f, 0.f}, red2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = I0 + 4 * g4 + r;
+            if (i >= rows) continue;
+            const size_t tok = ((size_t)b * L + t0 + i) * H + h;
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) {
+                const int n = nt * 16 + l16;
+                const float o = acc[nt][r];
+                if constexpr (OP == kOpC) {
+                    a.dCh[tok * S + n] = o;
+                    red[r] += o * to_f32(cr[i * GS + n]);
+                } else if constexpr (OP == kOpB) {
+                    a.dBh[tok * S + n] = s_dt[i] * o;
+                } else {
+                    const float dyv = dyr[i * HP + n], xv = to_f32(xr[i * HP + n]);
+                    a.dx[tok * P + n] = dval * dyv + s_dt[i] * o;
+                    red[r] += xv * o;
+                    red2[r] += xv * dyv;
+                }
+            }
+        }
+        if constexpr (OP != kOpB) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) {
+                    red[r] += __shfl_xor(red[r], m, 64);
+                    if constexpr (OP == kOpX) red2[r] += __shfl_xor(red2[r], m, 64);
+                }
+                const int i = I0 + 4 * g4 + r;
+                if (l16 == 0 && i < rows) {
+                    if constexpr (OP == kOpC) {
+                        a.q[bhl + i] = red[r];
+                    } else {
+                        a.v[bhl + i] = red[r];
+                        a.dyx[bhl + i] = red2[r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---- per-chunk sums for the reverse carry: dR_c = sum_t 2^{G_t} dy_t C_t^T -------------
+// One workgroup of T/32 waves per (batch, chunk, head). The rows 2^{G_t} dy_t (fp32, split
+// into bf16 high and low parts) and C_t sit in LDS as [t][.]; each output tile [16 p x 16 s]
+// contracts over the chunk's tokens with both operands read down the token axis by the
+// transposing LDS read (token slot (g, v) <-> t = 4 g + v, 16 + 4 g + v - 4 in each
+// 32-token step, the same for both operands).
+template <int P, int S, int T>
+struct DrCfg {
+    static constexpr int NW = T / 32, NTHR = 64 * NW;
+    static constexpr int YS = col_stride<bf16>(P), CS = col_stride<bf16>(S);
+    static constexpr size_t Y_BYTES = (size_t)T * YS * 2;  // each part
+    static constexpr size_t C_BYTES = (size_t)T * CS * 2;
+    static constexpr size_t LDS_BYTES = 2 * Y_BYTES + C_BYTES;
+    static constexpr bool FITS = LDS_BYTES <= 163840 && P % 16 == 0 && S % 16 == 0;
+};
+
+template <int P, int S, int T>
+__global__ __launch_bounds__(2 * T) void bwd_dR_mfma_kernel(BwdArgs a) {
+    using Cfg = DrCfg<P, S, T>;
+    constexpr int YS = Cfg::YS, CS = Cfg::CS, NTHR = Cfg::NTHR, NW = Cfg::NW;
+    constexpr int NPT = P / 16, NST = S / 16, NTILE = NPT * NST;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    bf16* s_yh = (bf16*)smem;                              // [T][YS]
+    bf16* s_yl = (bf16*)(smem + Cfg::Y_BYTES);             // [T][YS]
+    bf16* s_c = (bf16*)(smem + 2 * Cfg::Y_BYTES);          // [T][CS]
+
+    const int L = a.L, H = a.H, NG = a.G;
+    const int nC = (L + T - 1) / T;
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = id % H, c = (id / H) % nC, b = id / (H * nC);
+    const int g = h / (H / NG);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int t0 = c * T, rows = min(T, L - t0);
+    const size_t HP = (size_t)H * P, GS = (size_t)NG * S;
+    const float* dyr = a.dy + (((size_t)b * L + t0) * H + h) * P;
+    const bf16* cr = (const bf16*)a.Cm + (((size_t)b * L + t0) * NG + g) * S;
+    const size_t bhl = ((size_t)b * H + h) * L + t0;
+
+    // rows of 2^{G_t} dy_t: every load in flight, then the weighted split into LDS
+    constexpr int PER = P / 8, NVY = (T * PER + NTHR - 1) / NTHR;
+    f32x4 ry[2 * NVY];
+    float wt[NVY];
+#pragma unroll
+    for (int i = 0; i < NVY; ++i) {
+        const int v = tid + i * NTHR;
+        const int r = v / PER, col = (v % PER) * 8;
+        const bool ok = v < T * PER && r < rows;
+        ry[2 * i] = ok ? *(const f32x4*)(dyr + r * HP + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+        ry[2 * i + 1] = ok ? *(const f32x4*)(dyr + r * HP + col + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        wt[i] = ok ? a.Gc[bhl + r] : 0.f;
+    }
+    Stager<bf16, NTHR, T, S, false> stc;
+    stc.load(cr, GS, rows, tid);
+#pragma unroll
+    for (int i = 0; i < NVY; ++i) {
+        const int v = tid + i * NTHR;
+        if (v >= T * PER) continue;
+        const int r = v / PER, col = (v % PER) * 8;
+        const float w = exp2_fast(wt[i]);
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float u0 = w * ry[2 * i][k], u1 = w * ry[2 * i + 1][k];
+            hi[k] = (bf16)u0;
+            hi[k + 4] = (bf16)u1;
+            lo[k] = (bf16)(u0 - to_f32(hi[k]));
+            lo[k + 4] = (bf16)(u1 - to_f32(hi[k + 4]));
+        }
+        *(bf16x8*)(s_yh + r * YS + col) = hi;
+        *(bf16x8*)(s_yl + r * YS + col) = lo;
+    }
+    stc.store(s_c, nullptr, CS, tid);
+    __syncthreads();
+
+    float* out = a.R + (((size_t)b * H + h) * nC + c) * P * S;
+#pragma unroll 1
+    for (int tile = wave; tile < NTILE; tile += NW) {
+        const int p0 = (tile / NST) * 16, s0 = (tile % NST) * 16;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < T; k0 += 32) {
+            Frag<bf16> yh, yl, cf;
+            yh.v = __builtin_shufflevector(lds_col4(s_yh, YS, k0 + 4 * g4, p0, lane),
+                                           lds_col4(s_yh, YS, k0 + 16 + 4 * g4, p0, lane),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
+            yl.v = __builtin_shufflevector(lds_col4(s_yl, YS, k0 + 4 * g4, p0, lane),
+                                           lds_col4(s_yl, YS, k0 + 16 + 4 * g4, p0, lane),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
+            cf.v = __builtin_shufflevector(lds_col4(s_c, CS, k0 + 4 * g4, s0, lane),
+                                           lds_col4(s_c, CS, k0 + 16 + 4 * g4, s0, lane),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
+            mma(acc, yh, cf);
+            mma(acc, yl, cf);
+        }
+        // element (row p0 + 4 g4 + r, column s0 + l16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[(size_t)(p0 + 4 * g4 + r) * S + s0 + l16] = acc[r];
+    }
+}
+
+template <int P, int S, int T>
+hipError_t run_bwd_dR_mfma(const BwdArgs& a, int batch, hipStream_t stream) {
+    using Cfg = DrCfg<P, S, T>;
+    auto kern = bwd_dR_mfma_kernel<P, S, T>;
+    if (Cfg::LDS_BYTES > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)Cfg::LDS_BYTES);
+        if (e != hipSuccess) return e;
+    }
+    const int nC = (a.L + T - 1) / T;
+    kern<<<batch * nC * a.H, 2 * T, Cfg::LDS_BYTES, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int OP, int P, int S, int T>
+hipError_t run_bwd_mfma(const BwdArgs& a, int batch, hipStream_t stream) {
+    using Cfg = BmCfg<OP, P, S, T>;
+    auto kern = bwd_mfma_kernel<OP, P, S, T>;
+    if (Cfg::LDS_BYTES > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)Cfg::LDS_BYTES);
+        if (e != hipSuccess) return e;
+    }
+    const int nC = (a.L + T - 1) / T;
+    kern<<<batch * nC * a.H, 2 * T, Cfg::LDS_BYTES, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int P, int S, int T>
+constexpr bool bwd_mfma_fits() {
+    return BmCfg<kOpC, P, S, T>::FITS && BmCfg<kOpB, P, S, T>::FITS &&
+           BmCfg<kOpX, P, S, T>::FITS && DrCfg<P, S, T>::FITS;
+}
+
+template <int P, int S, int T>
+hipError_t run_bwd_mfma_all(const BwdArgs& a, int batch, hipStream_t st) {
+    hipError_t e = run_bwd_mfma<kOpC, P, S, T>(a, batch, st);
+    if (e == hipSuccess) e = run_bwd_mfma<kOpB, P, S, T>(a, batch, st);
+    if (e == hipSuccess) e = run_bwd_mfma<kOpX, P, S, T>(a, batch, st);
+    return e;
+}
+
+}  // namespace ssd

@@ -10,6 +10,8 @@ hipError_t launch_bwd_chunks_bf16(const BwdArgs& a, int batch, int P, int S, boo
                                   bool v, hipStream_t st);
 hipError_t launch_bwd_chunks_f32(const BwdArgs& a, int batch, int P, int S, bool f, bool r,
                                  bool v, hipStream_t st);
+hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, int batch, int P, int S, hipStream_t st);
+hipError_t launch_bwd_dR_mfma_bf16(const BwdArgs& a, int batch, int P, int S, hipStream_t st);
 
 // ---- reverse carry over chunks: R_c (gradient at chunk c's end), dh0 -------------------
 // In place over the per-chunk sums: reads dR_c, stores R_c, then R <- 2^{G_last} R + dR_c.
@@ -168,6 +170,7 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
 
     BwdArgs a;
     a.x = k.x; a.dt = k.dt; a.Bm = k.B; a.Cm = k.C; a.A = k.A; a.D = k.D; a.dy = k.dy;
+    a.Gc = k.ws.G; a.dtt = k.ws.dt_t;
     a.Hc = k.ws.Hc; a.R = k.ws.R; a.dx = k.dx;
     a.dBh = hpg == 1 ? k.dB : k.ws.dBh;
     a.dCh = hpg == 1 ? k.dC : k.ws.dCh;
@@ -177,13 +180,23 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
         return in_dtype == kBF16 ? launch_bwd_chunks_bf16(a, B, P, S, f, r, v, s)
                                  : launch_bwd_chunks_f32(a, B, P, S, f, r, v, s);
     };
-    // forward walk (dC, q) and the per-chunk sums dR_c (over the consumed increments)
-    e = chunks(true, true, false);
+    // bf16 inputs with a matrix-core plan for this shape (run at its own chunk length,
+    // which the caller has put in d): dC, dB and dx as chunked products; otherwise the
+    // fp32 token walks
+    const bool mfma = bwd_mfma_chunk(in_dtype, P, S) == T;
+    // per-chunk sums dR_c (over the consumed increments), and with the walks the forward
+    // walk (dC, q)
+    if (mfma) e = launch_bwd_dR_mfma_bf16(a, B, P, S, s);
+    else e = chunks(true, true, false);
     if (e != hipSuccess) return e;
     bwd_carry_kernel<<<B * H * (PS / 256), 64, 0, s>>>(k.ws.R, k.ws.G, k.dfinal, k.dh0, L, T, nC,
                                                        PS);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = chunks(false, false, true);
+    if (mfma) {
+        e = launch_bwd_mfma_bf16(a, B, P, S, s);
+    } else {
+        e = chunks(false, false, true);
+    }
     if (e != hipSuccess) return e;
     bwd_scan_kernel<<<B * H, 256, 0, s>>>(k.ws.q, k.ws.v, k.ws.dyx, k.ws.dt_t, k.A, k.dfinal,
                                           k.ws.fin, k.ddt, k.ws.dA_bh, k.ws.dD_bh, L, H, PS);

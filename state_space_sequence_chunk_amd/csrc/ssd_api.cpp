@@ -104,7 +104,18 @@ size_t forward_ws(const ssd_shape* s) {  // G, dt_t, increments, chunk-initial s
 struct BwdSizes {
     size_t dec, st, fin, tok, bh, part, total;
 };
-BwdSizes bwd_sizes(const ssd_shape* s) {
+// The shape the backward pass runs at: the caller's, with the chunk length of the
+// matrix-core plan when there is one.
+ssd_shape bwd_shape(const ssd_shape* s) {
+    ssd_shape b = *s;
+    const int t = ssd::bwd_mfma_chunk(s->in_dtype, (int)s->headdim, (int)s->dstate);
+    if (t) b.chunk = t;
+    return b;
+}
+
+BwdSizes bwd_sizes(const ssd_shape* shape) {
+    const ssd_shape bs = bwd_shape(shape);
+    const ssd_shape* s = &bs;
     BwdSizes z;
     const size_t BH = (size_t)s->batch * s->nheads;
     z.dec = round_up(BH * s->seqlen * sizeof(float));
@@ -319,7 +330,8 @@ ssd_status ssd_backward(const ssd_shape* shape, const void* x, const void* dt, c
     k.ws.dD_bh = take(z.bh);
     k.ws.dBh = take(z.part);
     k.ws.dCh = take(z.part);
-    return hip_status(ssd::launch_backward(shape->in_dtype, k, dims_of(shape), (hipStream_t)stream));
+    const ssd_shape bs = bwd_shape(shape);
+    return hip_status(ssd::launch_backward(shape->in_dtype, k, dims_of(&bs), (hipStream_t)stream));
 }
 
 }  // extern "C"

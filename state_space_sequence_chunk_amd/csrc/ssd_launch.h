@@ -53,6 +53,9 @@ struct BwdLaunch {
     BwdWorkspace ws;
 };
 hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipStream_t stream);
+// Chunk length at which the backward pass runs its matrix-core kernels for this shape (0:
+// none; the token walks then run at the caller's chunk length).
+int bwd_mfma_chunk(int in_dtype, int P, int S);
 
 hipError_t launch_chunk_out(int in_dtype, int states_dtype, int out_dtype, const void* x,
                             const void* Bm, const void* Cm, const float* G, const float* dt_t,

@@ -193,19 +193,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_backward_workspace_sizes():
     # G, dt_t, chunk-initial states, gradients at the chunk ends, final state, three
     # per-token scalars, two per-(batch, head) partials, and per-head dB, dC (shared groups)
+    # bf16 inputs, P = 64, S = 128: the matrix-core kernels run at 128-token chunks (3 here)
     s = shape(seqlen=300)
     dec = _round256(2 * 8 * 300 * 4)
-    st = 2 * 8 * 2 * 64 * 128 * 4
     fin = 2 * 8 * 64 * 128 * 4
     part = _round256(2 * 300 * 8 * 128 * 4)
+    st = 2 * 8 * 3 * 64 * 128 * 4
     want = 2 * dec + 2 * st + fin + 3 * dec + 2 * 256 + 2 * part
     assert ssd.backward_workspace_bytes(s) == want
     # one head per group: the per-head partials are the outputs themselves
     s1 = shape(seqlen=300, ngroups=8)
     assert ssd.backward_workspace_bytes(s1) == want - 2 * part
-    # the backward pass ignores states_dtype and out_dtype
-    assert ssd.backward_workspace_bytes(shape(seqlen=300, in_dtype=ssd.SSD_F32,
-                                              states_dtype=ssd.SSD_BF16)) == want
+    # fp32 inputs take the token walks at the caller's chunk (2 chunks of 256); the
+    # backward pass ignores states_dtype and out_dtype
+    st2 = 2 * 8 * 2 * 64 * 128 * 4
+    want2 = 2 * dec + 2 * st2 + fin + 3 * dec + 2 * 256 + 2 * part
+    for sd in (ssd.SSD_F32, ssd.SSD_BF16):
+        assert ssd.backward_workspace_bytes(shape(seqlen=300, in_dtype=ssd.SSD_F32,
+                                                  states_dtype=sd)) == want2
+    assert ssd.backward_workspace_bytes(shape(seqlen=300, out_dtype=ssd.SSD_BF16)) == want
     assert ssd.backward_workspace_bytes(shape(seqlen=0)) == 0
 
 
