@@ -44,16 +44,17 @@ struct BmCfg {
     static constexpr int N = OP == kOpX ? P : S;   // output width
     // dy (fp32) is the operand split into bf16 high and low parts: Q of dC, K of dB, V of dxh
     static constexpr bool QSPLIT = OP == kOpC, KSPLIT = OP == kOpB, VSPLIT = OP == kOpX;
-    static constexpr int NIT = T / 16, NW = T / 32, NTHR = 64 * NW;
-    static constexpr int NKS = KD / 32, NNT = N / 16;
+    // T/32 pairs of row tiles; two waves per pair, each taking half of the output columns
+    static constexpr int NIT = T / 16, NW = T / 32, NTHR = 128 * NW;
+    static constexpr int NKS = KD / 32, NNT = N / 16, NNH = NNT / 2;
     static constexpr int KS = row_stride<bf16>(KD);  // K rows and Z rows (read by rows)
     static constexpr int VS = col_stride<bf16>(N);   // V rows (read by columns)
     static constexpr size_t K_BYTES = (size_t)T * KS * 2;  // each part
     static constexpr size_t V_BYTES = (size_t)T * VS * 2;  // each part
     static constexpr size_t Z_BYTES = (size_t)N * KS * 2;  // each part
     static constexpr size_t LDS_BYTES = K_BYTES * (KSPLIT ? 2 : 1) + V_BYTES * (VSPLIT ? 2 : 1) +
-                                        2 * Z_BYTES + 2 * (size_t)T * 4;
-    static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && N % 16 == 0;
+                                        2 * Z_BYTES + 2 * (size_t)T * 4 + 4 * (size_t)T * 4;
+    static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && N % 32 == 0;
 };
 
 // 8 consecutive values as bf16 (high part) and, for fp32 sources, the bf16 remainders
@@ -121,16 +122,22 @@ struct Stager {
     }
 };
 
-// The state [P][S] (fp32) transposed into LDS: Z[s][p], high and low bf16 parts.
+// The state [P][S] (fp32) transposed into LDS: Z[s][p], high and low bf16 parts. Each
+// thread takes two neighbouring rows p, p + 1 and four columns, so the lanes of a wave
+// write consecutive 4-byte words of a Z row (a pair of bf16 values each).
 template <int NTHR, int P, int S>
 struct StateTStager {
-    static constexpr int NVEC = P * S / 4, NV = (NVEC + NTHR - 1) / NTHR;
-    f32x4 raw[NV];
+    static constexpr int NVEC = (P / 2) * (S / 4), NV = (NVEC + NTHR - 1) / NTHR;
+    f32x4 raw[2 * NV];
     __device__ __forceinline__ void load(const float* src, int tid) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int v = tid + i * NTHR;
-            raw[i] = v < NVEC ? *(const f32x4*)(src + (size_t)v * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int p = 2 * (v % (P / 2)), s0 = 4 * (v / (P / 2));
+            const bool ok = v < NVEC;
+            raw[2 * i] = ok ? *(const f32x4*)(src + (size_t)p * S + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+            raw[2 * i + 1] =
+                ok ? *(const f32x4*)(src + (size_t)(p + 1) * S + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     __device__ __forceinline__ void store(bf16* zh, bf16* zl, int ks, int tid) const {
@@ -138,21 +145,27 @@ struct StateTStager {
         for (int i = 0; i < NV; ++i) {
             const int v = tid + i * NTHR;
             if (v >= NVEC) continue;
-            const int p = v / (S / 4), s0 = (v % (S / 4)) * 4;
+            const int p = 2 * (v % (P / 2)), s0 = 4 * (v / (P / 2));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const bf16 hi = (bf16)raw[i][k];
-                zh[(s0 + k) * ks + p] = hi;
-                zl[(s0 + k) * ks + p] = (bf16)(raw[i][k] - to_f32(hi));
+                const float a0 = raw[2 * i][k], a1 = raw[2 * i + 1][k];
+                const bf16 h0 = (bf16)a0, h1 = (bf16)a1;
+                const bf16 l0 = (bf16)(a0 - to_f32(h0)), l1 = (bf16)(a1 - to_f32(h1));
+                const uint32_t hw = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                const uint32_t lw = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+                *(uint32_t*)(zh + (s0 + k) * ks + p) = hw;
+                *(uint32_t*)(zl + (s0 + k) * ks + p) = lw;
             }
         }
     }
 };
 
 template <int OP, int P, int S, int T>
-__global__ __launch_bounds__(2 * T) void bwd_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     using Cfg = BmCfg<OP, P, S, T>;
-    constexpr int N = Cfg::N, NKS = Cfg::NKS, NNT = Cfg::NNT;
+    constexpr int N = Cfg::N, NKS = Cfg::NKS, NNH = Cfg::NNH;
     constexpr int KS = Cfg::KS, VS = Cfg::VS, NTHR = Cfg::NTHR, NIT = Cfg::NIT;
     constexpr bool REV = Cfg::REV, QSPLIT = Cfg::QSPLIT, KSPLIT = Cfg::KSPLIT,
                    VSPLIT = Cfg::VSPLIT;
@@ -172,6 +185,7 @@ __global__ __launch_bounds__(2 * T) void bwd_mfma_kernel(BwdArgs a) {
     sp += 2 * Cfg::Z_BYTES;
     float* s_g = (float*)sp;                             // [T]
     float* s_dt = s_g + T;                               // [T]
+    float* s_red = s_dt + T;                             // [2 halves][2][T] row-sum partials
 
     const int L = a.L, H = a.H, NG = a.G;
     const int nC = (L + T - 1) / T;
@@ -179,7 +193,9 @@ __global__ __launch_bounds__(2 * T) void bwd_mfma_kernel(BwdArgs a) {
     const int h = id % H, c = (id / H) % nC, b = id / (H * nC);
     const int g = h / (H / NG);
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wid % Cfg::NW, half = wid / Cfg::NW;  // row-tile pair, column half
+    const int nt0 = half * NNH;
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T, rows = min(T, L - t0);
     const size_t HP = (size_t)H * P, GS = (size_t)NG * S;
@@ -254,27 +270,28 @@ __global__ __launch_bounds__(2 * T) void bwd_mfma_kernel(BwdArgs a) {
             qf[ks].v = hi;
             ql[ks].v = lo;
         }
-        f32x4 acc[NNT];
+        f32x4 acc[NNH];  // output columns 16 (nt0 + j) + l16
 #pragma unroll
-        for (int nt = 0; nt < NNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NNH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         // carried-state term Q_i . Z, scaled per row
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) {
+            for (int j = 0; j < NNH; ++j) {
+                const int o = ((nt0 + j) * 16 + l16) * KS + ks * 32 + g4 * 8;
                 Frag<bf16> zh, zl;
-                zh.v = *(const bf16x8*)(s_zh + (nt * 16 + l16) * KS + ks * 32 + g4 * 8);
-                zl.v = *(const bf16x8*)(s_zl + (nt * 16 + l16) * KS + ks * 32 + g4 * 8);
-                mma(acc[nt], qf[ks], zh);
-                mma(acc[nt], qf[ks], zl);
-                if constexpr (QSPLIT) mma(acc[nt], ql[ks], zh);
+                zh.v = *(const bf16x8*)(s_zh + o);
+                zl.v = *(const bf16x8*)(s_zl + o);
+                mma(acc[j], qf[ks], zh);
+                mma(acc[j], qf[ks], zl);
+                if constexpr (QSPLIT) mma(acc[j], ql[ks], zh);
             }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float gi = s_g[I0 + 4 * g4 + r];
             const float sc = exp2_fast(REV ? g_end - gi : gi);
 #pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) acc[nt][r] *= sc;
+            for (int j = 0; j < NNH; ++j) acc[j][r] *= sc;
         }
         // intra-chunk term over 32-wide blocks of j
         const float gi = s_g[qrow];
@@ -317,41 +334,68 @@ __global__ __launch_bounds__(2 * T) void bwd_mfma_kernel(BwdArgs a) {
                 }
             }
 #pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) {
+            for (int j = 0; j < NNH; ++j) {
+                const int n0 = (nt0 + j) * 16;
                 Frag<bf16> vf;
-                vf.v = __builtin_shufflevector(lds_col4(s_v, VS, J0 + 4 * g4, nt * 16, lane),
-                                               lds_col4(s_v, VS, J0 + 16 + 4 * g4, nt * 16, lane),
+                vf.v = __builtin_shufflevector(lds_col4(s_v, VS, J0 + 4 * g4, n0, lane),
+                                               lds_col4(s_v, VS, J0 + 16 + 4 * g4, n0, lane),
                                                0, 1, 2, 3, 4, 5, 6, 7);
-                mma(acc[nt], wf, vf);
-                mma(acc[nt], wl, vf);
+                mma(acc[j], wf, vf);
+                mma(acc[j], wl, vf);
                 if constexpr (VSPLIT) {
-                    vf.v = __builtin_shufflevector(
-                        lds_col4(s_vl, VS, J0 + 4 * g4, nt * 16, lane),
-                        lds_col4(s_vl, VS, J0 + 16 + 4 * g4, nt * 16, lane), 0, 1, 2, 3, 4, 5,
-                        6, 7);
-                    mma(acc[nt], wf, vf);
+                    vf.v = __builtin_shufflevector(lds_col4(s_vl, VS, J0 + 4 * g4, n0, lane),
+                                                   lds_col4(s_vl, VS, J0 + 16 + 4 * g4, n0, lane),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+                    mma(acc[j], wf, vf);
                 }
             }
         }
         // ---- epilogue: element (row I0 + 4 g4 + r, column 16 nt + l16) of the tile ------
+        // Rows sit in the per-lane offset, the head in the uniform one; rows of a partial
+        // chunk past its real tokens fall outside the descriptors (stores dropped, loads 0).
+        const uint32_t row0 = (uint32_t)(I0 + 4 * g4);
         float red[4] = {0.f, 0.f, 0.f, 0.f}, red2[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (OP == kOpC || OP == kOpB) {
+            float* outp = (OP == kOpC ? a.dCh : a.dBh) + ((size_t)b * L + t0) * H * S;
+            const BufRsrc ro = make_rsrc(outp, (uint32_t)(rows * H * S * 4));
+            const BufRsrc rc = make_rsrc(cr, (uint32_t)(rows * GS * 2));
+            const uint32_t hs4 = (uint32_t)(H * S * 4), soff = (uint32_t)(h * S * 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = I0 + 4 * g4 + r;
-            if (i >= rows) continue;
-            const size_t tok = ((size_t)b * L + t0 + i) * H + h;
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t vo = (row0 + r) * hs4 + l16 * 4;
+                const uint32_t vc = (row0 + r) * (uint32_t)(GS * 2) + l16 * 2;
+                const float sc = OP == kOpB ? s_dt[row0 + r] : 1.f;
 #pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) {
-                const int n = nt * 16 + l16;
-                const float o = acc[nt][r];
-                if constexpr (OP == kOpC) {
-                    a.dCh[tok * S + n] = o;
-                    red[r] += o * to_f32(cr[i * GS + n]);
-                } else if constexpr (OP == kOpB) {
-                    a.dBh[tok * S + n] = s_dt[i] * o;
-                } else {
-                    const float dyv = dyr[i * HP + n], xv = to_f32(xr[i * HP + n]);
-                    a.dx[tok * P + n] = dval * dyv + s_dt[i] * o;
+                for (int j = 0; j < NNH; ++j) {
+                    const int nt = nt0 + j;
+                    const float o = acc[j][r];
+                    buf_store_f32(sc * o, ro, vo + nt * 64, soff);
+                    if constexpr (OP == kOpC) {
+                        const uint16_t cb = __builtin_amdgcn_raw_buffer_load_b16(rc, vc + nt * 32, 0, 0);
+                        red[r] += o * to_f32(__builtin_bit_cast(bf16, cb));
+                    }
+                }
+            }
+        } else {
+            const size_t base = ((size_t)b * L + t0) * HP;
+            const BufRsrc rdx = make_rsrc(a.dx + base, (uint32_t)(rows * HP * 4));
+            const BufRsrc rdy = make_rsrc(a.dy + base, (uint32_t)(rows * HP * 4));
+            const BufRsrc rxx = make_rsrc((const bf16*)a.x + base, (uint32_t)(rows * HP * 2));
+            const uint32_t hp4 = (uint32_t)(HP * 4), soff4 = (uint32_t)(h * P * 4);
+            const uint32_t soff2 = (uint32_t)(h * P * 2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t vo = (row0 + r) * hp4 + l16 * 4;
+                const uint32_t vx = (row0 + r) * (uint32_t)(HP * 2) + l16 * 2;
+                const float dtr = s_dt[row0 + r];
+#pragma unroll
+                for (int j = 0; j < NNH; ++j) {
+                    const int nt = nt0 + j;
+                    const float o = acc[j][r];
+                    const float dyv = buf_load_f32(rdy, vo + nt * 64, soff4);
+                    const uint16_t xb = __builtin_amdgcn_raw_buffer_load_b16(rxx, vx + nt * 32, soff2, 0);
+                    const float xv = to_f32(__builtin_bit_cast(bf16, xb));
+                    buf_store_f32(dval * dyv + dtr * o, rdx, vo + nt * 64, soff4);
                     red[r] += xv * o;
                     red2[r] += xv * dyv;
                 }
@@ -365,15 +409,23 @@ __global__ __launch_bounds__(2 * T) void bwd_mfma_kernel(BwdArgs a) {
                     red[r] += __shfl_xor(red[r], m, 64);
                     if constexpr (OP == kOpX) red2[r] += __shfl_xor(red2[r], m, 64);
                 }
-                const int i = I0 + 4 * g4 + r;
-                if (l16 == 0 && i < rows) {
-                    if constexpr (OP == kOpC) {
-                        a.q[bhl + i] = red[r];
-                    } else {
-                        a.v[bhl + i] = red[r];
-                        a.dyx[bhl + i] = red2[r];
-                    }
+                // this half's partial row sums; the halves are added after the loop
+                if (l16 == 0) {
+                    s_red[(half * 2) * T + I0 + 4 * g4 + r] = red[r];
+                    s_red[(half * 2 + 1) * T + I0 + 4 * g4 + r] = red2[r];
                 }
+            }
+        }
+    }
+    if constexpr (OP != kOpB) {
+        __syncthreads();
+        if (tid < rows) {
+            const float s0 = s_red[tid] + s_red[2 * T + tid];
+            if constexpr (OP == kOpC) {
+                a.q[bhl + tid] = s0;
+            } else {
+                a.v[bhl + tid] = s0;
+                a.dyx[bhl + tid] = s_red[T + tid] + s_red[3 * T + tid];
             }
         }
     }
@@ -507,7 +559,7 @@ hipError_t run_bwd_mfma(const BwdArgs& a, int batch, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const int nC = (a.L + T - 1) / T;
-    kern<<<batch * nC * a.H, 2 * T, Cfg::LDS_BYTES, stream>>>(a);
+    kern<<<batch * nC * a.H, 4 * T, Cfg::LDS_BYTES, stream>>>(a);
     return hipGetLastError();
 }
 
