@@ -79,6 +79,7 @@ struct BwdArgs {
     float* q;         // [B, H, L]
     float* dyx;       // [B, H, L]
     int L, H, G, T;
+    int NH;           // heads per workgroup of the matrix-core kernels (divides H / G)
 };
 
 struct BwdUnit {

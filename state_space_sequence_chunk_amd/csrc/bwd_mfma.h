@@ -165,10 +165,11 @@ struct StateTStager {
 template <int OP, int P, int S, int T>
 __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     using Cfg = BmCfg<OP, P, S, T>;
-    constexpr int N = Cfg::N, NKS = Cfg::NKS, NNH = Cfg::NNH;
+    constexpr int N = Cfg::N, KD = Cfg::KD, NKS = Cfg::NKS, NNH = Cfg::NNH;
     constexpr int KS = Cfg::KS, VS = Cfg::VS, NTHR = Cfg::NTHR, NIT = Cfg::NIT;
     constexpr bool REV = Cfg::REV, QSPLIT = Cfg::QSPLIT, KSPLIT = Cfg::KSPLIT,
                    VSPLIT = Cfg::VSPLIT;
+    constexpr bool SUM = OP != kOpX;  // output summed over the workgroup's heads
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char* sp = smem;
@@ -187,11 +188,13 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     float* s_dt = s_g + T;                               // [T]
     float* s_red = s_dt + T;                             // [2 halves][2][T] row-sum partials
 
-    const int L = a.L, H = a.H, NG = a.G;
-    const int nC = (L + T - 1) / T;
+    // workgroup: (batch, chunk, block of NH heads of one group)
+    const int L = a.L, H = a.H, NG = a.G, NH = a.NH;
+    const int nC = (L + T - 1) / T, nhb = H / NH;
     const int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = id % H, c = (id / H) % nC, b = id / (H * nC);
-    const int g = h / (H / NG);
+    const int hb = id % nhb, c = (id / nhb) % nC, b = id / (nhb * nC);
+    const int h_first = hb * NH;
+    const int g = h_first / (H / NG);  // NH divides the heads per group
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave = wid % Cfg::NW, half = wid / Cfg::NW;  // row-tile pair, column half
@@ -199,235 +202,284 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T, rows = min(T, L - t0);
     const size_t HP = (size_t)H * P, GS = (size_t)NG * S;
-    const bf16* xr = (const bf16*)a.x + (((size_t)b * L + t0) * H + h) * P;    // stride HP
-    const float* dyr = a.dy + (((size_t)b * L + t0) * H + h) * P;             // stride HP
-    const bf16* br = (const bf16*)a.Bm + (((size_t)b * L + t0) * NG + g) * S;  // stride GS
-    const bf16* cr = (const bf16*)a.Cm + (((size_t)b * L + t0) * NG + g) * S;  // stride GS
-    const size_t bhl = ((size_t)b * H + h) * L + t0;
-    const float* zsrc = (OP == kOpC ? a.Hc : a.R) + (((size_t)b * H + h) * nC + c) * P * S;
+    const size_t tok0 = (size_t)b * L + t0;
+    const bf16* br = (const bf16*)a.Bm + (tok0 * NG + g) * S;  // stride GS
+    const bf16* cr = (const bf16*)a.Cm + (tok0 * NG + g) * S;  // stride GS
+    auto xr_of = [&](int h) { return (const bf16*)a.x + (tok0 * H + h) * P; };  // stride HP
+    auto dyr_of = [&](int h) { return a.dy + (tok0 * H + h) * P; };             // stride HP
+    auto bhl_of = [&](int h) { return ((size_t)b * H + h) * L + t0; };
+    auto zsrc_of = [&](int h) {
+        return (OP == kOpC ? a.Hc : a.R) + (((size_t)b * H + h) * nC + c) * P * S;
+    };
 
-    // ---- staging: K and V rows, the state (high/low bf16), G and dt ---------------------
-    // (every load in flight before the first LDS write)
+    // ---- staging ----------------------------------------------------------------------
+    // Shared by the heads: V = B (dC), V = C (dB), K = C (dxh). Per head: K = x (dC),
+    // K = dy (dB), V = dy (dxh), the state Z (high/low bf16), G and dt. The next head's
+    // loads are in flight while the current head computes.
     using KSrc = std::conditional_t<OP == kOpB, float, bf16>;
     using VSrc = std::conditional_t<OP == kOpX, float, bf16>;
-    constexpr int KD = Cfg::KD;
+    using ZStage = std::conditional_t<OP == kOpX, Stager<float, NTHR, P, S, true>,
+                                      StateTStager<NTHR, P, S>>;
     Stager<KSrc, NTHR, T, KD, KSPLIT> stk;
     Stager<VSrc, NTHR, T, N, VSPLIT> stv;
-    if constexpr (OP == kOpC) {
-        stk.load(xr, HP, rows, tid);
-        stv.load(br, GS, rows, tid);
-    } else if constexpr (OP == kOpB) {
-        stk.load(dyr, HP, rows, tid);
-        stv.load(cr, GS, rows, tid);
-    } else {
-        stk.load(cr, GS, rows, tid);
-        stv.load(dyr, HP, rows, tid);
-    }
+    ZStage stz;
     float pg = 0.f, pdt = 0.f;
-    if (tid < T) {
-        pg = a.Gc[bhl + min(tid, rows - 1)];
-        pdt = tid < rows ? a.dtt[bhl + tid] : 0.f;
-    }
-    if constexpr (OP == kOpX) {
-        // Z[n = p][k = s] = R_c[p][s]: rows of the state as they are
-        Stager<float, NTHR, P, S, true> stz;
-        stz.load(zsrc, S, P, tid);
-        stk.store(s_k, s_kl, KS, tid);
-        stv.store(s_v, s_vl, VS, tid);
+    auto load_head = [&](int h) {
+        if constexpr (OP == kOpC) stk.load(xr_of(h), HP, rows, tid);
+        else if constexpr (OP == kOpB) stk.load(dyr_of(h), HP, rows, tid);
+        else stv.load(dyr_of(h), HP, rows, tid);
+        if constexpr (OP == kOpX) stz.load(zsrc_of(h), S, P, tid);
+        else stz.load(zsrc_of(h), tid);
+        if (tid < T) {
+            pg = a.Gc[bhl_of(h) + min(tid, rows - 1)];
+            pdt = tid < rows ? a.dtt[bhl_of(h) + tid] : 0.f;
+        }
+    };
+    auto store_head = [&]() {
+        if constexpr (OP == kOpX) stv.store(s_v, s_vl, VS, tid);
+        else stk.store(s_k, s_kl, KS, tid);
         stz.store(s_zh, s_zl, KS, tid);
-    } else {
-        // Z[n = s][k = p] = state[p][s]: the state transposed
-        StateTStager<NTHR, P, S> stz;
-        stz.load(zsrc, tid);
-        stk.store(s_k, s_kl, KS, tid);
-        stv.store(s_v, s_vl, VS, tid);
-        stz.store(s_zh, s_zl, KS, tid);
-    }
-    if (tid < T) {
-        s_g[tid] = pg;
-        s_dt[tid] = pdt;
-    }
+        if (tid < T) {
+            s_g[tid] = pg;
+            s_dt[tid] = pdt;
+        }
+    };
+    if constexpr (OP == kOpC) stv.load(br, GS, rows, tid);
+    else if constexpr (OP == kOpB) stv.load(cr, GS, rows, tid);
+    else stk.load(cr, GS, rows, tid);
+    load_head(h_first);
+    if constexpr (OP == kOpX) stk.store(s_k, nullptr, KS, tid);
+    else stv.store(s_v, nullptr, VS, tid);
+    store_head();
     __syncthreads();
 
-    const float g_end = s_g[T - 1];  // = G at the last real token (padded rows repeat it)
-    const float dval = a.D ? a.D[h] : 0.f;
+    const uint32_t row0s[2] = {(uint32_t)(wave * 16 + 4 * g4),
+                               (uint32_t)((NIT - 1 - wave) * 16 + 4 * g4)};
+    // dC: C's values at this lane's output elements (the same for every head)
+    float cval[SUM && OP == kOpC ? 2 : 1][NNH][4];
+    if constexpr (OP == kOpC) {
+        const BufRsrc rc = make_rsrc(cr, (uint32_t)(rows * GS * 2));
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < NNH; ++j) {
+                    const uint32_t vc = (row0s[qi] + r) * (uint32_t)(GS * 2) + l16 * 2;
+                    const uint16_t cb =
+                        __builtin_amdgcn_raw_buffer_load_b16(rc, vc + (nt0 + j) * 32, 0, 0);
+                    cval[qi][j][r] = to_f32(__builtin_bit_cast(bf16, cb));
+                }
+    }
+    f32x4 tot[SUM ? 2 : 1][NNH];  // sums over the heads (dC, dB)
+#pragma unroll
+    for (int qi = 0; qi < (SUM ? 2 : 1); ++qi)
+#pragma unroll
+        for (int j = 0; j < NNH; ++j) tot[qi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll 1
-    for (int qi = 0; qi < 2; ++qi) {
-        const int it = qi == 0 ? wave : NIT - 1 - wave;  // this wave's row tiles
-        const int I0 = it * 16;
-        // Q's rows of this tile (lane: row I0 + l16, k = 32 ks + 8 g4 + v)
-        Frag<bf16> qf[NKS], ql[NKS];
-        const int qrow = I0 + l16;
+    for (int hh = 0; hh < NH; ++hh) {
+        const int h = h_first + hh;
+        if (hh + 1 < NH) load_head(h + 1);  // lands in registers while this head computes
+        const float g_end = s_g[T - 1];     // = G at the last real token
+        const float dval = a.D ? a.D[h] : 0.f;
+        const bf16* xr = xr_of(h);
+        const float* dyr = dyr_of(h);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int k0 = ks * 32 + g4 * 8;
-            bf16x8 hi = bf16x8{0, 0, 0, 0, 0, 0, 0, 0}, lo = hi;
-            if (qrow < rows) {
-                if constexpr (OP == kOpC) ld8_split(dyr + qrow * HP + k0, hi, lo);
-                else if constexpr (OP == kOpB) ld8_split(xr + qrow * HP + k0, hi, lo);
-                else ld8_split(br + qrow * GS + k0, hi, lo);
+        for (int qi = 0; qi < 2; ++qi) {
+            const int it = qi == 0 ? wave : NIT - 1 - wave;  // this wave's row tiles
+            const int I0 = it * 16;
+            // Q's rows of this tile (lane: row I0 + l16, k = 32 ks + 8 g4 + v)
+            Frag<bf16> qf[NKS], ql[NKS];
+            const int qrow = I0 + l16;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int k0 = ks * 32 + g4 * 8;
+                bf16x8 hi = bf16x8{0, 0, 0, 0, 0, 0, 0, 0}, lo = hi;
+                if (qrow < rows) {
+                    if constexpr (OP == kOpC) ld8_split(dyr + qrow * HP + k0, hi, lo);
+                    else if constexpr (OP == kOpB) ld8_split(xr + qrow * HP + k0, hi, lo);
+                    else ld8_split(br + qrow * GS + k0, hi, lo);
+                }
+                qf[ks].v = hi;
+                ql[ks].v = lo;
             }
-            qf[ks].v = hi;
-            ql[ks].v = lo;
-        }
-        f32x4 acc[NNH];  // output columns 16 (nt0 + j) + l16
+            f32x4 acc[NNH];  // output columns 16 (nt0 + j) + l16
 #pragma unroll
-        for (int j = 0; j < NNH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // carried-state term Q_i . Z, scaled per row
+            for (int j = 0; j < NNH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // carried-state term Q_i . Z, scaled per row
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int j = 0; j < NNH; ++j) {
-                const int o = ((nt0 + j) * 16 + l16) * KS + ks * 32 + g4 * 8;
-                Frag<bf16> zh, zl;
-                zh.v = *(const bf16x8*)(s_zh + o);
-                zl.v = *(const bf16x8*)(s_zl + o);
-                mma(acc[j], qf[ks], zh);
-                mma(acc[j], qf[ks], zl);
-                if constexpr (QSPLIT) mma(acc[j], ql[ks], zh);
+                for (int j = 0; j < NNH; ++j) {
+                    const int o = ((nt0 + j) * 16 + l16) * KS + ks * 32 + g4 * 8;
+                    Frag<bf16> zh, zl;
+                    zh.v = *(const bf16x8*)(s_zh + o);
+                    zl.v = *(const bf16x8*)(s_zl + o);
+                    mma(acc[j], qf[ks], zh);
+                    mma(acc[j], qf[ks], zl);
+                    if constexpr (QSPLIT) mma(acc[j], ql[ks], zh);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float gi = s_g[I0 + 4 * g4 + r];
+                const float sc = exp2_fast(REV ? g_end - gi : gi);
+#pragma unroll
+                for (int j = 0; j < NNH; ++j) acc[j][r] *= sc;
             }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float gi = s_g[I0 + 4 * g4 + r];
-            const float sc = exp2_fast(REV ? g_end - gi : gi);
-#pragma unroll
-            for (int j = 0; j < NNH; ++j) acc[j][r] *= sc;
-        }
-        // intra-chunk term over 32-wide blocks of j
-        const float gi = s_g[qrow];
-        const int jp_lo = REV ? it / 2 : 0, jp_hi = REV ? NIT / 2 - 1 : it / 2;
+            // intra-chunk term over 32-wide blocks of j
+            const float gi = s_g[qrow];
+            const int jp_lo = REV ? it / 2 : 0, jp_hi = REV ? NIT / 2 - 1 : it / 2;
 #pragma unroll 1
-        for (int jp = jp_lo; jp <= jp_hi; ++jp) {
-            const int J0 = jp * 32;
-            f32x4 zt[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            for (int jp = jp_lo; jp <= jp_hi; ++jp) {
+                const int J0 = jp * 32;
+                f32x4 zt[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt)
+                for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int o = (J0 + jt * 16 + l16) * KS + ks * 32 + g4 * 8;
-                    Frag<bf16> kf;
-                    kf.v = *(const bf16x8*)(s_k + o);
-                    mma(zt[jt], kf, qf[ks]);
-                    if constexpr (QSPLIT) mma(zt[jt], kf, ql[ks]);
-                    if constexpr (KSPLIT) {
-                        kf.v = *(const bf16x8*)(s_kl + o);
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int o = (J0 + jt * 16 + l16) * KS + ks * 32 + g4 * 8;
+                        Frag<bf16> kf;
+                        kf.v = *(const bf16x8*)(s_k + o);
                         mma(zt[jt], kf, qf[ks]);
+                        if constexpr (QSPLIT) mma(zt[jt], kf, ql[ks]);
+                        if constexpr (KSPLIT) {
+                            kf.v = *(const bf16x8*)(s_kl + o);
+                            mma(zt[jt], kf, qf[ks]);
+                        }
+                    }
+                // W[i][j] in the A-operand layout (row i = qrow, item 4 jt + r <-> j), split
+                // into bf16 high and low parts
+                Frag<bf16> wf, wl;
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+                    const f32x4 gj = *(const f32x4*)(s_g + J0 + jt * 16 + 4 * g4);
+                    f32x4 wj = f32x4{1.f, 1.f, 1.f, 1.f};
+                    if constexpr (!REV) wj = *(const f32x4*)(s_dt + J0 + jt * 16 + 4 * g4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = J0 + jt * 16 + 4 * g4 + r;
+                        const bool keep = REV ? j >= qrow : j <= qrow;
+                        const float e = exp2_fast(REV ? gj[r] - gi : gi - gj[r]);
+                        const float w = keep ? e * wj[r] * zt[jt][r] : 0.f;
+                        const bf16 hi = (bf16)w;
+                        wf.v[jt * 4 + r] = hi;
+                        wl.v[jt * 4 + r] = (bf16)(w - to_f32(hi));
                     }
                 }
-            // W[i][j] in the A-operand layout (row i = qrow, item 4 jt + r <-> j), split
-            // into bf16 high and low parts
-            Frag<bf16> wf, wl;
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                const f32x4 gj = *(const f32x4*)(s_g + J0 + jt * 16 + 4 * g4);
-                f32x4 wj = f32x4{1.f, 1.f, 1.f, 1.f};
-                if constexpr (!REV) wj = *(const f32x4*)(s_dt + J0 + jt * 16 + 4 * g4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = J0 + jt * 16 + 4 * g4 + r;
-                    const bool keep = REV ? j >= qrow : j <= qrow;
-                    const float e = exp2_fast(REV ? gj[r] - gi : gi - gj[r]);
-                    const float w = keep ? e * wj[r] * zt[jt][r] : 0.f;
-                    const bf16 hi = (bf16)w;
-                    wf.v[jt * 4 + r] = hi;
-                    wl.v[jt * 4 + r] = (bf16)(w - to_f32(hi));
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < NNH; ++j) {
-                const int n0 = (nt0 + j) * 16;
-                Frag<bf16> vf;
-                vf.v = __builtin_shufflevector(lds_col4(s_v, VS, J0 + 4 * g4, n0, lane),
-                                               lds_col4(s_v, VS, J0 + 16 + 4 * g4, n0, lane),
-                                               0, 1, 2, 3, 4, 5, 6, 7);
-                mma(acc[j], wf, vf);
-                mma(acc[j], wl, vf);
-                if constexpr (VSPLIT) {
-                    vf.v = __builtin_shufflevector(lds_col4(s_vl, VS, J0 + 4 * g4, n0, lane),
-                                                   lds_col4(s_vl, VS, J0 + 16 + 4 * g4, n0, lane),
+                for (int j = 0; j < NNH; ++j) {
+                    const int n0 = (nt0 + j) * 16;
+                    Frag<bf16> vf;
+                    vf.v = __builtin_shufflevector(lds_col4(s_v, VS, J0 + 4 * g4, n0, lane),
+                                                   lds_col4(s_v, VS, J0 + 16 + 4 * g4, n0, lane),
                                                    0, 1, 2, 3, 4, 5, 6, 7);
                     mma(acc[j], wf, vf);
-                }
-            }
-        }
-        // ---- epilogue: element (row I0 + 4 g4 + r, column 16 nt + l16) of the tile ------
-        // Rows sit in the per-lane offset, the head in the uniform one; rows of a partial
-        // chunk past its real tokens fall outside the descriptors (stores dropped, loads 0).
-        const uint32_t row0 = (uint32_t)(I0 + 4 * g4);
-        float red[4] = {0.f, 0.f, 0.f, 0.f}, red2[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (OP == kOpC || OP == kOpB) {
-            float* outp = (OP == kOpC ? a.dCh : a.dBh) + ((size_t)b * L + t0) * H * S;
-            const BufRsrc ro = make_rsrc(outp, (uint32_t)(rows * H * S * 4));
-            const BufRsrc rc = make_rsrc(cr, (uint32_t)(rows * GS * 2));
-            const uint32_t hs4 = (uint32_t)(H * S * 4), soff = (uint32_t)(h * S * 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t vo = (row0 + r) * hs4 + l16 * 4;
-                const uint32_t vc = (row0 + r) * (uint32_t)(GS * 2) + l16 * 2;
-                const float sc = OP == kOpB ? s_dt[row0 + r] : 1.f;
-#pragma unroll
-                for (int j = 0; j < NNH; ++j) {
-                    const int nt = nt0 + j;
-                    const float o = acc[j][r];
-                    buf_store_f32(sc * o, ro, vo + nt * 64, soff);
-                    if constexpr (OP == kOpC) {
-                        const uint16_t cb = __builtin_amdgcn_raw_buffer_load_b16(rc, vc + nt * 32, 0, 0);
-                        red[r] += o * to_f32(__builtin_bit_cast(bf16, cb));
+                    mma(acc[j], wl, vf);
+                    if constexpr (VSPLIT) {
+                        vf.v = __builtin_shufflevector(
+                            lds_col4(s_vl, VS, J0 + 4 * g4, n0, lane),
+                            lds_col4(s_vl, VS, J0 + 16 + 4 * g4, n0, lane), 0, 1, 2, 3, 4, 5,
+                            6, 7);
+                        mma(acc[j], wf, vf);
                     }
                 }
             }
-        } else {
-            const size_t base = ((size_t)b * L + t0) * HP;
-            const BufRsrc rdx = make_rsrc(a.dx + base, (uint32_t)(rows * HP * 4));
-            const BufRsrc rdy = make_rsrc(a.dy + base, (uint32_t)(rows * HP * 4));
-            const BufRsrc rxx = make_rsrc((const bf16*)a.x + base, (uint32_t)(rows * HP * 2));
-            const uint32_t hp4 = (uint32_t)(HP * 4), soff4 = (uint32_t)(h * P * 4);
-            const uint32_t soff2 = (uint32_t)(h * P * 2);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t vo = (row0 + r) * hp4 + l16 * 4;
-                const uint32_t vx = (row0 + r) * (uint32_t)(HP * 2) + l16 * 2;
-                const float dtr = s_dt[row0 + r];
-#pragma unroll
-                for (int j = 0; j < NNH; ++j) {
-                    const int nt = nt0 + j;
-                    const float o = acc[j][r];
-                    const float dyv = buf_load_f32(rdy, vo + nt * 64, soff4);
-                    const uint16_t xb = __builtin_amdgcn_raw_buffer_load_b16(rxx, vx + nt * 32, soff2, 0);
-                    const float xv = to_f32(__builtin_bit_cast(bf16, xb));
-                    buf_store_f32(dval * dyv + dtr * o, rdx, vo + nt * 64, soff4);
-                    red[r] += xv * o;
-                    red2[r] += xv * dyv;
-                }
-            }
-        }
-        if constexpr (OP != kOpB) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-#pragma unroll
-                for (int m = 1; m < 16; m <<= 1) {
-                    red[r] += __shfl_xor(red[r], m, 64);
-                    if constexpr (OP == kOpX) red2[r] += __shfl_xor(red2[r], m, 64);
-                }
-                // this half's partial row sums; the halves are added after the loop
-                if (l16 == 0) {
-                    s_red[(half * 2) * T + I0 + 4 * g4 + r] = red[r];
-                    s_red[(half * 2 + 1) * T + I0 + 4 * g4 + r] = red2[r];
-                }
-            }
-        }
-    }
-    if constexpr (OP != kOpB) {
-        __syncthreads();
-        if (tid < rows) {
-            const float s0 = s_red[tid] + s_red[2 * T + tid];
+            // ---- this head's contribution: element (row I0 + 4 g4 + r, column
+            // 16 (nt0 + j) + l16) of the tile
+            const uint32_t row0 = row0s[qi];
+            float red[4] = {0.f, 0.f, 0.f, 0.f}, red2[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (OP == kOpC) {
-                a.q[bhl + tid] = s0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int j = 0; j < NNH; ++j) {
+                        red[r] += acc[j][r] * cval[qi][j][r];
+                        tot[qi][j][r] += acc[j][r];
+                    }
+            } else if constexpr (OP == kOpB) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float dti = s_dt[row0 + r];
+#pragma unroll
+                    for (int j = 0; j < NNH; ++j) tot[qi][j][r] += dti * acc[j][r];
+                }
             } else {
-                a.v[bhl + tid] = s0;
-                a.dyx[bhl + tid] = s_red[T + tid] + s_red[3 * T + tid];
+                // rows sit in the per-lane offset, the head in the uniform one; rows of a
+                // partial chunk past its real tokens fall outside the descriptors
+                const size_t base = tok0 * HP;
+                const BufRsrc rdx = make_rsrc(a.dx + base, (uint32_t)(rows * HP * 4));
+                const BufRsrc rdy = make_rsrc(a.dy + base, (uint32_t)(rows * HP * 4));
+                const BufRsrc rxx = make_rsrc((const bf16*)a.x + base, (uint32_t)(rows * HP * 2));
+                const uint32_t hp4 = (uint32_t)(HP * 4), soff4 = (uint32_t)(h * P * 4);
+                const uint32_t soff2 = (uint32_t)(h * P * 2);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t vo = (row0 + r) * hp4 + l16 * 4;
+                    const uint32_t vx = (row0 + r) * (uint32_t)(HP * 2) + l16 * 2;
+                    const float dtr = s_dt[row0 + r];
+#pragma unroll
+                    for (int j = 0; j < NNH; ++j) {
+                        const int nt = nt0 + j;
+                        const float o = acc[j][r];
+                        const float dyv = buf_load_f32(rdy, vo + nt * 64, soff4);
+                        const uint16_t xb =
+                            __builtin_amdgcn_raw_buffer_load_b16(rxx, vx + nt * 32, soff2, 0);
+                        const float xv = to_f32(__builtin_bit_cast(bf16, xb));
+                        buf_store_f32(dval * dyv + dtr * o, rdx, vo + nt * 64, soff4);
+                        red[r] += xv * o;
+                        red2[r] += xv * dyv;
+                    }
+                }
+            }
+            if constexpr (OP != kOpB) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                    for (int m = 1; m < 16; m <<= 1) {
+                        red[r] += __shfl_xor(red[r], m, 64);
+                        if constexpr (OP == kOpX) red2[r] += __shfl_xor(red2[r], m, 64);
+                    }
+                    // this half's partial row sums; the halves are added below
+                    if (l16 == 0) {
+                        s_red[(half * 2) * T + row0 + r] = red[r];
+                        s_red[(half * 2 + 1) * T + row0 + r] = red2[r];
+                    }
+                }
             }
         }
+        __syncthreads();  // every wave is done with this head's LDS and partials
+        if constexpr (OP != kOpB) {
+            const size_t bhl = bhl_of(h);
+            if (tid < rows) {
+                const float s0 = s_red[tid] + s_red[2 * T + tid];
+                if constexpr (OP == kOpC) {
+                    a.q[bhl + tid] = s0;
+                } else {
+                    a.v[bhl + tid] = s0;
+                    a.dyx[bhl + tid] = s_red[T + tid] + s_red[3 * T + tid];
+                }
+            }
+        }
+        if (hh + 1 < NH) store_head();
+        __syncthreads();
+    }
+
+    // ---- dC, dB: the sum over this workgroup's heads, [B, L, H / NH, S] (the output itself
+    // when the workgroup holds all heads of its group)
+    if constexpr (SUM) {
+        float* outp = (OP == kOpC ? a.dCh : a.dBh) + tok0 * nhb * S;
+        const BufRsrc ro = make_rsrc(outp, (uint32_t)(rows * nhb * S * 4));
+        const uint32_t hs4 = (uint32_t)(nhb * S * 4), soff = (uint32_t)(hb * S * 4);
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t vo = (row0s[qi] + r) * hs4 + l16 * 4;
+#pragma unroll
+                for (int j = 0; j < NNH; ++j)
+                    buf_store_f32(tot[qi][j][r], ro, vo + (nt0 + j) * 64, soff);
+            }
     }
 }
 
@@ -559,7 +611,7 @@ hipError_t run_bwd_mfma(const BwdArgs& a, int batch, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const int nC = (a.L + T - 1) / T;
-    kern<<<batch * nC * a.H, 4 * T, Cfg::LDS_BYTES, stream>>>(a);
+    kern<<<batch * nC * (a.H / a.NH), 4 * T, Cfg::LDS_BYTES, stream>>>(a);
     return hipGetLastError();
 }
 

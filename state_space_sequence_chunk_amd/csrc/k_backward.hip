@@ -146,6 +146,15 @@ static hipError_t fill_zero(float* p, size_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Heads per workgroup of the matrix-core kernels: the largest divisor of the heads per
+// group that still leaves a workgroup for every compute unit.
+static int bwd_heads_per_block(int B, int nC, int H, int hpg) {
+    int best = 1;
+    for (int nh = 1; nh <= hpg; ++nh)
+        if (hpg % nh == 0 && (long)B * nC * (H / nh) >= 256) best = nh;
+    return best;
+}
+
 hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipStream_t s) {
     const int B = d.batch, L = d.seqlen, H = d.nheads, P = d.headdim, S = d.dstate;
     const int G = d.ngroups, T = d.chunk, nC = d.nchunks(), PS = P * S;
@@ -175,7 +184,7 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
     a.dBh = hpg == 1 ? k.dB : k.ws.dBh;
     a.dCh = hpg == 1 ? k.dC : k.ws.dCh;
     a.v = k.ws.v; a.q = k.ws.q; a.dyx = k.ws.dyx;
-    a.L = L; a.H = H; a.G = G; a.T = T;
+    a.L = L; a.H = H; a.G = G; a.T = T; a.NH = 1;
     auto chunks = [&](bool f, bool r, bool v) {
         return in_dtype == kBF16 ? launch_bwd_chunks_bf16(a, B, P, S, f, r, v, s)
                                  : launch_bwd_chunks_f32(a, B, P, S, f, r, v, s);
@@ -184,6 +193,14 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
     // which the caller has put in d): dC, dB and dx as chunked products; otherwise the
     // fp32 token walks
     const bool mfma = bwd_mfma_chunk(in_dtype, P, S) == T;
+    int parts = hpg;  // per-head dB, dC partials to sum per group
+    if (mfma) {
+        // dB and dC summed over blocks of a.NH heads inside the kernels
+        a.NH = bwd_heads_per_block(B, nC, H, hpg);
+        parts = hpg / a.NH;
+        a.dBh = parts == 1 ? k.dB : k.ws.dBh;
+        a.dCh = parts == 1 ? k.dC : k.ws.dCh;
+    }
     // per-chunk sums dR_c (over the consumed increments), and with the walks the forward
     // walk (dC, q)
     if (mfma) e = launch_bwd_dR_mfma_bf16(a, B, P, S, s);
@@ -201,10 +218,10 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
     bwd_scan_kernel<<<B * H, 256, 0, s>>>(k.ws.q, k.ws.v, k.ws.dyx, k.ws.dt_t, k.A, k.dfinal,
                                           k.ws.fin, k.ddt, k.ws.dA_bh, k.ws.dD_bh, L, H, PS);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (hpg > 1) {
+    if (parts > 1) {
         const size_t n = (size_t)B * L * G * S;
         bwd_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k.ws.dBh, k.ws.dCh, k.dB,
-                                                                      k.dC, n, hpg, S);
+                                                                      k.dC, n, parts, S);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     bwd_reduce_heads_kernel<<<(H + 255) / 256, 256, 0, s>>>(k.ws.dA_bh, k.ws.dD_bh, k.dA, k.dD,
