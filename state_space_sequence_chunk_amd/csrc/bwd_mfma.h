@@ -277,32 +277,81 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < NNH; ++j) tot[qi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Q's rows (lane: row I0 + l16, k = 32 ks + 8 g4 + v) are loaded one step ahead: the
+    // rows of the next (head, row tile) step are in flight during the current one
+    constexpr bool QF32 = OP == kOpC;
+    f32x4 qraw[NKS * (QF32 ? 2 : 1)];
+    auto load_q = [&](int h, int it) {
+        const int qrow = it * 16 + l16;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int k0 = ks * 32 + g4 * 8;
+            const bool ok = qrow < rows;
+            const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (OP == kOpC) {
+                const float* p = dyr_of(h) + qrow * HP + k0;
+                qraw[2 * ks] = ok ? *(const f32x4*)p : z4;
+                qraw[2 * ks + 1] = ok ? *(const f32x4*)(p + 4) : z4;
+            } else if constexpr (OP == kOpB) {
+                qraw[ks] = ok ? *(const f32x4*)(xr_of(h) + qrow * HP + k0) : z4;
+            } else {
+                qraw[ks] = ok ? *(const f32x4*)(br + qrow * GS + k0) : z4;
+            }
+        }
+    };
+    load_q(h_first, wave);
+
 #pragma unroll 1
     for (int hh = 0; hh < NH; ++hh) {
         const int h = h_first + hh;
         if (hh + 1 < NH) load_head(h + 1);  // lands in registers while this head computes
         const float g_end = s_g[T - 1];     // = G at the last real token
         const float dval = a.D ? a.D[h] : 0.f;
-        const bf16* xr = xr_of(h);
-        const float* dyr = dyr_of(h);
 #pragma unroll
         for (int qi = 0; qi < 2; ++qi) {
             const int it = qi == 0 ? wave : NIT - 1 - wave;  // this wave's row tiles
             const int I0 = it * 16;
-            // Q's rows of this tile (lane: row I0 + l16, k = 32 ks + 8 g4 + v)
-            Frag<bf16> qf[NKS], ql[NKS];
             const int qrow = I0 + l16;
+            Frag<bf16> qf[NKS], ql[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const int k0 = ks * 32 + g4 * 8;
-                bf16x8 hi = bf16x8{0, 0, 0, 0, 0, 0, 0, 0}, lo = hi;
-                if (qrow < rows) {
-                    if constexpr (OP == kOpC) ld8_split(dyr + qrow * HP + k0, hi, lo);
-                    else if constexpr (OP == kOpB) ld8_split(xr + qrow * HP + k0, hi, lo);
-                    else ld8_split(br + qrow * GS + k0, hi, lo);
+                if constexpr (QF32) {
+                    bf16x8 hi, lo;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float u0 = qraw[2 * ks][k], u1 = qraw[2 * ks + 1][k];
+                        hi[k] = (bf16)u0;
+                        hi[k + 4] = (bf16)u1;
+                        lo[k] = (bf16)(u0 - to_f32(hi[k]));
+                        lo[k + 4] = (bf16)(u1 - to_f32(hi[k + 4]));
+                    }
+                    qf[ks].v = hi;
+                    ql[ks].v = lo;
+                } else {
+                    qf[ks].v = __builtin_bit_cast(bf16x8, qraw[ks]);
                 }
-                qf[ks].v = hi;
-                ql[ks].v = lo;
+            }
+            // the next step's rows
+            if (qi == 0) load_q(h, NIT - 1 - wave);
+            else if (hh + 1 < NH) load_q(h + 1, wave);
+            // dxh epilogue: x and dy (fp32) at this lane's output elements, loaded ahead
+            // of use
+            const uint32_t row0 = row0s[qi];
+            float xv[OP == kOpX ? 4 : 1][NNH], dyv[OP == kOpX ? 4 : 1][NNH];
+            if constexpr (OP == kOpX) {
+                const BufRsrc rxx = make_rsrc((const bf16*)a.x + tok0 * HP, (uint32_t)(rows * HP * 2));
+                const BufRsrc rdy = make_rsrc(a.dy + tok0 * HP, (uint32_t)(rows * HP * 4));
+                const uint32_t soff2 = (uint32_t)(h * P * 2), soff4 = (uint32_t)(h * P * 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int j = 0; j < NNH; ++j) {
+                        const uint32_t vx = (row0 + r) * (uint32_t)(HP * 2) + l16 * 2;
+                        const uint16_t xb = __builtin_amdgcn_raw_buffer_load_b16(
+                            rxx, vx + (nt0 + j) * 32, soff2, 0);
+                        xv[r][j] = to_f32(__builtin_bit_cast(bf16, xb));
+                        dyv[r][j] = buf_load_f32(rdy, 2 * vx + (nt0 + j) * 64, soff4);
+                    }
             }
             f32x4 acc[NNH];  // output columns 16 (nt0 + j) + l16
 #pragma unroll
@@ -387,7 +436,6 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
             }
             // ---- this head's contribution: element (row I0 + 4 g4 + r, column
             // 16 (nt0 + j) + l16) of the tile
-            const uint32_t row0 = row0s[qi];
             float red[4] = {0.f, 0.f, 0.f, 0.f}, red2[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (OP == kOpC) {
 #pragma unroll
@@ -407,28 +455,19 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
             } else {
                 // rows sit in the per-lane offset, the head in the uniform one; rows of a
                 // partial chunk past its real tokens fall outside the descriptors
-                const size_t base = tok0 * HP;
-                const BufRsrc rdx = make_rsrc(a.dx + base, (uint32_t)(rows * HP * 4));
-                const BufRsrc rdy = make_rsrc(a.dy + base, (uint32_t)(rows * HP * 4));
-                const BufRsrc rxx = make_rsrc((const bf16*)a.x + base, (uint32_t)(rows * HP * 2));
+                const BufRsrc rdx = make_rsrc(a.dx + tok0 * HP, (uint32_t)(rows * HP * 4));
                 const uint32_t hp4 = (uint32_t)(HP * 4), soff4 = (uint32_t)(h * P * 4);
-                const uint32_t soff2 = (uint32_t)(h * P * 2);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t vo = (row0 + r) * hp4 + l16 * 4;
-                    const uint32_t vx = (row0 + r) * (uint32_t)(HP * 2) + l16 * 2;
                     const float dtr = s_dt[row0 + r];
 #pragma unroll
                     for (int j = 0; j < NNH; ++j) {
                         const int nt = nt0 + j;
                         const float o = acc[j][r];
-                        const float dyv = buf_load_f32(rdy, vo + nt * 64, soff4);
-                        const uint16_t xb =
-                            __builtin_amdgcn_raw_buffer_load_b16(rxx, vx + nt * 32, soff2, 0);
-                        const float xv = to_f32(__builtin_bit_cast(bf16, xb));
-                        buf_store_f32(dval * dyv + dtr * o, rdx, vo + nt * 64, soff4);
-                        red[r] += xv * o;
-                        red2[r] += xv * dyv;
+                        buf_store_f32(dval * dyv[r][j] + dtr * o, rdx, vo + nt * 64, soff4);
+                        red[r] += xv[r][j] * o;
+                        red2[r] += xv[r][j] * dyv[r][j];
                     }
                 }
             }

@@ -6,9 +6,11 @@
 
 namespace ssd {
 
+// 128 tokens where the plan fits (64 for headdim 128, whose 128-token dx kernel would
+// spill registers)
 template <int P, int S>
 constexpr int mfma_chunk() {
-    return bwd_mfma_fits<P, S, 128>() ? 128 : bwd_mfma_fits<P, S, 64>() ? 64 : 0;
+    return P <= 64 && bwd_mfma_fits<P, S, 128>() ? 128 : bwd_mfma_fits<P, S, 64>() ? 64 : 0;
 }
 
 template <int P, int S>

@@ -160,3 +160,16 @@ def test_backward_full_size_sampled_heads():
              "dA": got["dA"][heads], "dD": got["dD"][heads], "dh0": got["dh0"][:, heads]}
     check("2.7b-bf16 full size, heads " + str(heads), got_s, ref, "bf16",
           names=("dx", "ddt", "dA", "dD", "dh0"))
+
+
+# bf16 shapes of the matrix-core path beyond the workloads: headdim 128 (64-token chunks),
+# one head per group (dB, dC written directly), heads per group with no head blocking (a
+# reduce over every head) and with blocks of 2 heads summed in the kernel (then 4 blocks
+# reduced)
+@pytest.mark.parametrize("shape", [
+    (1, 200, 4, 128, 64, 2, 64), (1, 150, 2, 128, 128, 1, 128), (2, 90, 4, 64, 64, 4, 256),
+    (1, 300, 6, 64, 128, 2, 256), (2, 4096, 8, 64, 64, 1, 256)])
+def test_backward_bf16_shapes(shape):
+    b, L, H, P, S, G, T = shape
+    cpu = problem(b, L, H, P, S, G, "bf16", seed=3 + L)
+    check(f"bf16 shape {shape}", run_gpu(cpu, T), run_oracle(cpu), "bf16")
