@@ -55,6 +55,18 @@ def algorithmic(w):
     return by, fl
 
 
+def backward_bytes(w):
+    """Bytes the backward call must move: x, dt, B, C, h0 (when present), dy and dfinal
+    read once; dx, ddt, dB, dC, dh0, dA and dD (fp32) written once."""
+    B, L, H, P, S, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    e = 2 if w.dtype == "bf16" else 4
+    tok_h, tok_g, st = B * L * H, B * L * G, B * H * P * S
+    reads = tok_h * P * e + tok_h * e + 2 * tok_g * S * e + (st * 4 if w.h0 else 0) \
+        + tok_h * P * 4 + st * 4 + 2 * H * 4
+    writes = tok_h * P * 4 + tok_h * 4 + 2 * tok_g * S * 4 + st * 4 + 2 * H * 4
+    return reads + writes
+
+
 # Sources of the chunk-output kernel; the HBM traffic measured with rocprofv3 counters
 # is reported only while they are unchanged since the counters were taken.
 CHUNK_OUT_SOURCES = ("chunk_out.h", "k_chunk_out.cpp", "k_chunk_out_bf16.hip",
@@ -202,8 +214,11 @@ def time_backward(torch, ssd, gen, w, d, stream, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    nbytes = backward_bytes(w)
     return {"value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
-            "steps": steps, "workspace_bytes": ws.numel()}
+            "steps": steps, "workspace_bytes": ws.numel(), "algorithmic_bytes": nbytes,
+            "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def main():

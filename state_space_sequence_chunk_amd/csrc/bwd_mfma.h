@@ -52,8 +52,12 @@ struct BmCfg {
     static constexpr size_t K_BYTES = (size_t)T * KS * 2;  // each part
     static constexpr size_t V_BYTES = (size_t)T * VS * 2;  // each part
     static constexpr size_t Z_BYTES = (size_t)N * KS * 2;  // each part
+    // dxh: dy's rows also kept in fp32 for the epilogue's D dy and dy . x
+    static constexpr int DS = P + 4;
+    static constexpr size_t DY_BYTES = OP == kOpX ? (size_t)T * DS * 4 : 0;
     static constexpr size_t LDS_BYTES = K_BYTES * (KSPLIT ? 2 : 1) + V_BYTES * (VSPLIT ? 2 : 1) +
-                                        2 * Z_BYTES + 2 * (size_t)T * 4 + 4 * (size_t)T * 4;
+                                        2 * Z_BYTES + 2 * (size_t)T * 4 + 4 * (size_t)T * 4 +
+                                        DY_BYTES;
     static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && N % 32 == 0;
 };
 
@@ -96,6 +100,18 @@ struct Stager {
             } else {
                 raw[i] = ok ? *(const f32x4*)(src + r * sstride + col) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
+        }
+    }
+    // fp32 sources: the values as they are (row stride dstride floats)
+    __device__ __forceinline__ void store_f32(float* dst, int dstride, int tid) const {
+        static_assert(F32, "fp32 source only");
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v >= NVEC) continue;
+            const int r = v / PER, col = (v % PER) * 8;
+            *(f32x4*)(dst + r * dstride + col) = raw[2 * i];
+            *(f32x4*)(dst + r * dstride + col + 4) = raw[2 * i + 1];
         }
     }
     __device__ __forceinline__ void store(bf16* dst, bf16* dst_lo, int dstride, int tid) const {
@@ -187,6 +203,7 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     float* s_g = (float*)sp;                             // [T]
     float* s_dt = s_g + T;                               // [T]
     float* s_red = s_dt + T;                             // [2 halves][2][T] row-sum partials
+    float* s_dy32 = s_red + 4 * T;                       // dxh: [T][DS] dy (fp32)
 
     // workgroup: (batch, chunk, block of NH heads of one group)
     const int L = a.L, H = a.H, NG = a.G, NH = a.NH;
@@ -236,8 +253,12 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
         }
     };
     auto store_head = [&]() {
-        if constexpr (OP == kOpX) stv.store(s_v, s_vl, VS, tid);
-        else stk.store(s_k, s_kl, KS, tid);
+        if constexpr (OP == kOpX) {
+            stv.store(s_v, s_vl, VS, tid);
+            stv.store_f32(s_dy32, Cfg::DS, tid);
+        } else {
+            stk.store(s_k, s_kl, KS, tid);
+        }
         stz.store(s_zh, s_zl, KS, tid);
         if (tid < T) {
             s_g[tid] = pg;
@@ -334,14 +355,12 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
             // the next step's rows
             if (qi == 0) load_q(h, NIT - 1 - wave);
             else if (hh + 1 < NH) load_q(h + 1, wave);
-            // dxh epilogue: x and dy (fp32) at this lane's output elements, loaded ahead
-            // of use
+            // dxh epilogue: x at this lane's output elements, loaded ahead of use
             const uint32_t row0 = row0s[qi];
-            float xv[OP == kOpX ? 4 : 1][NNH], dyv[OP == kOpX ? 4 : 1][NNH];
+            float xv[OP == kOpX ? 4 : 1][NNH];
             if constexpr (OP == kOpX) {
                 const BufRsrc rxx = make_rsrc((const bf16*)a.x + tok0 * HP, (uint32_t)(rows * HP * 2));
-                const BufRsrc rdy = make_rsrc(a.dy + tok0 * HP, (uint32_t)(rows * HP * 4));
-                const uint32_t soff2 = (uint32_t)(h * P * 2), soff4 = (uint32_t)(h * P * 4);
+                const uint32_t soff2 = (uint32_t)(h * P * 2);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -350,7 +369,6 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
                         const uint16_t xb = __builtin_amdgcn_raw_buffer_load_b16(
                             rxx, vx + (nt0 + j) * 32, soff2, 0);
                         xv[r][j] = to_f32(__builtin_bit_cast(bf16, xb));
-                        dyv[r][j] = buf_load_f32(rdy, 2 * vx + (nt0 + j) * 64, soff4);
                     }
             }
             f32x4 acc[NNH];  // output columns 16 (nt0 + j) + l16
@@ -465,9 +483,10 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
                     for (int j = 0; j < NNH; ++j) {
                         const int nt = nt0 + j;
                         const float o = acc[j][r];
-                        buf_store_f32(dval * dyv[r][j] + dtr * o, rdx, vo + nt * 64, soff4);
+                        const float dyv = s_dy32[(row0 + r) * Cfg::DS + nt * 16 + l16];
+                        buf_store_f32(dval * dyv + dtr * o, rdx, vo + nt * 64, soff4);
                         red[r] += xv[r][j] * o;
-                        red2[r] += xv[r][j] * dyv[r][j];
+                        red2[r] += xv[r][j] * dyv;
                     }
                 }
             }
