@@ -38,64 +38,98 @@ __global__ __launch_bounds__(64) void bwd_carry_kernel(float* __restrict__ R,
 }
 
 // ---- per (batch, head): the suffix sum for the log-decay gradient, ddt, dA and dD -------
-// da_t = sum_{t' >= t} (q_t' - dt_t' v_t') + <dfinal, final>; 256 threads, each a
-// contiguous run of tokens, combined with a block-wide scan of the run totals.
-__global__ __launch_bounds__(256) void bwd_scan_kernel(
+// da_t = sum_{t' >= t} (q_t' - dt_t' v_t') + <dfinal, final>. 1024 threads per (batch,
+// head), each a contiguous run of tokens; the runs' totals are combined with wave prefix
+// scans (DPP) and one LDS pass over the 16 wave totals.
+constexpr int kScanThreads = 1024, kScanWaves = kScanThreads / 64;
+
+// Sum over the workgroup (every thread gets the total); `red` holds kScanWaves floats.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kScanWaves; ++w) t += red[w];
+    return t;
+}
+
+__global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(
     const float* __restrict__ q, const float* __restrict__ v, const float* __restrict__ dyx,
     const float* __restrict__ dt_t, const float* __restrict__ A, const float* __restrict__ dfinal,
     const float* __restrict__ fin, float* __restrict__ ddt, float* __restrict__ dA_bh,
     float* __restrict__ dD_bh, int L, int H, int PS) {
-    __shared__ float s_tot[256];
-    __shared__ float s_red[3][256];
+    __shared__ float s_red[kScanWaves], s_wave[kScanWaves];
     const int bh = blockIdx.x, h = bh % H, b = bh / H;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // <dfinal, final>
     float cst = 0.f;
     if (dfinal)
-        for (int i = tid; i < PS; i += 256) cst += dfinal[(size_t)bh * PS + i] * fin[(size_t)bh * PS + i];
-    s_red[0][tid] = cst;
-    // this thread's run of tokens
-    const int per = (L + 255) / 256;
+        for (int i = tid; i < PS; i += kScanThreads)
+            cst += dfinal[(size_t)bh * PS + i] * fin[(size_t)bh * PS + i];
+    cst = block_sum(cst, s_red);
+    // this thread's run of tokens and its total
+    const int per = (L + kScanThreads - 1) / kScanThreads;
     const int ta = min(tid * per, L), tz = min(ta + per, L);
     const size_t o = (size_t)bh * L;
+    // tokens in batches of 8 so that each batch's loads are in flight together
+    constexpr int NB = 8;
     float run = 0.f;
-    for (int t = ta; t < tz; ++t) run += q[o + t] - dt_t[o + t] * v[o + t];
-    s_tot[tid] = run;
-    __syncthreads();
-    if (tid == 0) {
-        float c = 0.f;
-        for (int i = 0; i < 256; ++i) c += s_red[0][i];
-        s_red[1][0] = c;
-        // suffix sums of the run totals: s_tot[i] <- sum_{j > i} tot_j
-        float acc = 0.f;
-        for (int i = 255; i >= 0; --i) {
-            const float tt = s_tot[i];
-            s_tot[i] = acc;
-            acc += tt;
+    for (int tb = ta; tb < tz; tb += NB) {
+        float tq[NB], td[NB], tv[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const bool ok = tb + k < tz;
+            tq[k] = ok ? q[o + tb + k] : 0.f;
+            td[k] = ok ? dt_t[o + tb + k] : 0.f;
+            tv[k] = ok ? v[o + tb + k] : 0.f;
         }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) run += tq[k] - td[k] * tv[k];
     }
+    // sum of the runs after this thread's: total - inclusive prefix
+    const float incl = wave_inclusive_scan(run);
+    if (lane == 63) s_wave[wv] = incl;
     __syncthreads();
+    float before = 0.f, total = 0.f;  // wave totals before this wave; all of them
+#pragma unroll
+    for (int w = 0; w < kScanWaves; ++w) {
+        const float x = s_wave[w];
+        before += w < wv ? x : 0.f;
+        total += x;
+    }
+    float suffix = cst + total - (before + incl);
     const float ah = A[h];
-    float suffix = s_tot[tid] + s_red[1][0];
     float pa = 0.f, pd = 0.f;
-    for (int t = tz - 1; t >= ta; --t) {
-        suffix += q[o + t] - dt_t[o + t] * v[o + t];
-        ddt[((size_t)b * L + t) * H + h] = v[o + t] + ah * suffix;
-        pa += dt_t[o + t] * suffix;
-        pd += dyx[o + t];
-    }
-    __syncthreads();
-    s_red[0][tid] = pa;
-    s_red[2][tid] = pd;
-    __syncthreads();
-    if (tid == 0) {
-        float sa = 0.f, sd = 0.f;
-        for (int i = 0; i < 256; ++i) {
-            sa += s_red[0][i];
-            sd += s_red[2][i];
+    // the same batches, last to first; token tb + k of a batch
+    const int nbat = (tz - ta + NB - 1) / NB;
+    for (int bi = nbat - 1; bi >= 0; --bi) {
+        const int tb = ta + bi * NB;
+        float tq[NB], td[NB], tv[NB], tx[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const bool ok = tb + k < tz;
+            tq[k] = ok ? q[o + tb + k] : 0.f;
+            td[k] = ok ? dt_t[o + tb + k] : 0.f;
+            tv[k] = ok ? v[o + tb + k] : 0.f;
+            tx[k] = ok ? dyx[o + tb + k] : 0.f;
         }
-        dA_bh[bh] = sa;
-        dD_bh[bh] = sd;
+#pragma unroll
+        for (int k = NB - 1; k >= 0; --k) {
+            if (tb + k >= tz) continue;
+            suffix += tq[k] - td[k] * tv[k];
+            ddt[((size_t)b * L + tb + k) * H + h] = tv[k] + ah * suffix;
+            pa += td[k] * suffix;
+            pd += tx[k];
+        }
+    }
+    pa = block_sum(pa, s_red);
+    pd = block_sum(pd, s_red);
+    if (tid == 0) {
+        dA_bh[bh] = pa;
+        dD_bh[bh] = pd;
     }
 }
 
@@ -215,7 +249,7 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
         e = chunks(false, false, true);
     }
     if (e != hipSuccess) return e;
-    bwd_scan_kernel<<<B * H, 256, 0, s>>>(k.ws.q, k.ws.v, k.ws.dyx, k.ws.dt_t, k.A, k.dfinal,
+    bwd_scan_kernel<<<B * H, kScanThreads, 0, s>>>(k.ws.q, k.ws.v, k.ws.dyx, k.ws.dt_t, k.A, k.dfinal,
                                           k.ws.fin, k.ddt, k.ws.dA_bh, k.ws.dD_bh, L, H, PS);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (parts > 1) {
