@@ -56,7 +56,7 @@ struct BmCfg {
     static constexpr int DS = P + 4;
     static constexpr size_t DY_BYTES = OP == kOpX ? (size_t)T * DS * 4 : 0;
     static constexpr size_t LDS_BYTES = K_BYTES * (KSPLIT ? 2 : 1) + V_BYTES * (VSPLIT ? 2 : 1) +
-                                        2 * Z_BYTES + 2 * (size_t)T * 4 + 4 * (size_t)T * 4 +
+                                        2 * Z_BYTES + 3 * (size_t)T * 4 + 4 * (size_t)T * 4 +
                                         DY_BYTES;
     static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && N % 32 == 0;
 };
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     sp += 2 * Cfg::Z_BYTES;
     float* s_g = (float*)sp;                             // [T]
     float* s_dt = s_g + T;                               // [T]
-    float* s_red = s_dt + T;                             // [2 halves][2][T] row-sum partials
+    float* s_u = s_dt + T;                               // [T] per-token decay factors
+    float* s_red = s_u + T;                              // [2 halves][2][T] row-sum partials
     float* s_dy32 = s_red + 4 * T;                       // dxh: [T][DS] dy (fp32)
 
     // workgroup: (batch, chunk, block of NH heads of one group)
@@ -240,7 +241,9 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     Stager<KSrc, NTHR, T, KD, KSPLIT> stk;
     Stager<VSrc, NTHR, T, N, VSPLIT> stv;
     ZStage stz;
-    float pg = 0.f, pdt = 0.f;
+    // G at this token and at the start (backward in time) or end (forward) of its 16-token
+    // tile; u = 2^{G - G_start}, or dt 2^{G_end - G}: the decay from the tile's edge (<= 1)
+    float pg = 0.f, pdt = 0.f, pge = 0.f;
     auto load_head = [&](int h) {
         if constexpr (OP == kOpC) stk.load(xr_of(h), HP, rows, tid);
         else if constexpr (OP == kOpB) stk.load(dyr_of(h), HP, rows, tid);
@@ -250,6 +253,7 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
         if (tid < T) {
             pg = a.Gc[bhl_of(h) + min(tid, rows - 1)];
             pdt = tid < rows ? a.dtt[bhl_of(h) + tid] : 0.f;
+            pge = a.Gc[bhl_of(h) + min(REV ? (tid & ~15) : (tid | 15), rows - 1)];
         }
     };
     auto store_head = [&]() {
@@ -263,6 +267,7 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
         if (tid < T) {
             s_g[tid] = pg;
             s_dt[tid] = pdt;
+            s_u[tid] = REV ? exp2_fast(pg - pge) : pdt * exp2_fast(pge - pg);
         }
     };
     if constexpr (OP == kOpC) stv.load(br, GS, rows, tid);
@@ -416,22 +421,40 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
                         }
                     }
                 // W[i][j] in the A-operand layout (row i = qrow, item 4 jt + r <-> j), split
-                // into bf16 high and low parts
+                // into bf16 high and low parts. Off the diagonal tile the decay is a row
+                // factor (one exp) times the staged per-token factor u_j, both <= 1; on it
+                // each element is exact, with the causal mask; tiles on the far side of
+                // the diagonal are zero.
+                // (dB keeps the per-element form everywhere: the factored form's extra
+                // branches push its registers past the two-waves-per-SIMD budget.)
                 Frag<bf16> wf, wl;
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
-                    const f32x4 gj = *(const f32x4*)(s_g + J0 + jt * 16 + 4 * g4);
-                    f32x4 wj = f32x4{1.f, 1.f, 1.f, 1.f};
-                    if constexpr (!REV) wj = *(const f32x4*)(s_dt + J0 + jt * 16 + 4 * g4);
+                    const int tj = jp * 2 + jt;  // j-tile (wave-uniform, as is it)
+                    const int jb = J0 + jt * 16 + 4 * g4;
+                    f32x4 w4 = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (OP == kOpB || tj == it) {
+                        const f32x4 gj = *(const f32x4*)(s_g + jb);
+                        f32x4 wj = f32x4{1.f, 1.f, 1.f, 1.f};
+                        if constexpr (!REV) wj = *(const f32x4*)(s_dt + jb);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const bool keep = REV ? jb + r >= qrow : jb + r <= qrow;
+                            const float e = exp2_fast(REV ? gj[r] - gi : gi - gj[r]);
+                            w4[r] = keep ? e * wj[r] * zt[jt][r] : 0.f;
+                        }
+                    } else if (REV ? tj > it : tj < it) {
+                        const float gref = s_g[J0 + jt * 16 + (REV ? 0 : 15)];
+                        const float rr = exp2_fast(REV ? gref - gi : gi - gref);
+                        const f32x4 u4 = *(const f32x4*)(s_u + jb);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) w4[r] = (rr * u4[r]) * zt[jt][r];
+                    }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int j = J0 + jt * 16 + 4 * g4 + r;
-                        const bool keep = REV ? j >= qrow : j <= qrow;
-                        const float e = exp2_fast(REV ? gj[r] - gi : gi - gj[r]);
-                        const float w = keep ? e * wj[r] * zt[jt][r] : 0.f;
-                        const bf16 hi = (bf16)w;
+                        const bf16 hi = (bf16)w4[r];
                         wf.v[jt * 4 + r] = hi;
-                        wl.v[jt * 4 + r] = (bf16)(w - to_f32(hi));
+                        wl.v[jt * 4 + r] = (bf16)(w4[r] - to_f32(hi));
                     }
                 }
 #pragma unroll
