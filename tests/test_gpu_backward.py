@@ -173,3 +173,18 @@ def test_backward_bf16_shapes(shape):
     b, L, H, P, S, G, T = shape
     cpu = problem(b, L, H, P, S, G, "bf16", seed=3 + L)
     check(f"bf16 shape {shape}", run_gpu(cpu, T), run_oracle(cpu), "bf16")
+
+
+@pytest.mark.parametrize("dtype,T", [("bf16", 256), ("fp32", 64)])
+def test_backward_extreme_decay(dtype, T):
+    # dt up to 2 with A down to -16: per-token log2 decays near -46, so decays across a
+    # 16-token tile leave the fp32 range; every factor the kernels form must stay <= 1
+    g = torch.Generator()
+    g.manual_seed(77)
+    cpu = gen.draw(1, 300, 4, 64, 128, 2, gen.torch_dtype(dtype), g, random_h0=True,
+                   dt_range=(0.05, 2.0), A_range=(1.0, 16.0))
+    cpu.update(gen.draw_cotangents(1, 300, 4, 64, 128, g))
+    got = run_gpu(cpu, T)
+    for n in NAMES:
+        assert torch.isfinite(got[n]).all(), n
+    check(f"extreme decay {dtype}", got, run_oracle(cpu), dtype)
