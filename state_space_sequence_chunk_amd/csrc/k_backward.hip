@@ -189,6 +189,13 @@ static int bwd_heads_per_block(int B, int nC, int H, int hpg) {
     return best;
 }
 
+int bwd_partials_per_group(int in_dtype, const Dims& d) {
+    const int hpg = d.nheads / d.ngroups;
+    if (bwd_mfma_chunk(in_dtype, d.headdim, d.dstate) == d.chunk)
+        return hpg / bwd_heads_per_block(d.batch, d.nchunks(), d.nheads, hpg);
+    return hpg;
+}
+
 hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipStream_t s) {
     const int B = d.batch, L = d.seqlen, H = d.nheads, P = d.headdim, S = d.dstate;
     const int G = d.ngroups, T = d.chunk, nC = d.nchunks(), PS = P * S;
@@ -227,11 +234,11 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
     // which the caller has put in d): dC, dB and dx as chunked products; otherwise the
     // fp32 token walks
     const bool mfma = bwd_mfma_chunk(in_dtype, P, S) == T;
-    int parts = hpg;  // per-head dB, dC partials to sum per group
+    // dB, dC partials to sum per group (per head with the walks; per block of a.NH heads,
+    // summed inside the kernels, with the matrix-core path)
+    const int parts = bwd_partials_per_group(in_dtype, d);
     if (mfma) {
-        // dB and dC summed over blocks of a.NH heads inside the kernels
-        a.NH = bwd_heads_per_block(B, nC, H, hpg);
-        parts = hpg / a.NH;
+        a.NH = hpg / parts;
         a.dBh = parts == 1 ? k.dB : k.ws.dBh;
         a.dCh = parts == 1 ? k.dC : k.ws.dCh;
     }

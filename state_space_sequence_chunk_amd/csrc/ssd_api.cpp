@@ -123,9 +123,11 @@ BwdSizes bwd_sizes(const ssd_shape* shape) {
     z.fin = round_up(BH * s->headdim * s->dstate * sizeof(float));
     z.tok = z.dec;
     z.bh = round_up(BH * sizeof(float));
-    const bool shared = s->nheads != s->ngroups;
-    z.part = shared ? round_up((size_t)s->batch * s->seqlen * s->nheads * s->dstate * sizeof(float))
-                    : 0;
+    // partial dB, dC rows, [B, L, G * parts, S] (none when the kernels write dB, dC directly)
+    const int parts = ssd::bwd_partials_per_group(s->in_dtype, dims_of(s));
+    z.part = parts > 1 ? round_up((size_t)s->batch * s->seqlen * s->ngroups * parts * s->dstate *
+                                  sizeof(float))
+                       : 0;
     z.total = s->seqlen == 0 ? 0 : 2 * z.dec + 2 * z.st + z.fin + 3 * z.tok + 2 * z.bh + 2 * z.part;
     return z;
 }

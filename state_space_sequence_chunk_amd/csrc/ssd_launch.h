@@ -56,6 +56,9 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
 // Chunk length at which the backward pass runs its matrix-core kernels for this shape (0:
 // none; the token walks then run at the caller's chunk length).
 int bwd_mfma_chunk(int in_dtype, int P, int S);
+// Partial dB, dC rows the backward pass writes per (token, group) before summing them (1:
+// it writes dB and dC directly); d.chunk is the backward's chunk length.
+int bwd_partials_per_group(int in_dtype, const Dims& d);
 
 hipError_t launch_chunk_out(int in_dtype, int states_dtype, int out_dtype, const void* x,
                             const void* Bm, const void* Cm, const float* G, const float* dt_t,

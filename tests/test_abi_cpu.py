@@ -237,3 +237,15 @@ def test_backward_rejects_before_launch():
     n = ctypes.c_size_t(0)
     assert lib.ssd_backward_workspace_bytes(ctypes.byref(s), None) == 1
     assert lib.ssd_backward_workspace_bytes(ctypes.byref(shape(in_dtype=9)), ctypes.byref(n)) == 3
+
+
+def test_backward_workspace_without_partials():
+    # 2 x 16384 tokens, 80 heads in one group, bf16: the matrix-core kernels run at
+    # 128-token chunks with all 80 heads of the group in one workgroup and write dB, dC
+    # directly, so no per-head partials are reserved
+    s = shape(batch=2, seqlen=16384, nheads=80, ngroups=1, chunk=256)
+    dec = _round256(2 * 80 * 16384 * 4)
+    st = 2 * 80 * 128 * 64 * 128 * 4
+    fin = 2 * 80 * 64 * 128 * 4
+    bh = _round256(2 * 80 * 4)
+    assert ssd.backward_workspace_bytes(s) == 2 * dec + 2 * st + fin + 3 * dec + 2 * bh
