@@ -179,7 +179,13 @@ ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const void* dt
  *     heads),  dC_t = H_t^T dy_t (summed likewise),  dD = sum dy . x,  dh0 = dL/dH_{-1},
  *     ddt_t = x_t . Lam_t B_t + A dL/da_t,  dA = sum_t dt_t dL/da_t  (a_t = A dt_t).
  * The forward quantities it needs (cumulative decay, chunk-initial states, final state)
- * are recomputed here. All arithmetic is fp32; states_dtype and out_dtype are not used.
+ * are recomputed here, chunk by chunk; states_dtype and out_dtype are not used. Precision:
+ * fp32 accumulation throughout. With bf16 inputs (and headdim 64/128, dstate 64/128/256)
+ * the per-chunk products run on the matrix cores with every fp32 operand (dy, the decayed
+ * interaction weights, the states) entered as a bf16 high/low pair (about 16 significant
+ * bits), at a chunk length of the library's choosing (128 or 64 tokens; the chunked form
+ * is exact for any length, so shape->chunk only sizes the fp32 path); otherwise fp32 VALU
+ * arithmetic at shape->chunk. ssd_backward_workspace_bytes accounts for both.
  * Inputs: x, dt, B, C in in_dtype and A, D, h0 as for ssd_forward (D and h0 may be NULL);
  * dy [batch, seqlen, nheads, headdim] fp32; dfinal [batch, nheads, headdim, dstate] fp32
  * or NULL (zero). Outputs, all fp32, written in full: dx (x's layout), ddt (dt's layout),
