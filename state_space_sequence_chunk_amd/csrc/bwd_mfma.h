@@ -37,6 +37,31 @@ namespace ssd {
 
 enum BwdOp { kOpC = 0, kOpB = 1, kOpX = 2 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 values as packed bf16 high parts (round to nearest even) and packed bf16
+// remainders: one packed conversion each, the high parts widened back by bit operations.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+    const uint32_t hu = __builtin_bit_cast(uint32_t, h);
+    const float ah = __uint_as_float(hu << 16), bh = __uint_as_float(hu & 0xffff0000u);
+    hi = hu;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a - ah, b - bh}, bf16x2_t));
+}
+
+// Eight fp32 values (two f32x4) as a bf16x8 of high parts and one of remainders.
+__device__ __forceinline__ void split8(const f32x4& u, const f32x4& w, bf16x8& hi, bf16x8& lo) {
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    split2(u[0], u[1], h0, l0);
+    split2(u[2], u[3], h1, l1);
+    split2(w[0], w[1], h2, l2);
+    split2(w[2], w[3], h3, l3);
+    hi = __builtin_bit_cast(bf16x8, (u32x4){h0, h1, h2, h3});
+    lo = __builtin_bit_cast(bf16x8, (u32x4){l0, l1, l2, l3});
+}
+
 template <int OP, int P, int S, int T>
 struct BmCfg {
     static constexpr bool REV = OP != kOpC;
@@ -67,14 +92,7 @@ __device__ __forceinline__ void ld8_split(const bf16* p, bf16x8& hi, bf16x8& lo)
     lo = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
 }
 __device__ __forceinline__ void ld8_split(const float* p, bf16x8& hi, bf16x8& lo) {
-    const f32x4 u = *(const f32x4*)p, w = *(const f32x4*)(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = (bf16)u[i];
-        hi[i + 4] = (bf16)w[i];
-        lo[i] = (bf16)(u[i] - to_f32(hi[i]));
-        lo[i + 4] = (bf16)(w[i] - to_f32(hi[i + 4]));
-    }
+    split8(*(const f32x4*)p, *(const f32x4*)(p + 4), hi, lo);
 }
 
 // Rows [0, NROWS) x NCOLS (a multiple of 8) of a row-major source, staged into LDS as bf16
@@ -122,13 +140,7 @@ struct Stager {
             const int r = v / PER, col = (v % PER) * 8;
             if constexpr (F32) {
                 bf16x8 hi, lo;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    hi[k] = (bf16)raw[2 * i][k];
-                    hi[k + 4] = (bf16)raw[2 * i + 1][k];
-                    lo[k] = (bf16)(raw[2 * i][k] - to_f32(hi[k]));
-                    lo[k + 4] = (bf16)(raw[2 * i + 1][k] - to_f32(hi[k + 4]));
-                }
+                split8(raw[2 * i], raw[2 * i + 1], hi, lo);
                 *(bf16x8*)(dst + r * dstride + col) = hi;
                 if constexpr (SPLIT) *(bf16x8*)(dst_lo + r * dstride + col) = lo;
             } else {
@@ -164,13 +176,8 @@ struct StateTStager {
             const int p = 2 * (v % (P / 2)), s0 = 4 * (v / (P / 2));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float a0 = raw[2 * i][k], a1 = raw[2 * i + 1][k];
-                const bf16 h0 = (bf16)a0, h1 = (bf16)a1;
-                const bf16 l0 = (bf16)(a0 - to_f32(h0)), l1 = (bf16)(a1 - to_f32(h1));
-                const uint32_t hw = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                const uint32_t lw = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+                uint32_t hw, lw;
+                split2(raw[2 * i][k], raw[2 * i + 1][k], hw, lw);
                 *(uint32_t*)(zh + (s0 + k) * ks + p) = hw;
                 *(uint32_t*)(zl + (s0 + k) * ks + p) = lw;
             }
@@ -342,17 +349,7 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 if constexpr (QF32) {
-                    bf16x8 hi, lo;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float u0 = qraw[2 * ks][k], u1 = qraw[2 * ks + 1][k];
-                        hi[k] = (bf16)u0;
-                        hi[k + 4] = (bf16)u1;
-                        lo[k] = (bf16)(u0 - to_f32(hi[k]));
-                        lo[k + 4] = (bf16)(u1 - to_f32(hi[k + 4]));
-                    }
-                    qf[ks].v = hi;
-                    ql[ks].v = lo;
+                    split8(qraw[2 * ks], qraw[2 * ks + 1], qf[ks].v, ql[ks].v);
                 } else {
                     qf[ks].v = __builtin_bit_cast(bf16x8, qraw[ks]);
                 }
@@ -428,6 +425,7 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
                 // (dB keeps the per-element form everywhere: the factored form's extra
                 // branches push its registers past the two-waves-per-SIMD budget.)
                 Frag<bf16> wf, wl;
+                uint32_t wh[4], wlo[4];
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
                     const int tj = jp * 2 + jt;  // j-tile (wave-uniform, as is it)
@@ -450,13 +448,11 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) w4[r] = (rr * u4[r]) * zt[jt][r];
                     }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bf16 hi = (bf16)w4[r];
-                        wf.v[jt * 4 + r] = hi;
-                        wl.v[jt * 4 + r] = (bf16)(w4[r] - to_f32(hi));
-                    }
+                    split2(w4[0], w4[1], wh[2 * jt], wlo[2 * jt]);
+                    split2(w4[2], w4[3], wh[2 * jt + 1], wlo[2 * jt + 1]);
                 }
+                wf.v = __builtin_bit_cast(bf16x8, (u32x4){wh[0], wh[1], wh[2], wh[3]});
+                wl.v = __builtin_bit_cast(bf16x8, (u32x4){wlo[0], wlo[1], wlo[2], wlo[3]});
 #pragma unroll
                 for (int j = 0; j < NNH; ++j) {
                     const int n0 = (nt0 + j) * 16;
@@ -626,14 +622,7 @@ __global__ __launch_bounds__(2 * T) void bwd_dR_mfma_kernel(BwdArgs a) {
         const int r = v / PER, col = (v % PER) * 8;
         const float w = exp2_fast(wt[i]);
         bf16x8 hi, lo;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float u0 = w * ry[2 * i][k], u1 = w * ry[2 * i + 1][k];
-            hi[k] = (bf16)u0;
-            hi[k + 4] = (bf16)u1;
-            lo[k] = (bf16)(u0 - to_f32(hi[k]));
-            lo[k + 4] = (bf16)(u1 - to_f32(hi[k + 4]));
-        }
+        split8(w * ry[2 * i], w * ry[2 * i + 1], hi, lo);
         *(bf16x8*)(s_yh + r * YS + col) = hi;
         *(bf16x8*)(s_yl + r * YS + col) = lo;
     }
