@@ -69,9 +69,11 @@ struct BmCfg {
     static constexpr int N = OP == kOpX ? P : S;   // output width
     // dy (fp32) is the operand split into bf16 high and low parts: Q of dC, K of dB, V of dxh
     static constexpr bool QSPLIT = OP == kOpC, KSPLIT = OP == kOpB, VSPLIT = OP == kOpX;
-    // T/32 pairs of row tiles; two waves per pair, each taking half of the output columns
-    static constexpr int NIT = T / 16, NW = T / 32, NTHR = 128 * NW;
-    static constexpr int NKS = KD / 32, NNT = N / 16, NNH = NNT / 2;
+    // T/32 pairs of row tiles; NSPLIT waves per pair, each taking NNH of the output's 16-wide
+    // column tiles (at most 4, so the accumulators leave room for two waves per SIMD)
+    static constexpr int NSPLIT = N / 64 > 2 ? N / 64 : 2;
+    static constexpr int NIT = T / 16, NW = T / 32, NTHR = 64 * NW * NSPLIT;
+    static constexpr int NKS = KD / 32, NNT = N / 16, NNH = NNT / NSPLIT;
     static constexpr int KS = row_stride<bf16>(KD);  // K rows and Z rows (read by rows)
     static constexpr int VS = col_stride<bf16>(N);   // V rows (read by columns)
     static constexpr size_t K_BYTES = (size_t)T * KS * 2;  // each part
@@ -81,9 +83,9 @@ struct BmCfg {
     static constexpr int DS = P + 4;
     static constexpr size_t DY_BYTES = OP == kOpX ? (size_t)T * DS * 4 : 0;
     static constexpr size_t LDS_BYTES = K_BYTES * (KSPLIT ? 2 : 1) + V_BYTES * (VSPLIT ? 2 : 1) +
-                                        2 * Z_BYTES + 3 * (size_t)T * 4 + 4 * (size_t)T * 4 +
-                                        DY_BYTES;
-    static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && N % 32 == 0;
+                                        2 * Z_BYTES + 3 * (size_t)T * 4 +
+                                        2 * NSPLIT * (size_t)T * 4 + DY_BYTES;
+    static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && NNT % NSPLIT == 0;
 };
 
 // 8 consecutive values as bf16 (high part) and, for fp32 sources, the bf16 remainders
@@ -186,7 +188,8 @@ struct StateTStager {
 };
 
 template <int OP, int P, int S, int T>
-__global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTHR))) void bwd_mfma_kernel(
+    BwdArgs a) {
     using Cfg = BmCfg<OP, P, S, T>;
     constexpr int N = Cfg::N, KD = Cfg::KD, NKS = Cfg::NKS, NNH = Cfg::NNH;
     constexpr int KS = Cfg::KS, VS = Cfg::VS, NTHR = Cfg::NTHR, NIT = Cfg::NIT;
@@ -210,8 +213,8 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     float* s_g = (float*)sp;                             // [T]
     float* s_dt = s_g + T;                               // [T]
     float* s_u = s_dt + T;                               // [T] per-token decay factors
-    float* s_red = s_u + T;                              // [2 halves][2][T] row-sum partials
-    float* s_dy32 = s_red + 4 * T;                       // dxh: [T][DS] dy (fp32)
+    float* s_red = s_u + T;                              // [NSPLIT][2][T] row-sum partials
+    float* s_dy32 = s_red + 2 * Cfg::NSPLIT * T;         // dxh: [T][DS] dy (fp32)
 
     // workgroup: (batch, chunk, block of NH heads of one group)
     const int L = a.L, H = a.H, NG = a.G, NH = a.NH;
@@ -222,8 +225,8 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
     const int g = h_first / (H / NG);  // NH divides the heads per group
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave = wid % Cfg::NW, half = wid / Cfg::NW;  // row-tile pair, column half
-    const int nt0 = half * NNH;
+    const int wave = wid % Cfg::NW, part = wid / Cfg::NW;  // row-tile pair, column part
+    const int nt0 = part * NNH;
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T, rows = min(T, L - t0);
     const size_t HP = (size_t)H * P, GS = (size_t)NG * S;
@@ -517,10 +520,10 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
                         red[r] += __shfl_xor(red[r], m, 64);
                         if constexpr (OP == kOpX) red2[r] += __shfl_xor(red2[r], m, 64);
                     }
-                    // this half's partial row sums; the halves are added below
+                    // this part's partial row sums; the parts are added below
                     if (l16 == 0) {
-                        s_red[(half * 2) * T + row0 + r] = red[r];
-                        s_red[(half * 2 + 1) * T + row0 + r] = red2[r];
+                        s_red[(part * 2) * T + row0 + r] = red[r];
+                        s_red[(part * 2 + 1) * T + row0 + r] = red2[r];
                     }
                 }
             }
@@ -529,12 +532,17 @@ __global__ __launch_bounds__(4 * T) void bwd_mfma_kernel(BwdArgs a) {
         if constexpr (OP != kOpB) {
             const size_t bhl = bhl_of(h);
             if (tid < rows) {
-                const float s0 = s_red[tid] + s_red[2 * T + tid];
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int q = 0; q < Cfg::NSPLIT; ++q) {
+                    s0 += s_red[(2 * q) * T + tid];
+                    s1 += s_red[(2 * q + 1) * T + tid];
+                }
                 if constexpr (OP == kOpC) {
                     a.q[bhl + tid] = s0;
                 } else {
                     a.v[bhl + tid] = s0;
-                    a.dyx[bhl + tid] = s_red[T + tid] + s_red[3 * T + tid];
+                    a.dyx[bhl + tid] = s1;
                 }
             }
         }
@@ -681,7 +689,7 @@ hipError_t run_bwd_mfma(const BwdArgs& a, int batch, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const int nC = (a.L + T - 1) / T;
-    kern<<<batch * nC * (a.H / a.NH), 4 * T, Cfg::LDS_BYTES, stream>>>(a);
+    kern<<<batch * nC * (a.H / a.NH), Cfg::NTHR, Cfg::LDS_BYTES, stream>>>(a);
     return hipGetLastError();
 }
 
