@@ -93,10 +93,49 @@ def pin_closed_forms(o):
     assert np.array_equal(ge["dh0"], wf) and not np.any(ge["dA"]) and not np.any(ge["dD"])
 
 
+def pin_single_token(o):
+    # one token, worked by hand from H = e^{a} h0 + dt x B^T, y = H C + D x (a = A dt),
+    # loss = dy . y + <dfinal, H>; with Lam = dy C^T + dfinal:
+    #   dx = D dy + dt Lam B,  dB = dt Lam^T x,  dC = H^T dy,  dD = dy . x,
+    #   dh0 = e^{a} Lam,  ddt = x . Lam B + A e^{a} <Lam, h0>,  dA = dt e^{a} <Lam, h0>
+    rng = np.random.default_rng(8)
+    P, S, H = 3, 4, 2
+    x = rng.standard_normal((1, 1, H, P))
+    dt = rng.uniform(0.01, 0.5, (1, 1, H))
+    A = -rng.uniform(1.0, 8.0, H)
+    B = rng.standard_normal((1, 1, 1, S))
+    C = rng.standard_normal((1, 1, 1, S))
+    D = rng.standard_normal(H)
+    h0 = rng.standard_normal((1, H, P, S))
+    dy = rng.standard_normal((1, 1, H, P))
+    dfin = rng.standard_normal((1, H, P, S))
+    g = o.backward(x, dt, A, B, C, D, h0, dy, dfin)
+    b, c = B[0, 0, 0], C[0, 0, 0]
+    dB = np.zeros(S)
+    dC = np.zeros(S)
+    for h in range(H):
+        xv, dyv, d = x[0, 0, h], dy[0, 0, h], dt[0, 0, h]
+        e = np.exp(A[h] * d)
+        Hs = e * h0[0, h] + d * np.outer(xv, b)
+        lam = np.outer(dyv, c) + dfin[0, h]
+        np.testing.assert_allclose(g["dx"][0, 0, h], D[h] * dyv + d * lam @ b, rtol=1e-12)
+        np.testing.assert_allclose(g["dh0"][0, h], e * lam, rtol=1e-12)
+        inner = np.sum(lam * h0[0, h])
+        np.testing.assert_allclose(g["ddt"][0, 0, h], xv @ lam @ b + A[h] * e * inner,
+                                   rtol=1e-11)
+        np.testing.assert_allclose(g["dA"][h], d * e * inner, rtol=1e-11)
+        np.testing.assert_allclose(g["dD"][h], dyv @ xv, rtol=1e-12)
+        dB += d * lam.T @ xv
+        dC += Hs.T @ dyv
+    np.testing.assert_allclose(g["dB"][0, 0, 0], dB, rtol=1e-11)
+    np.testing.assert_allclose(g["dC"][0, 0, 0], dC, rtol=1e-11)
+
+
 def all_grad_pins():
     """(name, callable taking the oracle module) for every pin."""
     pins = [("forward64_is_forward", pin_forward64_is_forward),
-            ("closed_forms", pin_closed_forms)]
+            ("closed_forms", pin_closed_forms),
+            ("single_token", pin_single_token)]
     for shape, sample in FD_CASES:
         pins.append((f"finite_differences{shape}",
                      lambda o, shape=shape, sample=sample: pin_finite_differences(o, shape, sample)))

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from grad_pins import FD_CASES, pin_closed_forms, pin_finite_differences, \
-    pin_forward64_is_forward
+    pin_forward64_is_forward, pin_single_token
 
 
 def test_forward64_is_the_forward_oracle():
@@ -22,3 +22,7 @@ def test_gradients_match_finite_differences(shape, sample):
 
 def test_closed_forms():
     pin_closed_forms(oracle)
+
+
+def test_single_token_by_hand():
+    pin_single_token(oracle)
