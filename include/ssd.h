@@ -42,7 +42,10 @@
  *  - Supported sizes: chunk in {64, 128, 256}; headdim in {16, 32, 64, 128};
  *    dstate in {16, 32, 64, 128, 256}; nheads a multiple of ngroups; in_dtype and states_dtype in {SSD_F32, SSD_BF16},
  *    except fp32 inputs with bf16 states (SSD_ERR_UNSUPPORTED: it would only lose the
- *    precision the fp32 inputs ask for).
+ *    precision the fp32 inputs ask for). Size limits (SSD_ERR_UNSUPPORTED beyond them):
+ *    at most 2e9 elements in x and in the chunk states, and below 2 GiB for one chunk's
+ *    rows of x or B (chunk * max(nheads*headdim, ngroups*dstate) * 4 bytes) and for one
+ *    batch row's decays (nheads * seqlen * 4 bytes).
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
@@ -59,7 +62,7 @@ typedef enum ssd_status {
     SSD_ERR_NULL = 1,        /* a required pointer is NULL */
     SSD_ERR_SHAPE = 2,       /* a size < 1 (seqlen < 0), or nheads % ngroups != 0 */
     SSD_ERR_DTYPE = 3,       /* a dtype code that is neither SSD_F32 nor SSD_BF16 */
-    SSD_ERR_UNSUPPORTED = 4, /* chunk, headdim, dstate or dtype pair outside the supported sets */
+    SSD_ERR_UNSUPPORTED = 4, /* chunk, headdim, dstate, dtype pair or size outside the supported sets */
     SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
     SSD_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
     SSD_ERR_HIP = 7          /* the HIP runtime reported an error for a launch */
@@ -183,9 +186,13 @@ ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const void* dt
  * fp32 accumulation throughout. With bf16 inputs (and headdim 64/128, dstate 64/128/256)
  * the per-chunk products run on the matrix cores with every fp32 operand (dy, the decayed
  * interaction weights, the states) entered as a bf16 high/low pair (about 16 significant
- * bits), at a chunk length of the library's choosing (128 or 64 tokens; the chunked form
- * is exact for any length, so shape->chunk only sizes the fp32 path); otherwise fp32 VALU
- * arithmetic at shape->chunk. ssd_backward_workspace_bytes accounts for both.
+ * bits), at a chunk length of the library's choosing (128 or 64 tokens, where the fp32
+ * chunk states at that length stay within the size limits; the chunked form is exact for
+ * any length, so shape->chunk only sizes the fp32 path); otherwise fp32 VALU arithmetic at
+ * shape->chunk. ssd_backward_workspace_bytes accounts for both. dL/da_t is summed over the
+ * later tokens of its chunk only, starting from the value at the chunk's end, the inner
+ * product of the gradient arriving there with the state there; so its rounding error stays
+ * that of one chunk at any seqlen.
  * Inputs: x, dt, B, C in in_dtype and A, D, h0 as for ssd_forward (D and h0 may be NULL);
  * dy [batch, seqlen, nheads, headdim] fp32; dfinal [batch, nheads, headdim, dstate] fp32
  * or NULL (zero). Outputs, all fp32, written in full: dx (x's layout), ddt (dt's layout),

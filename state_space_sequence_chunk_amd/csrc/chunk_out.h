@@ -158,14 +158,13 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const TIn* bg = Bm + (((size_t)b * L + t0) * ngroups + g) * S;
     const int its[2] = {wave, Cfg::NIT - 1 - wave};
 
-    // buffer descriptors over this chunk's rows of x and y (all heads), the states and the
+    // buffer descriptors over this chunk's rows of x and y (all heads) and the
     // per-(batch, head) decay rows; per-head offsets go in the uniform offset operand
     // (x and y rows past the real tokens lie outside these descriptors: loads return zeros
-    // and stores are dropped)
+    // and stores are dropped). Each head's chunk-initial state gets a descriptor of its
+    // own, so the states of a batch row may exceed what 32-bit offsets reach.
     const BufRsrc rx = make_rsrc(x + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(TIn)));
     const BufRsrc ry = make_rsrc(y + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(TY)));
-    const BufRsrc rst = make_rsrc(states + (size_t)b * H * nC * P * S,
-                                  (uint32_t)((size_t)H * nC * P * S * sizeof(TS)));
     const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
     const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
 
@@ -180,11 +179,12 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             px[i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(TIn)),
                                (uint32_t)(h * P * sizeof(TIn)));
         }
-        const uint32_t st_off = (uint32_t)(((size_t)h * nC + c) * P * S * sizeof(TS));
+        const BufRsrc rst = make_rsrc(states + (((size_t)b * H + h) * nC + c) * P * S,
+                                      (uint32_t)(P * S * sizeof(TS)));
 #pragma unroll
         for (int i = 0; i < Cfg::NSV; ++i) {
             const int v = tid + i * NTHR;
-            if (v < P * S / VES) pst[i] = buf_load16(rst, (uint32_t)(v * 16), st_off);
+            if (v < P * S / VES) pst[i] = buf_load16(rst, (uint32_t)(v * 16), 0u);
         }
         if (tid < T) {
             const uint32_t o = (uint32_t)(((size_t)h * L + t0) * sizeof(float));

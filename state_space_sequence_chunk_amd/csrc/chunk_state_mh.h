@@ -79,8 +79,6 @@ __global__ __launch_bounds__(512) void chunk_state_mh_kernel(
     // x rows past the chunk's real tokens lie outside the descriptor and load as zeros
     const BufRsrc rx = make_rsrc(x + ((size_t)b * L + t0) * HP, (uint32_t)(rows * HP * sizeof(TIn)));
     const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
-    const BufRsrc rds = make_rsrc(dS + (size_t)b * H * nC * P * S,
-                                  (uint32_t)((size_t)H * nC * P * S * sizeof(float)));
 
     // ---- per-head staging --------------------------------------------------------------
     Vec16 px[Cfg::NXV];
@@ -223,8 +221,11 @@ __global__ __launch_bounds__(512) void chunk_state_mh_kernel(
                         if (st0 + Cfg::WPT * m < Cfg::NST) mma(acc[m], a, bf[m]);
                 }
             }
-            // dS[b, h, c, p, s]: element (row p = 16 pt + 4 g4 + r, column s) of tile m
-            const uint32_t so = (uint32_t)(((size_t)h * nC + c) * P * S * sizeof(float));
+            // dS[b, h, c, p, s]: element (row p = 16 pt + 4 g4 + r, column s) of tile m,
+            // through a descriptor over this head's P x S block alone (a batch row's
+            // increments may exceed what 32-bit offsets reach)
+            const BufRsrc rds = make_rsrc(dS + (((size_t)b * H + h) * nC + c) * P * S,
+                                          (uint32_t)(P * S * sizeof(float)));
 #pragma unroll
             for (int m = 0; m < Cfg::MST; ++m) {
                 const int st = st0 + Cfg::WPT * m;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(512) void chunk_state_mh_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         buf_store_f32(acc[m][r], rds,
-                                      (uint32_t)(((pt * 16 + 4 * g4 + r) * S + st * 16 + l16) * 4), so);
+                                      (uint32_t)(((pt * 16 + 4 * g4 + r) * S + st * 16 + l16) * 4), 0u);
                 }
             }
         }

@@ -13,40 +13,86 @@ hipError_t launch_bwd_chunks_f32(const BwdArgs& a, int batch, int P, int S, bool
 hipError_t launch_bwd_mfma_bf16(const BwdArgs& a, int batch, int P, int S, hipStream_t st);
 hipError_t launch_bwd_dR_mfma_bf16(const BwdArgs& a, int batch, int P, int S, hipStream_t st);
 
-// ---- reverse carry over chunks: R_c (gradient at chunk c's end), dh0 -------------------
+// ---- reverse carry over chunks: R_c (gradient at chunk c's end), dh0, anchors -----------
 // In place over the per-chunk sums: reads dR_c, stores R_c, then R <- 2^{G_last} R + dR_c.
+// R_c is the gradient reaching the state after chunk c (Hc_{c+1}, or the final state for
+// the last chunk) from everything later, so <R_c, Hc_{c+1}> is the log-decay gradient at
+// the first token after chunk c (da_t = alpha_t <Lam_t, h_{t-1}>). Each wave adds up its
+// 256 elements of that inner product and stores it as one of the PS/256 partials of
+// chunk c; the suffix sums for da then start from these anchors at every chunk end
+// instead of running over the whole sequence, which keeps their rounding local to a
+// chunk (over the whole sequence it grows with its length).
+constexpr int kCarryBatch = 4;  // chunks whose loads are in flight together
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
 __global__ __launch_bounds__(64) void bwd_carry_kernel(float* __restrict__ R,
                                                         const float* __restrict__ G,
+                                                        const float* __restrict__ Hc,
+                                                        const float* __restrict__ fin,
                                                         const float* __restrict__ dfinal,
-                                                        float* __restrict__ dh0, int L, int T,
+                                                        float* __restrict__ dh0,
+                                                        float* __restrict__ anc, int L, int T,
                                                         int nC, int PS) {
     const int per_bh = PS / 256;
     const size_t bh = blockIdx.x / per_bh;
-    const int e = (blockIdx.x % per_bh) * 256 + threadIdx.x * 4;
+    const int slot = blockIdx.x % per_bh;
+    const int e = slot * 256 + threadIdx.x * 4;
     f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
     if (dfinal) r = *(const f32x4*)(dfinal + bh * PS + e);
     const float* gr = G + bh * L;
     float* base = R + bh * nC * (size_t)PS + e;
-    for (int c = nC - 1; c >= 0; --c) {
-        float* p = base + (size_t)c * PS;
-        const f32x4 d = *(const f32x4*)p;
-        *(f32x4*)p = r;
-        const float dec = exp2_fast(gr[min((c + 1) * T, L) - 1]);
-        r = dec * r + d;
+    const float* hbase = Hc + bh * nC * (size_t)PS + e;
+    const f32x4 hfin = *(const f32x4*)(fin + bh * PS + e);
+    float* ap = anc + bh * nC * (size_t)per_bh + slot;
+    for (int c0 = nC - 1; c0 >= 0; c0 -= kCarryBatch) {
+        f32x4 d[kCarryBatch], hn[kCarryBatch];
+        float dec[kCarryBatch];
+#pragma unroll
+        for (int u = 0; u < kCarryBatch; ++u) {
+            const int c = c0 - u;
+            if (c >= 0) {
+                d[u] = *(const f32x4*)(base + (size_t)c * PS);
+                hn[u] = c + 1 < nC ? *(const f32x4*)(hbase + (size_t)(c + 1) * PS) : hfin;
+                dec[u] = exp2_fast(gr[min((c + 1) * T, L) - 1]);
+            }
+        }
+        float part[kCarryBatch];
+#pragma unroll
+        for (int u = 0; u < kCarryBatch; ++u) {
+            const int c = c0 - u;
+            part[u] = 0.f;
+            if (c >= 0) {
+                *(f32x4*)(base + (size_t)c * PS) = r;
+                part[u] = r[0] * hn[u][0] + r[1] * hn[u][1] + r[2] * hn[u][2] + r[3] * hn[u][3];
+                r = dec[u] * r + d[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCarryBatch; ++u) {
+            const float tot = wave_sum(part[u]);
+            if (threadIdx.x == 0 && c0 - u >= 0) ap[(size_t)(c0 - u) * per_bh] = tot;
+        }
     }
     if (dh0) *(f32x4*)(dh0 + bh * PS + e) = r;
 }
 
-// ---- per (batch, head): the suffix sum for the log-decay gradient, ddt, dA and dD -------
-// da_t = sum_{t' >= t} (q_t' - dt_t' v_t') + <dfinal, final>. 1024 threads per (batch,
-// head), each a contiguous run of tokens; the runs' totals are combined with wave prefix
-// scans (DPP) and one LDS pass over the 16 wave totals.
+// ---- per (batch, head): the suffix sums for the log-decay gradient, ddt, dA and dD ------
+// Within chunk c, da_t = a_c + sum_{t' >= t in chunk c} (q_t' - dt_t' v_t'), where the
+// anchor a_c = <R_c, state after chunk c> is the sum of the chunk's PS/256 partials (for
+// the last chunk R = dfinal and the state is the final one, so a = <dfinal, final>).
+// ddt_t = v_t + A da_t; dA = sum_t dt_t da_t; dD = sum_t dy_t . x_t. One workgroup of
+// 16 waves per (batch, head); the waves take the chunks in turn, each lane a run of
+// T/64 consecutive tokens, and a wave prefix scan (DPP) gives the sums over later lanes.
 constexpr int kScanThreads = 1024, kScanWaves = kScanThreads / 64;
 
 // Sum over the workgroup (every thread gets the total); `red` holds kScanWaves floats.
 __device__ __forceinline__ float block_sum(float v, float* red) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    v = wave_sum(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -56,78 +102,55 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return t;
 }
 
+template <int K>  // tokens per lane: T / 64
 __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(
     const float* __restrict__ q, const float* __restrict__ v, const float* __restrict__ dyx,
-    const float* __restrict__ dt_t, const float* __restrict__ A, const float* __restrict__ dfinal,
-    const float* __restrict__ fin, float* __restrict__ ddt, float* __restrict__ dA_bh,
-    float* __restrict__ dD_bh, int L, int H, int PS) {
-    __shared__ float s_red[kScanWaves], s_wave[kScanWaves];
+    const float* __restrict__ dt_t, const float* __restrict__ A, const float* __restrict__ anc,
+    float* __restrict__ ddt, float* __restrict__ dA_bh, float* __restrict__ dD_bh, int L, int H,
+    int nC, int per_bh) {
+    __shared__ float s_red[kScanWaves];
+    constexpr int T = 64 * K;
     const int bh = blockIdx.x, h = bh % H, b = bh / H;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    // <dfinal, final>
-    float cst = 0.f;
-    if (dfinal)
-        for (int i = tid; i < PS; i += kScanThreads)
-            cst += dfinal[(size_t)bh * PS + i] * fin[(size_t)bh * PS + i];
-    cst = block_sum(cst, s_red);
-    // this thread's run of tokens and its total
-    const int per = (L + kScanThreads - 1) / kScanThreads;
-    const int ta = min(tid * per, L), tz = min(ta + per, L);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const size_t o = (size_t)bh * L;
-    // tokens in batches of 8 so that each batch's loads are in flight together
-    constexpr int NB = 8;
-    float run = 0.f;
-    for (int tb = ta; tb < tz; tb += NB) {
-        float tq[NB], td[NB], tv[NB];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            const bool ok = tb + k < tz;
-            tq[k] = ok ? q[o + tb + k] : 0.f;
-            td[k] = ok ? dt_t[o + tb + k] : 0.f;
-            tv[k] = ok ? v[o + tb + k] : 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < NB; ++k) run += tq[k] - td[k] * tv[k];
-    }
-    // sum of the runs after this thread's: total - inclusive prefix
-    const float incl = wave_inclusive_scan(run);
-    if (lane == 63) s_wave[wv] = incl;
-    __syncthreads();
-    float before = 0.f, total = 0.f;  // wave totals before this wave; all of them
-#pragma unroll
-    for (int w = 0; w < kScanWaves; ++w) {
-        const float x = s_wave[w];
-        before += w < wv ? x : 0.f;
-        total += x;
-    }
-    float suffix = cst + total - (before + incl);
     const float ah = A[h];
     float pa = 0.f, pd = 0.f;
-    // the same batches, last to first; token tb + k of a batch
-    const int nbat = (tz - ta + NB - 1) / NB;
-    for (int bi = nbat - 1; bi >= 0; --bi) {
-        const int tb = ta + bi * NB;
-        float tq[NB], td[NB], tv[NB], tx[NB];
+    for (int c = wv; c < nC; c += kScanWaves) {
+        // the anchor: sum of the chunk's partials
+        const float* ap = anc + ((size_t)bh * nC + c) * per_bh;
+        float a = 0.f;
+        for (int i = lane; i < per_bh; i += 64) a += ap[i];
+        a = wave_sum(a);
+        // this lane's tokens t0 + K lane + k (zero past the sequence's end)
+        const int t0 = c * T + K * lane;
+        float tq[K], tv[K], td[K], tw[K];
+        float run = 0.f;
 #pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            const bool ok = tb + k < tz;
-            tq[k] = ok ? q[o + tb + k] : 0.f;
-            td[k] = ok ? dt_t[o + tb + k] : 0.f;
-            tv[k] = ok ? v[o + tb + k] : 0.f;
-            tx[k] = ok ? dyx[o + tb + k] : 0.f;
+        for (int k = 0; k < K; ++k) {
+            const bool ok = t0 + k < L;
+            tq[k] = ok ? q[o + t0 + k] : 0.f;
+            tv[k] = ok ? v[o + t0 + k] : 0.f;
+            td[k] = ok ? dt_t[o + t0 + k] : 0.f;
+            pd += ok ? dyx[o + t0 + k] : 0.f;
+            tw[k] = tq[k] - td[k] * tv[k];
+            run += tw[k];
         }
+        // sum over the later lanes of the chunk: wave total - inclusive prefix
+        const float incl = wave_inclusive_scan(run);
+        const float total = __shfl(incl, 63, 64);
+        float suffix = a + (total - incl);
 #pragma unroll
-        for (int k = NB - 1; k >= 0; --k) {
-            if (tb + k >= tz) continue;
-            suffix += tq[k] - td[k] * tv[k];
-            ddt[((size_t)b * L + tb + k) * H + h] = tv[k] + ah * suffix;
-            pa += td[k] * suffix;
-            pd += tx[k];
+        for (int k = K - 1; k >= 0; --k) {
+            suffix += tw[k];
+            if (t0 + k < L) {
+                ddt[((size_t)b * L + t0 + k) * H + h] = tv[k] + ah * suffix;
+                pa += td[k] * suffix;
+            }
         }
     }
     pa = block_sum(pa, s_red);
     pd = block_sum(pd, s_red);
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         dA_bh[bh] = pa;
         dD_bh[bh] = pd;
     }
@@ -247,8 +270,8 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
     if (mfma) e = launch_bwd_dR_mfma_bf16(a, B, P, S, s);
     else e = chunks(true, true, false);
     if (e != hipSuccess) return e;
-    bwd_carry_kernel<<<B * H * (PS / 256), 64, 0, s>>>(k.ws.R, k.ws.G, k.dfinal, k.dh0, L, T, nC,
-                                                       PS);
+    bwd_carry_kernel<<<B * H * (PS / 256), 64, 0, s>>>(k.ws.R, k.ws.G, k.ws.Hc, k.ws.fin,
+                                                       k.dfinal, k.dh0, k.ws.anc, L, T, nC, PS);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (mfma) {
         e = launch_bwd_mfma_bf16(a, B, P, S, s);
@@ -256,9 +279,12 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
         e = chunks(false, false, true);
     }
     if (e != hipSuccess) return e;
-    bwd_scan_kernel<<<B * H, kScanThreads, 0, s>>>(k.ws.q, k.ws.v, k.ws.dyx, k.ws.dt_t, k.A, k.dfinal,
-                                          k.ws.fin, k.ddt, k.ws.dA_bh, k.ws.dD_bh, L, H, PS);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        auto scan = T == 64 ? bwd_scan_kernel<1> : T == 128 ? bwd_scan_kernel<2> : bwd_scan_kernel<4>;
+        scan<<<B * H, kScanThreads, 0, s>>>(k.ws.q, k.ws.v, k.ws.dyx, k.ws.dt_t, k.A, k.ws.anc,
+                                            k.ddt, k.ws.dA_bh, k.ws.dD_bh, L, H, nC, PS / 256);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (parts > 1) {
         const size_t n = (size_t)B * L * G * S;
         bwd_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k.ws.dBh, k.ws.dCh, k.dB,

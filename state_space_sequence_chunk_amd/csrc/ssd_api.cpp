@@ -5,6 +5,8 @@
 // allocated here and no synchronisation happens.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../../include/ssd.h"
 #include "ssd_launch.h"
 
@@ -47,14 +49,16 @@ ssd_status check_shape(const ssd_shape* s) {
         !one_of(s->dstate, {16, 32, 64, 128, 256}))
         return SSD_ERR_UNSUPPORTED;
     // Element counts handed to a kernel must fit the 31-bit index arithmetic, and the
-    // per-batch extents the kernels address through buffer descriptors (32-bit byte
-    // counts and offsets) must stay below 2 GiB; reject larger sizes rather than overflow.
-    const double per_batch_states = (double)s->nheads * nchunks_of(s) * s->headdim *
-                                    s->dstate * 4.0;
-    const double states = per_batch_states / 4.0 * (double)s->batch;
+    // extents the kernels address through buffer descriptors (32-bit byte counts and
+    // offsets) must stay below 2 GiB: one chunk's rows of x, y, B, C and their gradients
+    // (all heads or groups), and one batch row's decay rows. Each head's chunk state has
+    // a descriptor of its own. Larger sizes are rejected rather than overflowed.
+    const double states = (double)s->batch * s->nheads * nchunks_of(s) * s->headdim * s->dstate;
     const double xs = (double)s->batch * s->seqlen * s->nheads * s->headdim;
+    const double row = (double)std::max(s->nheads * s->headdim, s->ngroups * s->dstate);
+    const double chunk_rows = (double)s->chunk * row * 4.0;
     const double per_batch_decay = (double)s->nheads * s->seqlen * 4.0;
-    if (states > 2.0e9 || xs > 2.0e9 || per_batch_states >= 2147483648.0 ||
+    if (states > 2.0e9 || xs > 2.0e9 || chunk_rows >= 2147483648.0 ||
         per_batch_decay >= 2147483648.0)
         return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
@@ -102,14 +106,22 @@ size_t forward_ws(const ssd_shape* s) {  // G, dt_t, increments, chunk-initial s
 
 // Backward workspace: the forward quantities it recomputes and its per-token partials.
 struct BwdSizes {
-    size_t dec, st, fin, tok, bh, part, total;
+    size_t dec, st, fin, tok, bh, part, anc, total;
 };
 // The shape the backward pass runs at: the caller's, with the chunk length of the
-// matrix-core plan when there is one.
+// matrix-core plan when there is one and the recomputed fp32 chunk states at that length
+// stay within the size limits (shorter chunks mean more states); otherwise the fp32 token
+// walks at the caller's chunk length. The backward keeps fp32 states and y.
 ssd_shape bwd_shape(const ssd_shape* s) {
     ssd_shape b = *s;
+    b.states_dtype = SSD_F32;
+    b.out_dtype = SSD_F32;
     const int t = ssd::bwd_mfma_chunk(s->in_dtype, (int)s->headdim, (int)s->dstate);
-    if (t) b.chunk = t;
+    if (t) {
+        ssd_shape m = b;
+        m.chunk = t;
+        if (check_shape(&m) == SSD_OK) b.chunk = t;
+    }
     return b;
 }
 
@@ -128,7 +140,11 @@ BwdSizes bwd_sizes(const ssd_shape* shape) {
     z.part = parts > 1 ? round_up((size_t)s->batch * s->seqlen * s->ngroups * parts * s->dstate *
                                   sizeof(float))
                        : 0;
-    z.total = s->seqlen == 0 ? 0 : 2 * z.dec + 2 * z.st + z.fin + 3 * z.tok + 2 * z.bh + 2 * z.part;
+    // per-chunk anchors of the log-decay suffix sums, P*S/256 partials per chunk
+    z.anc = round_up(chunk_states_elems(s) / 256 * sizeof(float));
+    z.total = s->seqlen == 0 ? 0
+                             : 2 * z.dec + 2 * z.st + z.fin + 3 * z.tok + 2 * z.bh + 2 * z.part +
+                                   z.anc;
     return z;
 }
 
@@ -332,6 +348,7 @@ ssd_status ssd_backward(const ssd_shape* shape, const void* x, const void* dt, c
     k.ws.dD_bh = take(z.bh);
     k.ws.dBh = take(z.part);
     k.ws.dCh = take(z.part);
+    k.ws.anc = take(z.anc);
     const ssd_shape bs = bwd_shape(shape);
     return hip_status(ssd::launch_backward(shape->in_dtype, k, dims_of(&bs), (hipStream_t)stream));
 }

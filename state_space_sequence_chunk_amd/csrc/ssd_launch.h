@@ -45,6 +45,7 @@ struct BwdWorkspace {
     float *v, *q, *dyx;   // [B, H, L] per-token scalars
     float *dA_bh, *dD_bh; // [B, H]
     float *dBh, *dCh;     // [B, L, H, S] per-head dB, dC (when heads share a group)
+    float* anc;           // [B, H, nC, P*S/256] partial sums of <R_c, state after chunk c>
 };
 struct BwdLaunch {
     const void *x, *dt, *B, *C;

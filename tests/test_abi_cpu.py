@@ -192,14 +192,16 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 def test_backward_workspace_sizes():
     # G, dt_t, chunk-initial states, gradients at the chunk ends, final state, three
-    # per-token scalars, two per-(batch, head) partials, and per-head dB, dC (shared groups)
+    # per-token scalars, two per-(batch, head) partials, per-head dB, dC (shared groups),
+    # and the per-chunk anchors of the log-decay suffix sums
     # bf16 inputs, P = 64, S = 128: the matrix-core kernels run at 128-token chunks (3 here)
     s = shape(seqlen=300)
     dec = _round256(2 * 8 * 300 * 4)
     fin = 2 * 8 * 64 * 128 * 4
     part = _round256(2 * 300 * 8 * 128 * 4)
     st = 2 * 8 * 3 * 64 * 128 * 4
-    want = 2 * dec + 2 * st + fin + 3 * dec + 2 * 256 + 2 * part
+    anc = _round256(st // 256)  # per-chunk anchors of the log-decay suffix sums
+    want = 2 * dec + 2 * st + fin + 3 * dec + 2 * 256 + 2 * part + anc
     assert ssd.backward_workspace_bytes(s) == want
     # one head per group: the per-head partials are the outputs themselves
     s1 = shape(seqlen=300, ngroups=8)
@@ -207,7 +209,7 @@ def test_backward_workspace_sizes():
     # fp32 inputs take the token walks at the caller's chunk (2 chunks of 256); the
     # backward pass ignores states_dtype and out_dtype
     st2 = 2 * 8 * 2 * 64 * 128 * 4
-    want2 = 2 * dec + 2 * st2 + fin + 3 * dec + 2 * 256 + 2 * part
+    want2 = 2 * dec + 2 * st2 + fin + 3 * dec + 2 * 256 + 2 * part + _round256(st2 // 256)
     for sd in (ssd.SSD_F32, ssd.SSD_BF16):
         assert ssd.backward_workspace_bytes(shape(seqlen=300, in_dtype=ssd.SSD_F32,
                                                   states_dtype=sd)) == want2
@@ -248,4 +250,25 @@ def test_backward_workspace_without_partials():
     st = 2 * 80 * 128 * 64 * 128 * 4
     fin = 2 * 80 * 64 * 128 * 4
     bh = _round256(2 * 80 * 4)
-    assert ssd.backward_workspace_bytes(s) == 2 * dec + 2 * st + fin + 3 * dec + 2 * bh
+    anc = _round256(st // 256)
+    assert ssd.backward_workspace_bytes(s) == 2 * dec + 2 * st + fin + 3 * dec + 2 * bh + anc
+
+
+def test_backward_chunk_stays_within_size_limits():
+    # dstate 256 has a matrix-core plan at 64-token chunks, but at 262144 tokens and 32
+    # heads its fp32 chunk states would pass 2e9 elements; the backward then takes the fp32
+    # token walks at the caller's 256-token chunks (a quarter of the states)
+    L = 262144
+    s = shape(batch=1, seqlen=L, nheads=32, ngroups=1, headdim=64, dstate=256, chunk=256)
+    dec = _round256(32 * L * 4)
+    st = 32 * (L // 256) * 64 * 256 * 4
+    fin = 32 * 64 * 256 * 4
+    bh = _round256(32 * 4)
+    part = L * 32 * 256 * 4  # per-head dB, dC partials of the walks
+    anc = _round256(st // 256)
+    assert ssd.backward_workspace_bytes(s) == (2 * dec + 2 * st + fin + 3 * dec + 2 * bh +
+                                               2 * part + anc)
+    # 16 heads stay within the limit at 64-token chunks: the matrix-core plan applies, with
+    # four times the chunk states
+    s16 = shape(batch=1, seqlen=L, nheads=16, ngroups=1, headdim=64, dstate=256, chunk=256)
+    assert ssd.backward_workspace_bytes(s16) > 2 * 16 * (L // 64) * 64 * 256 * 4

@@ -2,13 +2,13 @@
 
 The oracle's gradients are pinned by finite differences on the CPU. Bounds on
 max|got - oracle| / rms(oracle) for every gradient: 1e-4 with fp32 inputs (fp32
-arithmetic, the longest chains being the per-chunk and suffix sums over the tokens of a
-sequence), 2e-2 with bf16 inputs (the recomputed chunk-initial states go through the bf16
-forward state pass, as in the forward parity bound). dA gets 1e-3 with fp32 inputs: per
-head it is one number, sum_t dt_t sum_{t' >= t} (q_t' - dt_t' v_t'), whose terms cancel
-(q_t and dt_t v_t are of the same size and sign), so the fp32 rounding of every per-token
-term is amplified by the ratio of the terms' absolute sum to |dA|, which is in the
-hundreds to thousands for these inputs.
+arithmetic, the longest chains being the per-chunk sums over a chunk's tokens and the
+inner products over a head's P x S state), 2e-2 with bf16 inputs (the recomputed
+chunk-initial states go through the bf16 forward state pass, as in the forward parity
+bound). dA, one number per head, sums dt_t dL/da_t over the sequence; dL/da_t is summed
+from the end of its own chunk (anchored there by the inner product of gradient and
+state), so its rounding does not grow with the sequence length and dA takes the same
+bounds.
 """
 import numpy as np
 import pytest
@@ -54,15 +54,11 @@ def run_oracle(cpu, *, D=True, h0=True, dfinal=True):
                            cpu["dfinal"] if dfinal else None)
 
 
-TOL_DA = {"fp32": 1e-3, "bf16": 2e-2}
-
-
 def check(tag, got, ref, dtype, names=NAMES):
     errs = {n: max_rel_rms(got[n], ref[n]) for n in names}
     _print(f"{tag}: " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
     for n, e in errs.items():
-        tol = TOL_DA[dtype] if n == "dA" else TOL[dtype]
-        assert e <= tol, f"{tag}: {n} max|d|/rms = {e:.2e} > {tol}"
+        assert e <= TOL[dtype], f"{tag}: {n} max|d|/rms = {e:.2e} > {TOL[dtype]}"
 
 
 # The five workloads at sizes the oracle finishes in seconds: the small ones whole, the
@@ -162,6 +158,27 @@ def test_backward_full_size_sampled_heads():
           names=("dx", "ddt", "dA", "dD", "dh0"))
 
 
+def test_backward_long_full_size_sampled_heads():
+    # The long workload at full size (65536 tokens, 80 heads in 8 groups): the matrix-core
+    # plan runs at 64-token chunks, whose fp32 chunk states (5.4 GB for the batch row) pass
+    # what 32-bit byte offsets reach; the oracle checks 3 sampled heads.
+    w = W["long-bf16"]
+    cpu = problem(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.dtype,
+                  w.seed, h0=True)
+    got = run_gpu(cpu, w.chunk)
+    heads = [0, 44, 79]
+    hs = torch.tensor(heads)
+    g_of = hs // (w.nheads // w.ngroups)
+    sub = {"x": cpu["x"][:, :, hs], "dt": cpu["dt"][:, :, hs], "A": cpu["A"][hs],
+           "B": cpu["B"][:, :, g_of], "C": cpu["C"][:, :, g_of], "D": cpu["D"][hs],
+           "h0": cpu["h0"][:, hs], "dy": cpu["dy"][:, :, hs], "dfinal": cpu["dfinal"][:, hs]}
+    ref = run_oracle(sub)
+    got_s = {"dx": got["dx"][:, :, heads], "ddt": got["ddt"][:, :, heads],
+             "dA": got["dA"][heads], "dD": got["dD"][heads], "dh0": got["dh0"][:, heads]}
+    check("long-bf16 full size, heads " + str(heads), got_s, ref, "bf16",
+          names=("dx", "ddt", "dA", "dD", "dh0"))
+
+
 # bf16 shapes of the matrix-core path beyond the workloads: headdim 128 (64-token chunks),
 # one head per group (dB, dC written directly), heads per group with no head blocking (a
 # reduce over every head) and with blocks of 2 heads summed in the kernel (then 4 blocks
@@ -188,3 +205,28 @@ def test_backward_extreme_decay(dtype, T):
     for n in NAMES:
         assert torch.isfinite(got[n]).all(), n
     check(f"extreme decay {dtype}", got, run_oracle(cpu), dtype)
+
+
+def test_backward_bf16_token_walks():
+    # a bf16 shape with no matrix-core plan (headdim 32) takes the token walks
+    cpu = problem(2, 300, 4, 32, 64, 2, "bf16", seed=41)
+    check("bf16 walks (P=32)", run_gpu(cpu, 128), run_oracle(cpu), "bf16")
+
+
+def test_backward_falls_back_within_size_limits():
+    # 262144 tokens, 32 heads, dstate 256: 64-token chunk states would pass 2e9 elements,
+    # so the backward runs the token walks at 256-token chunks; the oracle checks two
+    # sampled heads (each its own group with the shared B, C)
+    B_, L, H, P, S, G = 1, 262144, 32, 64, 256, 1
+    cpu = problem(B_, L, H, P, S, G, "bf16", seed=9)
+    got = run_gpu(cpu, 256)
+    heads = [5, 30]
+    hs = torch.tensor(heads)
+    sub = {"x": cpu["x"][:, :, hs], "dt": cpu["dt"][:, :, hs], "A": cpu["A"][hs],
+           "B": cpu["B"][:, :, [0, 0]], "C": cpu["C"][:, :, [0, 0]], "D": cpu["D"][hs],
+           "h0": cpu["h0"][:, hs], "dy": cpu["dy"][:, :, hs], "dfinal": cpu["dfinal"][:, hs]}
+    ref = run_oracle(sub)
+    got_s = {"dx": got["dx"][:, :, heads], "ddt": got["ddt"][:, :, heads],
+             "dA": got["dA"][heads], "dD": got["dD"][heads], "dh0": got["dh0"][:, heads]}
+    check("size-limit fallback, heads " + str(heads), got_s, ref, "bf16",
+          names=("dx", "ddt", "dA", "dD", "dh0"))
