@@ -22,7 +22,10 @@ hipError_t launch_bwd_dR_mfma_bf16(const BwdArgs& a, int batch, int P, int S, hi
 // chunk c; the suffix sums for da then start from these anchors at every chunk end
 // instead of running over the whole sequence, which keeps their rounding local to a
 // chunk (over the whole sequence it grows with its length).
-constexpr int kCarryBatch = 4;  // chunks whose loads are in flight together
+// dR_c and H_{c+1} are read once and R_c written once here (R_c is read again only by
+// later kernels, long after it has left the caches), so all three go through
+// non-temporal accesses.
+constexpr int kCarryBatch = 8;  // chunks whose loads are in flight together
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -56,8 +59,10 @@ __global__ __launch_bounds__(64) void bwd_carry_kernel(float* __restrict__ R,
         for (int u = 0; u < kCarryBatch; ++u) {
             const int c = c0 - u;
             if (c >= 0) {
-                d[u] = *(const f32x4*)(base + (size_t)c * PS);
-                hn[u] = c + 1 < nC ? *(const f32x4*)(hbase + (size_t)(c + 1) * PS) : hfin;
+                d[u] = __builtin_nontemporal_load((const f32x4*)(base + (size_t)c * PS));
+                hn[u] = c + 1 < nC
+                            ? __builtin_nontemporal_load((const f32x4*)(hbase + (size_t)(c + 1) * PS))
+                            : hfin;
                 dec[u] = exp2_fast(gr[min((c + 1) * T, L) - 1]);
             }
         }
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(64) void bwd_carry_kernel(float* __restrict__ R,
             const int c = c0 - u;
             part[u] = 0.f;
             if (c >= 0) {
-                *(f32x4*)(base + (size_t)c * PS) = r;
+                __builtin_nontemporal_store(r, (f32x4*)(base + (size_t)c * PS));
                 part[u] = r[0] * hn[u][0] + r[1] * hn[u][1] + r[2] * hn[u][2] + r[3] * hn[u][3];
                 r = dec[u] * r + d[u];
             }
