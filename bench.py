@@ -9,6 +9,9 @@ bracketed by device synchronisation and timed with HIP events; `value` is tokens
 second over it. A second region runs the same K steps through the three stage entry
 points with HIP events between them on the launch stream, which gives each stage's
 average duration for the roofline figures. Prints one JSON line.
+
+python bench.py --state-pass-sweep times the two state-pass implementations (two kernels,
+or one sequential pass) over layers of growing batch, one JSON line per layer.
 """
 from __future__ import annotations
 
@@ -221,6 +224,59 @@ def time_backward(torch, ssd, gen, w, d, stream, steps, warmup):
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+# Layers of the workloads' per-head shapes at growing batch (tokens per batch row as in
+# the workload, or split so the total stays that of one 65536-token row): batch, seqlen,
+# nheads, headdim, dstate, ngroups, chunk.
+SWEEP_SHAPES = [("2.7b", b, 16384, 80, 64, 128, 1, 256) for b in (1, 2, 4, 8, 16)] + \
+    [("780m", b, 8192, 48, 64, 128, 1, 256) for b in (2, 4, 8, 16)] + \
+    [("long", b, 65536 // b, 80, 64, 256, 8, 256) for b in (1, 2, 4)] + \
+    [("headdim128", 4, 8192, 32, 128, 128, 1, 256)]
+
+
+def state_pass_sweep(torch, ssd, gen, reps=20, warmup=5):
+    """The two state-pass implementations on the same bf16 inputs: ssd_state_pass
+    (chunk_state + state_carry) and ssd_state_scan (one sequential pass per (batch, head,
+    64-row slice)), bf16 states, ms per call with events on the launch stream; one JSON
+    line per shape."""
+    stream = torch.cuda.current_stream()
+
+    def t_ms(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for name, B, L, H, P, S, G, T in SWEEP_SHAPES:
+        g = torch.Generator()
+        g.manual_seed(1)
+        d = {k: (None if v is None else v.cuda())
+             for k, v in gen.draw(B, L, H, P, S, G, torch.bfloat16, g).items()}
+        sh = ssd.shape_of(d["x"], d["B"], T, torch.bfloat16)
+        Gc = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+        dtt = torch.empty_like(Gc)
+        ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], Gc, dtt, stream)
+        st = torch.empty((B, H, L // T, P, S), dtype=torch.bfloat16, device="cuda")
+        fin = torch.empty((B, H, P, S), dtype=torch.float32, device="cuda")
+        ws = torch.empty(ssd.state_pass_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+        tp = t_ms(lambda: ssd.ssd_state_pass(sh, d["x"], d["A"], d["B"], Gc, dtt, d["h0"], st,
+                                             fin, ws, stream))
+        ts = t_ms(lambda: ssd.ssd_state_scan(sh, d["x"], d["A"], d["B"], dtt, d["h0"], st, fin,
+                                             stream))
+        blocks = B * H * (P // 64)
+        print(json.dumps({"layer": name, "batch": B, "seqlen": L, "nheads": H, "headdim": P,
+                          "dstate": S, "chunk": T, "workgroups_64_rows": blocks,
+                          "state_pass_ms": round(tp, 4), "state_scan_ms": round(ts, 4),
+                          "scan_over_pass": round(ts / tp, 3)}), flush=True)
+        del d, Gc, dtt, st, fin, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +289,8 @@ def main():
                          "used to calibrate the HBM byte counters")
     ap.add_argument("--sources-sha256", action="store_true",
                     help="print the hash of the chunk-output kernel sources and exit")
+    ap.add_argument("--state-pass-sweep", action="store_true",
+                    help="only time the two state-pass kernels over layers of growing batch")
     args = ap.parse_args()
     if args.sources_sha256:
         print(sources_sha256(CHUNK_OUT_SOURCES))
@@ -256,6 +314,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 3}), flush=True)
+        return
+    if args.state_pass_sweep:
+        state_pass_sweep(torch, ssd, gen)
         return
     copy_gbps = measure_copy_bandwidth(torch)
     w = gen.WORKLOADS[args.workload]

@@ -124,6 +124,21 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
                           void* stream);
 
 /*
+ * Stage 2 in one kernel, as the page's state kernel does it (section "Kernel 2:
+ * fwd_pass_state"): the same outputs as ssd_state_pass (states for every chunk, and the
+ * final state when final_state is not NULL) from one sequential pass over the chunks per
+ * (batch, head, slice of headdim rows), the running state held on chip; no workspace, and
+ * G is not needed (the exponents come from A and dt_t). Built for bf16 inputs, headdim 64
+ * or 128, dstate 64, 128 or 256, and seqlen a positive multiple of chunk; other shapes
+ * return SSD_ERR_UNSUPPORTED. The fused state operand dt_j 2^{G_last - G_j} x_j enters the
+ * matrix cores as a bf16 high/low pair, as in ssd_state_pass. ssd_forward takes this kernel
+ * instead of the two-kernel pass for the shapes where it measured faster.
+ */
+ssd_status ssd_state_scan(const ssd_shape* shape, const void* x, const float* A, const void* B,
+                          const float* dt_t, const float* h0, void* states, float* final_state,
+                          void* stream);
+
+/*
  * Stage 3 -- fused chunk output (section "Kernel 3: compute_out"). For chunk c, rows i
  * and columns j the chunk's tokens:
  *     y_i = 2^{G_i} C_i^T S_c + sum_{j <= i} 2^{G_i - G_j} (C_i . B_j) dt_j x_j + D[h] x_i

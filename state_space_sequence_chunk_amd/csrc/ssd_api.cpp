@@ -227,6 +227,21 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
                                               final_state, d, s));
 }
 
+ssd_status ssd_state_scan(const ssd_shape* shape, const void* x, const float* A, const void* B,
+                          const float* dt_t, const float* h0, void* states, float* final_state,
+                          void* stream) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    const Dims d = dims_of(shape);
+    SSD_REQUIRE(ssd::state_scan_supported(shape->in_dtype, d), SSD_ERR_UNSUPPORTED);
+    SSD_REQUIRE(x && A && B && dt_t && states, SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(A) && aligned16(B) && aligned16(dt_t) && aligned16(h0) &&
+                    aligned16(states) && aligned16(final_state),
+                SSD_ERR_ALIGN);
+    return hip_status(ssd::launch_state_scan(shape->states_dtype, x, B, A, dt_t, h0, states,
+                                             final_state, d, (hipStream_t)stream));
+}
+
 ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, const void* C,
                          const float* G, const float* dt_t, const void* states, const float* D,
                          void* y, void* stream) {
@@ -269,9 +284,13 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
 
     hipError_t e = ssd::launch_cumsum(shape->in_dtype, dt, A, G, dt_t, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
-    e = ssd::launch_chunk_state(shape->in_dtype, x, B, A, dt_t, dS, d, s);
-    if (e != hipSuccess) return SSD_ERR_HIP;
-    e = ssd::launch_state_carry(shape->states_dtype, dS, G, h0, states, final_state, d, s);
+    if (ssd::state_scan_supported(shape->in_dtype, d) && ssd::state_scan_preferred(shape->in_dtype, d)) {
+        e = ssd::launch_state_scan(shape->states_dtype, x, B, A, dt_t, h0, states, final_state, d, s);
+    } else {
+        e = ssd::launch_chunk_state(shape->in_dtype, x, B, A, dt_t, dS, d, s);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+        e = ssd::launch_state_carry(shape->states_dtype, dS, G, h0, states, final_state, d, s);
+    }
     if (e != hipSuccess) return SSD_ERR_HIP;
     return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype,
                                             shape->out_dtype, x, B, C, G,

@@ -27,6 +27,17 @@ hipError_t launch_state_carry(int states_dtype, const float* dstate_chunks, cons
                               const float* h0, void* states, float* final_state, const Dims& d,
                               hipStream_t stream);
 
+// Single-pass state kernel, the alternative to chunk_state + state_carry: one workgroup
+// per (batch, head, slice of headdim rows) walks the whole sequence with the running state
+// in registers. Built for bf16 inputs, headdim 64 or 128, dstate 64, 128 or 256, and a
+// sequence of whole chunks (seqlen a positive multiple of the chunk length).
+bool state_scan_supported(int in_dtype, const Dims& d);
+// Whether the forward pass takes the single-pass kernel for this shape (measured faster).
+bool state_scan_preferred(int in_dtype, const Dims& d);
+hipError_t launch_state_scan(int states_dtype, const void* x, const void* Bm, const float* A,
+                             const float* dt_t, const float* h0, void* states,
+                             float* final_state, const Dims& d, hipStream_t stream);
+
 // final_state = h0 (zeros when h0 is NULL): the state after an empty sequence.
 hipError_t launch_state_init(const float* h0, float* final_state, const Dims& d,
                              hipStream_t stream);

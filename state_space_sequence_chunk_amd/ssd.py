@@ -22,7 +22,7 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE"
 # Entry points declared in include/ssd.h.
 EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_bytes",
            "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
-           "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
+           "ssd_state_scan", "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
            "ssd_backward")
 
 
@@ -64,6 +64,7 @@ def load_library():
     lib.ssd_state_pass_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
     lib.ssd_chunk_cumsum.argtypes = [sp, vp, vp, vp, vp, vp]
     lib.ssd_state_pass.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_state_scan.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_out.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -153,6 +154,12 @@ def ssd_state_pass(shape, x, A, B, G, dt_t, h0, states, final_state, workspace, 
     _check(load_library().ssd_state_pass(ctypes.byref(shape), _p(x), _p(A), _p(B), _p(G), _p(dt_t),
                                          _p(h0), _p(states), _p(final_state), _p(workspace),
                                          nbytes, _stream(stream)), "ssd_state_pass")
+
+
+def ssd_state_scan(shape, x, A, B, dt_t, h0, states, final_state, stream=None):
+    _check(load_library().ssd_state_scan(ctypes.byref(shape), _p(x), _p(A), _p(B), _p(dt_t),
+                                         _p(h0), _p(states), _p(final_state), _stream(stream)),
+           "ssd_state_scan")
 
 
 def ssd_chunk_out(shape, x, B, C, G, dt_t, states, D, y, stream=None):

@@ -152,6 +152,28 @@ def test_stage_entry_points_reject_before_launch():
     assert lib.ssd_chunk_out(ctypes.byref(s), f, f, f, f, f, f, _v(FAKE + 2), f, None) == 6
 
 
+def test_state_scan_rejects_before_launch():
+    lib = ssd.load_library()
+    f = _v(FAKE)
+    # x A B dt_t h0 states final
+    args = [f, f, f, f, None, f, None]
+    s = shape()
+    for i in (0, 1, 2, 3, 5):  # required pointers
+        bad = list(args)
+        bad[i] = None
+        assert lib.ssd_state_scan(ctypes.byref(s), *bad, None) == 1, i
+    bad = list(args)
+    bad[5] = _v(FAKE + 4)  # misaligned states
+    assert lib.ssd_state_scan(ctypes.byref(s), *bad, None) == 6
+    # shapes outside the kernel's plans: fp32 inputs, a partial last chunk, headdim 32,
+    # dstate 32, the empty sequence
+    for kw in (dict(in_dtype=ssd.SSD_F32, states_dtype=ssd.SSD_F32), dict(seqlen=500),
+               dict(headdim=32), dict(dstate=32), dict(seqlen=0)):
+        assert lib.ssd_state_scan(ctypes.byref(shape(**kw)), *args, None) == 4, kw
+    assert lib.ssd_state_scan(ctypes.byref(shape(ngroups=3)), *args, None) == 2
+    assert lib.ssd_state_scan(None, *args, None) == 1
+
+
 def test_decode_step_rejects_before_launch():
     lib = ssd.load_library()
     f = _v(FAKE)

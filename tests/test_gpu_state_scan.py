@@ -1,0 +1,123 @@
+"""Parity of the single-pass state kernel (ssd_state_scan, through the C ABI) with the fp64
+oracle: the chunk-initial states and the final state, under the bounds the two-kernel
+state pass is held to (bf16 inputs: 2e-2 of max|d|/rms for fp32 states; bf16 states
+within their rounding bound), and the forward pass's dispatch between the two."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import TOL, gpu_forward, make, needs_gpu, np64, oracle_forward, reduced
+from metrics import max_rel_rms
+from state_space_sequence_chunk_amd import inputs as gen
+from state_space_sequence_chunk_amd import ssd
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+W = gen.WORKLOADS
+
+
+def _print(msg):
+    print(msg, flush=True)
+
+
+def run_scan(d, chunk, states_dtype, *, h0=True, final=True):
+    sh = ssd.shape_of(d["x"], d["B"], chunk, states_dtype)
+    b, L, H, P = d["x"].shape
+    S = d["B"].shape[3]
+    G = torch.empty((b, H, L), dtype=torch.float32, device="cuda")
+    dt_t = torch.empty_like(G)
+    ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dt_t)
+    st = torch.full((b, H, L // chunk, P, S), float("nan"), dtype=states_dtype, device="cuda")
+    fin = torch.full((b, H, P, S), float("nan"), dtype=torch.float32, device="cuda") if final else None
+    ssd.ssd_state_scan(sh, d["x"], d["A"], d["B"], dt_t, d["h0"] if h0 else None, st, fin)
+    torch.cuda.synchronize()
+    return st, fin
+
+
+def check_states(tag, got, s_ref, dtype):
+    got = np64(got)
+    r = float(np.sqrt(np.mean(s_ref * s_ref)))
+    if r == 0.0:
+        assert np.all(got == 0.0), tag
+        return
+    if dtype == torch.bfloat16:
+        # bf16 storage: rounding to nearest even moves each value by up to 2^-9 of itself;
+        # bound 2^-8 |ref| plus 1e-3 rms(ref) for the fp32 arithmetic before it
+        excess = np.abs(got - s_ref) - (2.0 ** -8 * np.abs(s_ref) + 1e-3 * r)
+        _print(f"{tag}: bf16 states, worst excess over the rounding bound {excess.max() / r:.2e} rms")
+        assert excess.max() <= 0.0, tag
+    else:
+        e = max_rel_rms(got, s_ref)
+        _print(f"{tag}: states max/rms {e:.2e}")
+        assert e <= TOL["bf16"], tag
+
+
+SHAPES = {
+    # the bf16 workloads on one batch row and 1024 tokens
+    "small-bf16": W["small-bf16"],
+    "780m-bf16": reduced(W["780m-bf16"], batch=1, seqlen=1024),
+    "2.7b-bf16": reduced(W["2.7b-bf16"], batch=1, seqlen=1024, nheads=40),
+    "long-bf16": reduced(W["long-bf16"], batch=1, seqlen=1024, nheads=40),
+    # headdim 128 (64-row slices) with dstate 64 and 256, 128- and 64-token chunks
+    "P128-S64-T128": gen.Workload("P128-S64-T128", 2, 512, 4, 128, 64, 2, 128, "bf16", True, 51),
+    "P128-S256-T64": gen.Workload("P128-S256-T64", 1, 384, 4, 128, 256, 1, 64, "bf16", True, 52),
+    # 256 (batch, head) pairs: 64-row slices of headdim 64
+    "many-heads": gen.Workload("many-heads", 4, 256, 64, 64, 64, 4, 64, "bf16", True, 53),
+}
+
+
+@pytest.mark.parametrize("states", ["bf16", "fp32"])
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_state_scan_parity(name, states):
+    w = SHAPES[name]
+    cpu, d = make(w)
+    st_dt = torch.bfloat16 if states == "bf16" else torch.float32
+    st, fin = run_scan(d, w.chunk, st_dt)
+    ref = oracle_forward(cpu, emit_every=w.chunk)
+    e_fin = max_rel_rms(fin, ref["final"])
+    _print(f"{name}/{states}: final max/rms {e_fin:.2e}")
+    assert e_fin <= TOL["bf16"]
+    check_states(f"{name}/{states}", st, ref["states"], st_dt)
+
+
+def test_state_scan_without_h0_or_final():
+    w = SHAPES["long-bf16"]  # a workload with a random h0, left out here
+    cpu, d = make(w)
+    st, fin = run_scan(d, w.chunk, torch.float32, h0=False, final=False)
+    assert fin is None
+    cpu0 = dict(cpu)
+    cpu0["h0"] = None
+    ref = oracle.forward(cpu0["x"], cpu0["dt"], cpu0["A"], cpu0["B"], cpu0["C"], cpu0["D"], None,
+                         emit_every=w.chunk)
+    assert torch.count_nonzero(st[:, :, 0]) == 0  # the state entering chunk 0 is zero
+    check_states("no h0", st, ref["states"], torch.float32)
+
+
+def test_state_scan_full_size_final_state():
+    # The 2.7B layer at full size (2 x 16384 tokens, 80 heads): final states of sampled
+    # (batch, head) pairs against the oracle's recurrence over every token
+    w = W["2.7b-bf16"]
+    cpu, d = make(w)
+    st, fin = run_scan(d, w.chunk, torch.bfloat16)
+    assert bool(torch.isfinite(fin).all())
+    pairs = [(0, 0), (1, 41), (1, 79)]
+    ref = oracle.forward_pairs(pairs, cpu["x"], cpu["dt"], cpu["A"], cpu["B"], cpu["C"],
+                               cpu["D"], cpu["h0"])
+    for k, (b, h) in enumerate(pairs):
+        e = max_rel_rms(fin[b, h], ref["final"][k])
+        _print(f"2.7b-bf16 full size (b={b}, h={h}): final max/rms {e:.2e}")
+        assert e <= TOL["bf16"]
+
+
+def test_forward_through_state_scan():
+    # 4 x 128 heads of headdim 64: 512 workgroups of 64 rows (two full rounds over the
+    # compute units), where ssd_forward takes the single-pass state kernel; y and the
+    # final state against the oracle, every element
+    w = gen.Workload("wide", 4, 512, 128, 64, 64, 4, 64, "bf16", True, 54)
+    cpu, d = make(w)
+    y, fin = gpu_forward(w, d)
+    ref = oracle_forward(cpu)
+    ey, ef = max_rel_rms(y, ref["y"]), max_rel_rms(fin, ref["final"])
+    _print(f"wide forward: y max/rms {ey:.2e}  final max/rms {ef:.2e}")
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
