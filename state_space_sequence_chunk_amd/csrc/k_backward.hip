@@ -241,10 +241,15 @@ hipError_t launch_backward(int in_dtype, const BwdLaunch& k, const Dims& d, hipS
     // forward quantities: cumulative decay, fp32 chunk-initial states, final state
     e = launch_cumsum(in_dtype, k.dt, k.A, k.ws.G, k.ws.dt_t, d, s);
     if (e != hipSuccess) return e;
-    e = launch_chunk_state(in_dtype, k.x, k.B, k.A, k.ws.dt_t, k.ws.R, d, s);
-    if (e != hipSuccess) return e;
-    e = launch_state_carry(kF32, k.ws.R, k.ws.G, k.h0, k.ws.Hc, k.ws.fin, d, s);
-    if (e != hipSuccess) return e;
+    if (state_scan_preferred(in_dtype, d)) {  // the single pass, where it is the faster
+        e = launch_state_scan(kF32, k.x, k.B, k.A, k.ws.dt_t, k.h0, k.ws.Hc, k.ws.fin, d, s);
+        if (e != hipSuccess) return e;
+    } else {
+        e = launch_chunk_state(in_dtype, k.x, k.B, k.A, k.ws.dt_t, k.ws.R, d, s);
+        if (e != hipSuccess) return e;
+        e = launch_state_carry(kF32, k.ws.R, k.ws.G, k.h0, k.ws.Hc, k.ws.fin, d, s);
+        if (e != hipSuccess) return e;
+    }
 
     BwdArgs a;
     a.x = k.x; a.dt = k.dt; a.Bm = k.B; a.Cm = k.C; a.A = k.A; a.D = k.D; a.dy = k.dy;

@@ -179,6 +179,13 @@ def test_backward_long_full_size_sampled_heads():
           names=("dx", "ddt", "dA", "dD", "dh0"))
 
 
+def test_backward_recompute_through_state_scan():
+    # 4 x 64 heads of headdim 64 at whole 128-token chunks: 256 slices of 64 rows, where
+    # the recomputed forward states come from the single-pass state kernel
+    cpu = problem(4, 256, 64, 64, 128, 1, "bf16", seed=57)
+    check("recompute via state scan", run_gpu(cpu, 256), run_oracle(cpu), "bf16")
+
+
 # bf16 shapes of the matrix-core path beyond the workloads: headdim 128 (64-token chunks),
 # one head per group (dB, dC written directly), heads per group with no head blocking (a
 # reduce over every head) and with blocks of 2 heads summed in the kernel (then 4 blocks

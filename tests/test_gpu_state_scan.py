@@ -64,6 +64,11 @@ SHAPES = {
     "P128-S256-T64": gen.Workload("P128-S256-T64", 1, 384, 4, 128, 256, 1, 64, "bf16", True, 52),
     # 256 (batch, head) pairs: 64-row slices of headdim 64
     "many-heads": gen.Workload("many-heads", 4, 256, 64, 64, 64, 4, 64, "bf16", True, 53),
+    # 64-row slices at the shapes the forward pass takes the kernel for: dstate 128 with
+    # 256-token chunks, and headdim 128 with dstate 256 and 128-token chunks
+    "slices-S128": gen.Workload("slices-S128", 4, 512, 64, 64, 128, 1, 256, "bf16", True, 55),
+    "slices-P128-S256": gen.Workload("slices-P128-S256", 2, 256, 64, 128, 256, 8, 128, "bf16",
+                                     True, 56),
 }
 
 
