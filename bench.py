@@ -49,6 +49,9 @@ def algorithmic(w):
         "cumsum": B * L * H * e + H * 4 + 2 * dec,
         "chunk_state": x + bc + dec + H * 4 + n_states * 4,
         "state_carry": n_states * 4 + B * H * nC * 4 + h0 + n_states * es + fin,
+        # the segmented pass: inputs once, the (segment-relative) chunk states and the
+        # final state once; its per-segment states are not counted (a few % at most)
+        "state_seg": x + bc + dec + H * 4 + h0 + n_states * es + fin,
         "chunk_out": x + 2 * bc + 2 * dec + n_states * es + H * 4 + B * L * H * P * 4,
     }
     fl = {
@@ -73,7 +76,8 @@ def backward_bytes(w):
 # Sources of the chunk-output kernel; the HBM traffic measured with rocprofv3 counters
 # is reported only while they are unchanged since the counters were taken.
 CHUNK_OUT_SOURCES = ("chunk_out.h", "k_chunk_out.cpp", "k_chunk_out_bf16.hip",
-                     "k_chunk_out_bf16_f32.hip", "k_chunk_out_f32.hip", "ssd_device.h")
+                     "k_chunk_out_bf16_f32.hip", "k_chunk_out_f32.hip",
+                     "k_chunk_out_bf16_seg.hip", "ssd_device.h")
 
 
 def sources_sha256(names):
@@ -268,12 +272,22 @@ def state_pass_sweep(torch, ssd, gen, reps=20, warmup=5):
                                              fin, ws, stream))
         ts = t_ms(lambda: ssd.ssd_state_scan(sh, d["x"], d["A"], d["B"], dtt, d["h0"], st, fin,
                                              stream))
+        rec = {}
+        try:
+            wseg = torch.empty(ssd.state_seg_workspace_bytes(sh), dtype=torch.uint8,
+                               device="cuda")
+        except ssd.SSDError:
+            wseg = None
+        if wseg is not None:
+            tg = t_ms(lambda: ssd.ssd_state_seg(sh, d["x"], d["A"], d["B"], Gc, dtt, d["h0"], st,
+                                                fin, wseg, stream))
+            rec = {"state_seg_ms": round(tg, 4), "seg_over_pass": round(tg / tp, 3)}
         blocks = B * H * (P // 64)
         print(json.dumps({"layer": name, "batch": B, "seqlen": L, "nheads": H, "headdim": P,
                           "dstate": S, "chunk": T, "workgroups_64_rows": blocks,
                           "state_pass_ms": round(tp, 4), "state_scan_ms": round(ts, 4),
-                          "scan_over_pass": round(ts / tp, 3)}), flush=True)
-        del d, Gc, dtt, st, fin, ws
+                          "scan_over_pass": round(ts / tp, 3), **rec}), flush=True)
+        del d, Gc, dtt, st, fin, ws, wseg
         torch.cuda.empty_cache()
 
 
@@ -331,7 +345,14 @@ def main():
     states = torch.empty((B, H, nC, P, S), dtype=d["x"].dtype, device=dev)
     fin = torch.empty((B, H, P, S), dtype=torch.float32, device=dev)
     y = torch.empty((B, L, H, P), dtype=torch.float32, device=dev)
-    ws_sp = torch.empty(ssd.state_pass_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+    # the stages as ssd_forward runs them: the segmented state pass (with its output
+    # kernel) where the shape has a segment plan, else the two-kernel state pass
+    try:
+        ws_sp = torch.empty(ssd.state_seg_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+        segmented = True
+    except ssd.SSDError:
+        ws_sp = torch.empty(ssd.state_pass_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+        segmented = False
     fwd = ssd.Forward(d["x"], d["B"], T)
     stream = torch.cuda.current_stream()
 
@@ -341,11 +362,19 @@ def main():
         ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dt_t, stream)
         if ev is not None:
             ev[1].record(stream)
-        ssd.ssd_state_pass(sh, d["x"], d["A"], d["B"], G, dt_t, d["h0"], states, fin, ws_sp,
-                           stream)
+        if segmented:
+            ssd.ssd_state_seg(sh, d["x"], d["A"], d["B"], G, dt_t, d["h0"], states, fin, ws_sp,
+                              stream)
+        else:
+            ssd.ssd_state_pass(sh, d["x"], d["A"], d["B"], G, dt_t, d["h0"], states, fin,
+                               ws_sp, stream)
         if ev is not None:
             ev[2].record(stream)
-        ssd.ssd_chunk_out(sh, d["x"], d["B"], d["C"], G, dt_t, states, d["D"], y, stream)
+        if segmented:
+            ssd.ssd_chunk_out_seg(sh, d["x"], d["B"], d["C"], G, dt_t, states, d["D"], y, ws_sp,
+                                  stream)
+        else:
+            ssd.ssd_chunk_out(sh, d["x"], d["B"], d["C"], G, dt_t, states, d["D"], y, stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -417,7 +446,10 @@ def main():
     kernels = {
         "cumsum": {"ms": stage_ms["cumsum"], "bytes": by["cumsum"]},
         "state_pass": {"ms": stage_ms["state_pass"],
-                       "bytes": by["chunk_state"] + by["state_carry"]},
+                       "impl": ("segmented (state_seg + seg_carry)" if segmented
+                                else "chunk_state + state_carry"),
+                       "bytes": by["state_seg"] if segmented
+                       else by["chunk_state"] + by["state_carry"]},
         "chunk_out": {"ms": stage_ms["chunk_out"], "bytes": by["chunk_out"],
                       "flops_per_head_dense": fl["chunk_out"]},
     }

@@ -89,7 +89,8 @@ const char* ssd_status_string(int status);
 /* Host-only check of a shape against the supported sets; enqueues nothing. */
 ssd_status ssd_validate_shape(const ssd_shape* shape);
 
-/* Workspace sizes in bytes for ssd_forward and ssd_state_pass. Host-only. */
+/* Workspace sizes in bytes for ssd_forward and ssd_state_pass (ssd_state_seg's below).
+ * Host-only. */
 ssd_status ssd_forward_workspace_bytes(const ssd_shape* shape, size_t* bytes);
 ssd_status ssd_state_pass_workspace_bytes(const ssd_shape* shape, size_t* bytes);
 
@@ -150,6 +151,38 @@ ssd_status ssd_state_scan(const ssd_shape* shape, const void* x, const float* A,
 ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, const void* C,
                          const float* G, const float* dt_t, const void* states, const float* D,
                          void* y, void* stream);
+
+/*
+ * Stage 2 by segments, with stage 3 to match (the linearity of the recurrence of section
+ * "Mamba-2 architecture" applied to the state kernel of section "Kernel 2:
+ * fwd_pass_state"). The chunks are cut into segments of K consecutive chunks (K and the
+ * heads per workgroup are the library's choice for the shape). Each segment is walked from
+ * a zero state (segment 0 from h0), so what ssd_state_seg records in states[b,h,c] is the
+ * state entering chunk c minus the part carried in from before its segment; the true
+ * state is
+ *     S_c = states[b,h,c] + 2^{D_c} S_in(k),   k = c / K,  D_c = sum of G_last over the
+ *                                              segment's chunks before c,
+ * with S_in(k) the state entering segment k (S_in(0) adds nothing). ssd_state_seg also
+ * writes S_in(k) (bf16), D_c and the final state (fp32, when final_state is not NULL)
+ * into / from its workspace, and ssd_chunk_out_seg computes y as ssd_chunk_out does from
+ * the true states, adding 2^{D_c} S_in(k) while it stages each chunk's state (fp32 sum,
+ * one bf16 rounding). The per-chunk state increments never go to HBM. ssd_forward runs
+ * these two (after stage 1) whenever the shape has a segment plan.
+ * Built for bf16 inputs with bf16 states (states_dtype SSD_BF16), headdim 64, dstate 64
+ * or 128; other shapes return SSD_ERR_UNSUPPORTED (as does the workspace query). Inputs
+ * as for ssd_state_pass and ssd_chunk_out; the workspace must hold
+ * ssd_state_seg_workspace_bytes bytes and is passed unchanged from ssd_state_seg to
+ * ssd_chunk_out_seg on the same stream (it carries S_in and D_c between them).
+ */
+ssd_status ssd_state_seg_workspace_bytes(const ssd_shape* shape, size_t* bytes);
+ssd_status ssd_state_seg(const ssd_shape* shape, const void* x, const float* A, const void* B,
+                         const float* G, const float* dt_t, const float* h0, void* states,
+                         float* final_state, void* workspace, size_t workspace_bytes,
+                         void* stream);
+ssd_status ssd_chunk_out_seg(const ssd_shape* shape, const void* x, const void* B, const void* C,
+                             const float* G, const float* dt_t, const void* states,
+                             const float* D, void* y, const void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * The whole forward pass: stage 1, stage 2, stage 3 on one stream. Returns y (out_dtype) and,

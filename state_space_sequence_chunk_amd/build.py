@@ -19,10 +19,10 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT, "libssd_mi355x.so")
 SOURCES = ["ssd_api.cpp", "k_cumsum.hip", "k_chunk_state.hip", "k_chunk_state_mh_bf16.hip",
            "k_chunk_state_mh_f32.hip", "k_state_carry.hip", "k_state_scan.cpp",
-           "k_state_scan_bf16.hip", "k_state_scan_bf16_f32.hip", "k_decode.hip",
+           "k_state_scan_bf16.hip", "k_state_scan_bf16_f32.hip", "k_state_seg_bf16.hip", "k_decode.hip",
            "k_backward.hip", "k_backward_bf16.hip", "k_backward_f32.hip", "k_backward_mfma.hip",
            "k_chunk_out.cpp", "k_chunk_out_bf16.hip", "k_chunk_out_bf16_f32.hip", "k_chunk_out_bf16_ybf16.hip",
-           "k_chunk_out_f32.hip"]
+           "k_chunk_out_f32.hip", "k_chunk_out_bf16_seg.hip"]
 ARCH = "gfx950"
 
 

@@ -118,12 +118,17 @@ __device__ __forceinline__ void store_y(float v, bf16*, BufRsrc r, uint32_t voff
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b), r, voff, soff, 0);
 }
 
-template <typename TIn, typename TS, typename TY, int P, int S, int T>
+// SEGC: the chunk states are relative to the start of their segment of seg_chunks chunks
+// (see state_seg.h); the state of chunk c in segment k >= 1 is states[c] +
+// 2^{dec_in[c]} seg_in[k], formed in fp32 while the state is staged and rounded once.
+template <typename TIn, typename TS, typename TY, int P, int S, int T, bool SEGC = false>
 __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ Bm, const TIn* __restrict__ Cm,
     const float* __restrict__ G, const float* __restrict__ dt_t, const TS* __restrict__ states,
-    const float* __restrict__ Dv, TY* __restrict__ y, int L, int H, int ngroups, int NH) {
+    const float* __restrict__ Dv, TY* __restrict__ y, int L, int H, int ngroups, int NH,
+    const TS* __restrict__ seg_in, const float* __restrict__ dec_in, int seg_chunks) {
     using Cfg = OutCfg<TIn, TS, P, S, T>;
+    static_assert(!SEGC || sizeof(TS) == 2, "segment-relative states are bf16");
     constexpr int NPT = Cfg::NPT, NKS = Cfg::NKS, XS = Cfg::XS, SS = Cfg::SS, BS = Cfg::BS;
     constexpr int VE = Cfg::VE, VES = Cfg::VES, NTHR = Cfg::NTHR;
 
@@ -171,6 +176,12 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     // ---- per-head staging: global -> registers (prefetch) -> LDS ----------------------
     Vec16 px[Cfg::NXV], pst[Cfg::NSV];
     float pg = 0.f, pdt = 0.f, pge = 0.f;
+    // segment correction (SEGC): entering state of this chunk's segment and its decay
+    const int seg = SEGC ? c / seg_chunks : 0;
+    const bool corr = SEGC && seg > 0;  // workgroup-uniform
+    const int nseg = SEGC ? (nC + seg_chunks - 1) / seg_chunks : 0;
+    Vec16 psi[SEGC ? Cfg::NSV : 1];
+    float pdec = 0.f;
     auto load_head = [&](int h) {
 #pragma unroll
         for (int i = 0; i < Cfg::NXV; ++i) {
@@ -186,6 +197,18 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             const int v = tid + i * NTHR;
             if (v < P * S / VES) pst[i] = buf_load16(rst, (uint32_t)(v * 16), 0u);
         }
+        if constexpr (SEGC) {
+            if (corr) {
+                const BufRsrc rsi = make_rsrc(seg_in + (((size_t)b * H + h) * nseg + seg) * P * S,
+                                              (uint32_t)(P * S * sizeof(TS)));
+#pragma unroll
+                for (int i = 0; i < Cfg::NSV; ++i) {
+                    const int v = tid + i * NTHR;
+                    if (v < P * S / VES) psi[i] = buf_load16(rsi, (uint32_t)(v * 16), 0u);
+                }
+                pdec = dec_in[((size_t)b * H + h) * nC + c];
+            }
+        }
         if (tid < T) {
             const uint32_t o = (uint32_t)(((size_t)h * L + t0) * sizeof(float));
             pg = buf_load_f32(rg, min(tid, rows - 1) * 4, o);
@@ -199,6 +222,20 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             const int v = tid + i * NTHR;
             const int r = v / (P / VE), col = (v % (P / VE)) * VE;
             *(Vec16*)(s_x + r * XS + col) = px[i];
+        }
+        if constexpr (SEGC) {
+            if (corr) {
+                const float f = exp2_fast(pdec);
+#pragma unroll
+                for (int i = 0; i < Cfg::NSV; ++i) {
+                    const bf16x8 l8 = __builtin_bit_cast(bf16x8, pst[i]);
+                    const bf16x8 s8 = __builtin_bit_cast(bf16x8, psi[i]);
+                    bf16x8 o;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(to_f32(l8[e]) + f * to_f32(s8[e]));
+                    pst[i] = __builtin_bit_cast(Vec16, o);
+                }
+            }
         }
 #pragma unroll
         for (int i = 0; i < Cfg::NSV; ++i) {
@@ -482,12 +519,13 @@ inline int heads_per_block(const Dims& d, size_t lds_bytes) {
     return best;
 }
 
-template <typename TIn, typename TS, typename TY, int P, int S, int T>
+template <typename TIn, typename TS, typename TY, int P, int S, int T, bool SEGC = false>
 hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G,
                    const float* dt_t, const void* states, const float* D, void* y,
-                   const Dims& d, hipStream_t stream) {
+                   const Dims& d, hipStream_t stream, const void* seg_in = nullptr,
+                   const float* dec_in = nullptr, int seg_chunks = 0) {
     using Cfg = OutCfg<TIn, TS, P, S, T>;
-    auto kern = chunk_out_kernel<TIn, TS, TY, P, S, T>;
+    auto kern = chunk_out_kernel<TIn, TS, TY, P, S, T, SEGC>;
     if (Cfg::LDS_BYTES > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -499,7 +537,8 @@ hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G
     kern<<<nblocks, 2 * T, Cfg::LDS_BYTES, stream>>>((const TIn*)x, (const TIn*)Bm,
                                                      (const TIn*)Cm, G, dt_t,
                                                      (const TS*)states, D, (TY*)y, d.seqlen,
-                                                     d.nheads, d.ngroups, nh);
+                                                     d.nheads, d.ngroups, nh, (const TS*)seg_in,
+                                                     dec_in, seg_chunks);
     return hipGetLastError();
 }
 
@@ -539,6 +578,22 @@ hipError_t out_by_p(const void* x, const void* Bm, const void* Cm, const float* 
         case 64: return out_by_s<TIn, TS, TY, 64>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
         case 128: return out_by_s<TIn, TS, TY, 128>(x, Bm, Cm, G, dt_t, st, D, y, d, s);
     }
+    return hipErrorInvalidValue;
+}
+
+// Segment-relative chunk states (bf16 inputs and states), for the shapes the segmented
+// state pass is built for (headdim 64, dstate 64 or 128).
+template <typename TY>
+hipError_t out_seg(const void* x, const void* Bm, const void* Cm, const float* G,
+                   const float* dt_t, const void* st, const void* seg_in, const float* dec_in,
+                   int seg_chunks, const float* D, void* y, const Dims& d, hipStream_t s) {
+#define SSD_OUT_SEG(p, s_, t)                                                                  \
+    if (d.headdim == p && d.dstate == s_ && d.chunk == t)                                      \
+        return run_out<bf16, bf16, TY, p, s_, t, true>(x, Bm, Cm, G, dt_t, st, D, y, d, s,     \
+                                                       seg_in, dec_in, seg_chunks);
+    SSD_OUT_SEG(64, 64, 64) SSD_OUT_SEG(64, 64, 128) SSD_OUT_SEG(64, 64, 256)
+    SSD_OUT_SEG(64, 128, 64) SSD_OUT_SEG(64, 128, 128) SSD_OUT_SEG(64, 128, 256)
+#undef SSD_OUT_SEG
     return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,151 @@
+// Segmented state pass for bf16 inputs: plan choice, workspace layout and launches
+// (kernels in state_seg.h).
+#include "state_seg.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kSegHeads[] = {1, 2, 3, 4, 5, 6, 8};  // instantiated heads per workgroup
+
+bool seg_shape_fits(int P, int S, int T) {
+    switch (P * 1000000 + S * 1000 + T) {
+#define SSD_SEG_FITS(p, s, t) \
+    case p * 1000000 + s * 1000 + t: return SegCfg<p, s, t>::FITS;
+        SSD_SEG_FITS(64, 64, 64) SSD_SEG_FITS(64, 64, 128) SSD_SEG_FITS(64, 64, 256)
+        SSD_SEG_FITS(64, 128, 64) SSD_SEG_FITS(64, 128, 128) SSD_SEG_FITS(64, 128, 256)
+#undef SSD_SEG_FITS
+    }
+    return false;
+}
+
+template <int P, int S, int T, int NH>
+hipError_t run_seg(const void* x, const void* Bm, const float* A, const float* G,
+                   const float* dt_t, const float* h0, void* states, const SegPlan& pl,
+                   const SegBuffers& sb, const Dims& d, hipStream_t stream) {
+    using Cfg = SegCfg<P, S, T>;
+    auto kern = state_seg_kernel<P, S, T, NH>;
+    if (Cfg::LDS_BYTES > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)Cfg::LDS_BYTES);
+        if (e != hipSuccess) return e;
+    }
+    const int nblocks = d.batch * pl.nseg * (d.nheads / NH);
+    kern<<<nblocks, Cfg::NTHR, Cfg::LDS_BYTES, stream>>>(
+        (const bf16*)x, (const bf16*)Bm, A, G, dt_t, h0, (bf16*)states, sb.seg_end, sb.dec_in,
+        sb.dec_seg, d.seqlen, d.nheads, d.ngroups, pl.chunks);
+    return hipGetLastError();
+}
+
+template <int P, int S, int T>
+hipError_t seg_by_nh(const void* x, const void* Bm, const float* A, const float* G,
+                     const float* dt_t, const float* h0, void* st, const SegPlan& pl,
+                     const SegBuffers& sb, const Dims& d, hipStream_t s) {
+    if constexpr (!SegCfg<P, S, T>::FITS) {
+        return hipErrorInvalidValue;
+    } else {
+        switch (pl.heads) {
+            case 1: return run_seg<P, S, T, 1>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+            case 2: return run_seg<P, S, T, 2>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+            case 3: return run_seg<P, S, T, 3>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+            case 4: return run_seg<P, S, T, 4>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+            case 5: return run_seg<P, S, T, 5>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+            case 6: return run_seg<P, S, T, 6>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+            case 8: return run_seg<P, S, T, 8>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+        }
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int P, int S>
+hipError_t seg_by_t(const void* x, const void* Bm, const float* A, const float* G,
+                    const float* dt_t, const float* h0, void* st, const SegPlan& pl,
+                    const SegBuffers& sb, const Dims& d, hipStream_t s) {
+    switch (d.chunk) {
+        case 64: return seg_by_nh<P, S, 64>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+        case 128: return seg_by_nh<P, S, 128>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+        case 256: return seg_by_nh<P, S, 256>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+}  // namespace
+
+// Plan: heads per workgroup (a divisor of the heads per group, at most 96 state
+// registers per lane) and chunks per segment (at least 2 unless the sequence has one
+// chunk). A workgroup holds one compute unit (its LDS plan takes most of the 160 KB), so
+// the grid runs in rounds of 256; the cost of a plan is its rounds times one workgroup's
+// work, counted in (chunk, head) steps plus a fixed share per workgroup, per chunk (B rows,
+// one more barrier) and per head (its end state). Ties go to longer segments (fewer
+// corrections downstream).
+bool state_seg_plan(int in_dtype, int states_dtype, const Dims& d, SegPlan* out) {
+    if (in_dtype != kBF16 || states_dtype != kBF16) return false;
+    if (!seg_shape_fits(d.headdim, d.dstate, d.chunk)) return false;
+    const int nC = d.nchunks();
+    if (nC < 1) return false;
+    const int hpg = d.nheads / d.ngroups;
+    const int regs_per_head = d.headdim * d.dstate / 512;
+    double best = 1e300;
+    SegPlan bp{0, 0, 0};
+    for (int nh : kSegHeads) {
+        if (hpg % nh != 0 || nh * regs_per_head > 96) continue;
+        for (int k = (nC == 1 ? 1 : 2); k <= nC; ++k) {
+            const int nseg = (nC + k - 1) / k;
+            const long wgs = (long)d.batch * nseg * (d.nheads / nh);
+            const long rounds = (wgs + 255) / 256;
+            const double cost = (double)rounds * (nh * k + 1.0 + 0.5 * k + 0.7 * nh);
+            if (cost < best - 1e-9 || (cost < best + 1e-9 && k > bp.chunks)) {
+                best = cost;
+                bp = SegPlan{nh, k, nseg};
+            }
+        }
+    }
+    if (bp.heads == 0) return false;
+    *out = bp;
+    return true;
+}
+
+// Workspace: segment end states [B,H,nseg,P,S] fp32, entering states [B,H,nseg,P,S] bf16,
+// per-chunk decays [B,H,nC] and per-segment decays [B,H,nseg] fp32.
+size_t state_seg_ws_bytes(const Dims& d, const SegPlan& pl) {
+    const size_t bh = (size_t)d.batch * d.nheads, ps = (size_t)d.headdim * d.dstate;
+    return round256(bh * pl.nseg * ps * 4) + round256(bh * pl.nseg * ps * 2) +
+           round256(bh * d.nchunks() * 4) + round256(bh * pl.nseg * 4);
+}
+
+SegBuffers state_seg_buffers(void* ws, const Dims& d, const SegPlan& pl) {
+    const size_t bh = (size_t)d.batch * d.nheads, ps = (size_t)d.headdim * d.dstate;
+    char* w = (char*)ws;
+    SegBuffers sb;
+    sb.seg_end = (float*)w;
+    w += round256(bh * pl.nseg * ps * 4);
+    sb.seg_in = (void*)w;
+    w += round256(bh * pl.nseg * ps * 2);
+    sb.dec_in = (float*)w;
+    w += round256(bh * d.nchunks() * 4);
+    sb.dec_seg = (float*)w;
+    return sb;
+}
+
+hipError_t launch_state_seg(const void* x, const void* Bm, const float* A, const float* G,
+                            const float* dt_t, const float* h0, void* states,
+                            float* final_state, const SegPlan& pl, const SegBuffers& sb,
+                            const Dims& d, hipStream_t stream) {
+    hipError_t e = hipErrorInvalidValue;
+    switch (d.headdim * 1000 + d.dstate) {
+        case 64064: e = seg_by_t<64, 64>(x, Bm, A, G, dt_t, h0, states, pl, sb, d, stream); break;
+        case 64128: e = seg_by_t<64, 128>(x, Bm, A, G, dt_t, h0, states, pl, sb, d, stream); break;
+    }
+    if (e != hipSuccess) return e;
+    if (pl.nseg == 1 && !final_state) return hipSuccess;
+    const int PS = d.headdim * d.dstate;  // a multiple of 256 for every instantiated size
+    const int nblocks = d.batch * d.nheads * (PS / 256);
+    seg_carry_kernel<<<nblocks, 64, 0, stream>>>(sb.seg_end, sb.dec_seg, (bf16*)sb.seg_in,
+                                                  final_state, pl.nseg, PS);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -99,8 +99,22 @@ size_t chunk_states_elems(const ssd_shape* s) {
 size_t state_pass_ws(const ssd_shape* s) {  // per-chunk state increments, fp32
     return round_up(chunk_states_elems(s) * sizeof(float));
 }
-size_t forward_ws(const ssd_shape* s) {  // G, dt_t, increments, chunk-initial states
-    return 2 * decay_bytes(s) + state_pass_ws(s) +
+// Segment plan of the segmented state pass, when the shape has one.
+bool seg_plan_of(const ssd_shape* s, ssd::SegPlan* plan) {
+    return s->seqlen > 0 && ssd::state_seg_plan(s->in_dtype, s->states_dtype, dims_of(s), plan);
+}
+size_t state_seg_ws(const ssd_shape* s) {  // 0 when the shape has no segment plan
+    ssd::SegPlan pl;
+    return seg_plan_of(s, &pl) ? round_up(ssd::state_seg_ws_bytes(dims_of(s), pl)) : 0;
+}
+// G, dt_t, then the state pass's own buffers (the segmented pass's, else the increments),
+// then the chunk-initial states
+size_t forward_mid_ws(const ssd_shape* s) {
+    ssd::SegPlan pl;
+    return seg_plan_of(s, &pl) ? state_seg_ws(s) : state_pass_ws(s);
+}
+size_t forward_ws(const ssd_shape* s) {
+    return 2 * decay_bytes(s) + forward_mid_ws(s) +
            round_up(chunk_states_elems(s) * esize(s->states_dtype));
 }
 
@@ -191,6 +205,16 @@ ssd_status ssd_state_pass_workspace_bytes(const ssd_shape* shape, size_t* bytes)
     return SSD_OK;
 }
 
+ssd_status ssd_state_seg_workspace_bytes(const ssd_shape* shape, size_t* bytes) {
+    SSD_REQUIRE(bytes, SSD_ERR_NULL);
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    ssd::SegPlan pl;
+    SSD_REQUIRE(shape->seqlen == 0 || seg_plan_of(shape, &pl), SSD_ERR_UNSUPPORTED);
+    *bytes = state_seg_ws(shape);
+    return SSD_OK;
+}
+
 ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float* A, float* G,
                             float* dt_t, void* stream) {
     ssd_status st = check_shape(shape);
@@ -225,6 +249,51 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
     if (e != hipSuccess) return SSD_ERR_HIP;
     return hip_status(ssd::launch_state_carry(shape->states_dtype, dS, G, h0, states,
                                               final_state, d, s));
+}
+
+ssd_status ssd_state_seg(const ssd_shape* shape, const void* x, const float* A, const void* B,
+                         const float* G, const float* dt_t, const float* h0, void* states,
+                         float* final_state, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    const bool empty = shape->seqlen == 0;  // only the final state (= h0) is written
+    ssd::SegPlan pl;
+    SSD_REQUIRE(empty || seg_plan_of(shape, &pl), SSD_ERR_UNSUPPORTED);
+    SSD_REQUIRE(A && (empty || (x && B && G && dt_t && states)), SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(A) && aligned16(B) && aligned16(G) && aligned16(dt_t) &&
+                    aligned16(h0) && aligned16(states) && aligned16(final_state),
+                SSD_ERR_ALIGN);
+    const size_t need = state_seg_ws(shape);
+    SSD_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), SSD_ERR_WORKSPACE);
+    SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
+    const Dims d = dims_of(shape);
+    hipStream_t s = (hipStream_t)stream;
+    if (empty) return final_state ? hip_status(ssd::launch_state_init(h0, final_state, d, s)) : SSD_OK;
+    return hip_status(ssd::launch_state_seg(x, B, A, G, dt_t, h0, states, final_state, pl,
+                                            ssd::state_seg_buffers(workspace, d, pl), d, s));
+}
+
+ssd_status ssd_chunk_out_seg(const ssd_shape* shape, const void* x, const void* B, const void* C,
+                             const float* G, const float* dt_t, const void* states,
+                             const float* D, void* y, const void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    if (shape->seqlen == 0) return SSD_OK;  // empty sequence: no output rows
+    ssd::SegPlan pl;
+    SSD_REQUIRE(seg_plan_of(shape, &pl), SSD_ERR_UNSUPPORTED);
+    SSD_REQUIRE(x && B && C && G && dt_t && states && y, SSD_ERR_NULL);
+    SSD_REQUIRE(aligned16(x) && aligned16(B) && aligned16(C) && aligned16(G) &&
+                    aligned16(dt_t) && aligned16(states) && aligned16(D) && aligned16(y),
+                SSD_ERR_ALIGN);
+    SSD_REQUIRE(workspace && workspace_bytes >= state_seg_ws(shape), SSD_ERR_WORKSPACE);
+    SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
+    const Dims d = dims_of(shape);
+    const ssd::SegBuffers sb = ssd::state_seg_buffers(const_cast<void*>(workspace), d, pl);
+    return hip_status(ssd::launch_chunk_out_seg(shape->out_dtype, x, B, C, G, dt_t, states,
+                                                sb.seg_in, sb.dec_in, pl.chunks, D, y, d,
+                                                (hipStream_t)stream));
 }
 
 ssd_status ssd_state_scan(const ssd_shape* shape, const void* x, const float* A, const void* B,
@@ -279,11 +348,20 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
     char* w = (char*)workspace;
     float* G = (float*)w;
     float* dt_t = (float*)(w + decay_bytes(shape));
-    float* dS = (float*)(w + 2 * decay_bytes(shape));
-    void* states = (void*)(w + 2 * decay_bytes(shape) + state_pass_ws(shape));
+    void* mid = (void*)(w + 2 * decay_bytes(shape));
+    float* dS = (float*)mid;
+    void* states = (void*)(w + 2 * decay_bytes(shape) + forward_mid_ws(shape));
 
     hipError_t e = ssd::launch_cumsum(shape->in_dtype, dt, A, G, dt_t, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
+    ssd::SegPlan pl;
+    if (seg_plan_of(shape, &pl)) {
+        const ssd::SegBuffers sb = ssd::state_seg_buffers(mid, d, pl);
+        e = ssd::launch_state_seg(x, B, A, G, dt_t, h0, states, final_state, pl, sb, d, s);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+        return hip_status(ssd::launch_chunk_out_seg(shape->out_dtype, x, B, C, G, dt_t, states,
+                                                    sb.seg_in, sb.dec_in, pl.chunks, D, y, d, s));
+    }
     if (ssd::state_scan_supported(shape->in_dtype, d) && ssd::state_scan_preferred(shape->in_dtype, d)) {
         e = ssd::launch_state_scan(shape->states_dtype, x, B, A, dt_t, h0, states, final_state, d, s);
     } else {

@@ -38,6 +38,28 @@ hipError_t launch_state_scan(int states_dtype, const void* x, const void* Bm, co
                              const float* dt_t, const float* h0, void* states,
                              float* final_state, const Dims& d, hipStream_t stream);
 
+// Segmented state pass (bf16 inputs, bf16 chunk states): workgroups walk runs of
+// `chunks` consecutive chunks for blocks of `heads` heads from a zero state (segment 0 from
+// h0), recording each chunk's state relative to its segment's start; a small sequential
+// kernel carries the states entering each segment and gives the final state. The output
+// kernel then adds 2^{dec_in} * seg_in to each recorded state (segments >= 1).
+struct SegPlan {
+    int heads, chunks, nseg;
+};
+struct SegBuffers {
+    float* seg_end;   // [B, H, nseg, P, S] each segment's end state from its own start
+    void* seg_in;     // [B, H, nseg, P, S] bf16 state entering each segment (>= 1)
+    float* dec_in;    // [B, H, nC] log2 decay from the segment's start to each chunk's start
+    float* dec_seg;   // [B, H, nseg] each segment's total log2 decay
+};
+bool state_seg_plan(int in_dtype, int states_dtype, const Dims& d, SegPlan* plan);
+size_t state_seg_ws_bytes(const Dims& d, const SegPlan& plan);
+SegBuffers state_seg_buffers(void* workspace, const Dims& d, const SegPlan& plan);
+hipError_t launch_state_seg(const void* x, const void* Bm, const float* A, const float* G,
+                            const float* dt_t, const float* h0, void* states,
+                            float* final_state, const SegPlan& plan, const SegBuffers& sb,
+                            const Dims& d, hipStream_t stream);
+
 // final_state = h0 (zeros when h0 is NULL): the state after an empty sequence.
 hipError_t launch_state_init(const float* h0, float* final_state, const Dims& d,
                              hipStream_t stream);
@@ -76,5 +98,13 @@ hipError_t launch_chunk_out(int in_dtype, int states_dtype, int out_dtype, const
                             const void* Bm, const void* Cm, const float* G, const float* dt_t,
                             const void* states, const float* D, void* y, const Dims& d,
                             hipStream_t stream);
+
+// The output kernel over segment-relative chunk states (bf16 inputs and states): each
+// chunk's state is taken as states[c] + 2^{dec_in[c]} seg_in[c / seg_chunks] for chunks
+// past the first segment.
+hipError_t launch_chunk_out_seg(int out_dtype, const void* x, const void* Bm, const void* Cm,
+                                const float* G, const float* dt_t, const void* states,
+                                const void* seg_in, const float* dec_in, int seg_chunks,
+                                const float* D, void* y, const Dims& d, hipStream_t stream);
 
 }  // namespace ssd

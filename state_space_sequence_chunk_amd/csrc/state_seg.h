@@ -1,0 +1,333 @@
+// Stage 2 by segments: the chunk-initial states of a run of consecutive chunks, with the
+// running state of a block of heads kept on chip (kernel template for bf16 inputs;
+// instances in k_state_seg_bf16.hip).
+//
+// Page "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA CUDA
+// Tile", section "Kernel 2: fwd_pass_state" (the state kernel walks the chunks in order,
+// records the state entering each chunk and advances it by the jump formula of section
+// "Mamba-2 architecture"):
+//     S_{c+1}[p][s] = 2^{g_c} S_c[p][s] + sum_{j in chunk c} x_j[p] (dt_j 2^{G_last - G_j} B_j[s])
+// Because the recurrence is linear in the state, a walk over segment k (chunks
+// kK .. kK+K-1) may start from zero instead of the true entering state S_in(k):
+//     S_c = L_c + 2^{D_c} S_in(k),    D_c = sum of g over the segment's chunks before c,
+// where L_c is the state the walk from zero records. Segment 0 starts from h0, so its
+// recorded states are the true ones. The walk writes L_c (rounded to bf16 like the
+// states the output kernel consumes), D_c, the segment's own end state E_k (fp32) and its
+// total decay; a small sequential kernel then carries S_in(k+1) = 2^{D_k} S_in(k) + E_k
+// across segments (and gives the final state), and the output kernel adds 2^{D_c} S_in(k)
+// while staging each chunk's state. The per-chunk increments never go to HBM.
+//
+// gfx950 mapping: one workgroup of 8 waves per (batch, segment, block of NH heads of one
+// B group). Each head's running state (P x S fp32) is spread over the waves in the MFMA
+// accumulator layout and stays in registers for the whole segment. Per chunk the group's
+// B rows are staged in LDS once and shared by the NH heads; per (chunk, head) the x rows
+// and the decay weights are double-buffered in LDS, the next step's 16-byte loads (and,
+// at a chunk's last head, the next chunk's B rows) in flight while the current products
+// run. The contraction over the chunk's tokens is dS^T = B^T (w o x) on bf16 MFMA
+// 16x16x32 with both operands from the transposing LDS read; the fused operand w_j x_j is
+// formed in fp32 and split into a bf16 high part and a bf16 remainder (two MFMAs against
+// the exact bf16 B). The accumulator holds four consecutive state columns s of one row p
+// per lane, so each recorded state leaves as one 8-byte store per lane and tile. Wave 0
+// forms each head's weights with a single-wave DPP suffix scan.
+#pragma once
+
+#include <algorithm>
+
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int P, int S, int T>
+struct SegCfg {
+    static constexpr int NTHR = 512, NWAVE = 8;
+    static constexpr int NPT = P / 16, NST = S / 16;
+    static constexpr int WPT = NPT >= NWAVE ? 1 : NWAVE / NPT;  // waves per p-tile
+    static constexpr int MST = (NST + WPT - 1) / WPT;           // s-tiles per wave
+    static constexpr int VE = 8;                                // bf16 per 16 bytes
+    static constexpr int XS = col_stride<bf16>(P), BS = col_stride<bf16>(S);
+    static constexpr int NXV = (T * P / VE + NTHR - 1) / NTHR;  // x vectors per thread
+    static constexpr int NBV = (T * S / VE + NTHR - 1) / NTHR;  // B vectors per thread
+    static constexpr int PER = T / 64;                          // tokens per lane in the scan
+    static constexpr size_t X_BYTES = (size_t)T * XS * sizeof(bf16);
+    static constexpr size_t W_BYTES = (size_t)T * sizeof(float);
+    static constexpr size_t B_BYTES = (size_t)T * BS * sizeof(bf16);
+    static constexpr size_t LDS_BYTES = B_BYTES + 2 * (X_BYTES + W_BYTES);
+    // registers per head for the running state (fp32 per lane)
+    static constexpr int STATE_REGS = MST * 4;
+    static constexpr bool FITS = LDS_BYTES <= 163840 && NPT <= NWAVE && NST % WPT == 0;
+};
+
+template <int P, int S, int T, int NH>
+__global__ __launch_bounds__(512) void state_seg_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ A,
+    const float* __restrict__ G, const float* __restrict__ dt_t, const float* __restrict__ h0,
+    bf16* __restrict__ states, float* __restrict__ seg_end, float* __restrict__ dec_in,
+    float* __restrict__ dec_seg, int L, int H, int ngroups, int K) {
+    using Cfg = SegCfg<P, S, T>;
+    constexpr int VE = Cfg::VE, XS = Cfg::XS, BS = Cfg::BS, NTHR = Cfg::NTHR, PER = Cfg::PER;
+    constexpr int MST = Cfg::MST, WPT = Cfg::WPT;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    bf16* s_b = (bf16*)smem;  // [T][BS]
+    auto s_x = [&](int k) { return (bf16*)(smem + Cfg::B_BYTES + k * (Cfg::X_BYTES + Cfg::W_BYTES)); };
+    auto s_w = [&](int k) {
+        return (float*)(smem + Cfg::B_BYTES + k * (Cfg::X_BYTES + Cfg::W_BYTES) + Cfg::X_BYTES);
+    };
+
+    const int nC = (L + T - 1) / T;
+    const int nseg = (nC + K - 1) / K;
+    const int nhb = H / NH;
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int hb = id % nhb;
+    const int seg = (id / nhb) % nseg;
+    const int b = id / (nhb * nseg);
+    const int h_first = hb * NH;
+    const int g = h_first / (H / ngroups);  // NH divides the heads per group
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int HP = H * P;
+    const size_t grow = (size_t)ngroups * S;
+    const int pt = wave / WPT;   // this wave's p-tile
+    const int st0 = wave % WPT;  // first s-tile; stride WPT
+    const int c_first = seg * K;
+    const int nck = min(K, nC - c_first);  // chunks of this segment
+    const int p = pt * 16 + l16;           // this lane's state row (accumulator column)
+    // byte offset of this lane's four state columns of its first s-tile in a P x S block
+    const uint32_t st_off = (uint32_t)((p * S + st0 * 16 + 4 * g4) * sizeof(bf16));
+
+    const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
+    const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
+    auto rows_of = [&](int c) { return min(T, L - c * T); };
+    // x rows past a chunk's real tokens lie outside its descriptor and load as zeros
+    auto x_rsrc = [&](int c) {
+        return make_rsrc(x + ((size_t)b * L + (size_t)c * T) * HP,
+                         (uint32_t)(rows_of(c) * HP * sizeof(bf16)));
+    };
+
+    // ---- staging: global -> registers (prefetch) -> LDS ---------------------------------
+    Vec16 px[Cfg::NXV], pb[Cfg::NBV];
+    float pdt[PER];
+    float gl_next = 0.f;  // the prefetched step's chunk decay g (log2), G at its last real token
+    auto load_head = [&](int c, int h, BufRsrc rx) {
+        const int rows = rows_of(c);
+#pragma unroll
+        for (int i = 0; i < Cfg::NXV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v < T * P / VE) {
+                const int r = v / (P / VE), col = (v % (P / VE)) * VE;
+                px[i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(bf16)),
+                                   (uint32_t)(h * P * sizeof(bf16)));
+            }
+        }
+        const uint32_t o = (uint32_t)(((size_t)h * L + (size_t)c * T) * sizeof(float));
+        gl_next = buf_load_f32(rg, (uint32_t)((rows - 1) * 4), o);
+        if (wave == 0) {  // wave 0 scans the head's decay; lane holds tokens T-1-(PER*lane+k)
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int t = T - 1 - (PER * lane + k);
+                pdt[k] = t < rows ? buf_load_f32(rdt, t * 4, o) : 0.f;
+            }
+        }
+    };
+    // B rows of chunk c through a descriptor over its real rows (padded rows read zeros)
+    auto load_b = [&](int c) {
+        const int rows = rows_of(c);
+        const BufRsrc rb = make_rsrc(Bm + (((size_t)b * L + (size_t)c * T) * ngroups + g) * S,
+                                     (uint32_t)(((size_t)(rows - 1) * grow + S) * sizeof(bf16)));
+#pragma unroll
+        for (int i = 0; i < Cfg::NBV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v < T * S / VE) {
+                const int r = v / (S / VE), col = (v % (S / VE)) * VE;
+                pb[i] = buf_load16(rb, (uint32_t)(((size_t)r * grow + col) * sizeof(bf16)), 0u);
+            }
+        }
+    };
+    auto store_b = [&]() {
+#pragma unroll
+        for (int i = 0; i < Cfg::NBV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v < T * S / VE) {
+                const int r = v / (S / VE), col = (v % (S / VE)) * VE;
+                *(Vec16*)(s_b + r * BS + col) = pb[i];
+            }
+        }
+    };
+    auto store_head = [&](int h, int kb) {
+        bf16* bx = s_x(kb);
+#pragma unroll
+        for (int i = 0; i < Cfg::NXV; ++i) {
+            const int v = tid + i * NTHR;
+            if (v < T * P / VE) {
+                const int r = v / (P / VE), col = (v % (P / VE)) * VE;
+                *(Vec16*)(bx + r * XS + col) = px[i];
+            }
+        }
+        if (wave == 0) {
+            // w_t = dt_t 2^{log2(e) sum_{k>t} A dt_k}: scanned from the chunk's end
+            const float ah = A[h];
+            float pre[PER], run = 0.f;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                pre[k] = run;
+                run += ah * pdt[k];
+            }
+            const float excl = wave_shift_up1(wave_inclusive_scan(run));
+            float* bw = s_w(kb);
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                bw[T - 1 - (PER * lane + k)] = pdt[k] * exp2_fast((excl + pre[k]) * kLog2e);
+        }
+    };
+
+    // ---- running states: h0 for segment 0, zero otherwise -------------------------------
+    // tile m of head hh: element (row s = 16 st + 4 g4 + r, column p) in register r
+    f32x4 acc[NH][MST];
+    float dacc[NH];  // log2 decay from the segment's start (wave-uniform)
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+        dacc[hh] = 0.f;
+#pragma unroll
+        for (int m = 0; m < MST; ++m) {
+            const int s = (st0 + WPT * m) * 16 + 4 * g4;
+            if (seg == 0 && h0)
+                acc[hh][m] = *(const f32x4*)(h0 + (((size_t)b * H + h_first + hh) * P + p) * S + s);
+            else
+                acc[hh][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // ---- prologue: the first chunk's B rows and first head ------------------------------
+    BufRsrc rx = x_rsrc(c_first);
+    load_head(c_first, h_first, rx);
+    load_b(c_first);
+    store_b();
+    store_head(h_first, 0);
+    __syncthreads();
+
+    int kb = 0;  // buffer of the current step
+    for (int ci = 0; ci < nck; ++ci) {
+        const int c = c_first + ci;
+        const bool more = ci + 1 < nck;
+        const BufRsrc rx_next = more ? x_rsrc(c + 1) : rx;
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+            const int h = h_first + hh;
+            const float gl = gl_next;  // this step's chunk decay
+            // the next step's loads are in flight while this step's products run
+            if (hh + 1 < NH) {
+                load_head(c, h + 1, rx);
+            } else if (more) {
+                load_head(c + 1, h_first, rx_next);
+                load_b(c + 1);
+            }
+
+            // record the state entering chunk c (from the segment's start), then advance it
+            const BufRsrc rst = make_rsrc(states + (((size_t)b * H + h) * nC + c) * (size_t)P * S,
+                                          (uint32_t)(P * S * sizeof(bf16)));
+#pragma unroll
+            for (int m = 0; m < MST; ++m) {
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = from_f32<bf16>(acc[hh][m][r]);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), rst, st_off,
+                                                      (uint32_t)(WPT * m * 16 * sizeof(bf16)), 0);
+            }
+            if (tid == 0) dec_in[((size_t)b * H + h) * nC + c] = dacc[hh];
+            dacc[hh] += gl;
+            const float dec = exp2_fast(gl);
+#pragma unroll
+            for (int m = 0; m < MST; ++m) acc[hh][m] *= dec;
+
+            const bf16* bx = s_x(kb);
+            const float* bw = s_w(kb);
+            // slot (g4, v) carries token 32 ks + 16 (v/4) + 4 g4 + v%4 (two column reads)
+#pragma unroll 1
+            for (int ks = 0; ks < T / 32; ++ks) {
+                const int r_lo = ks * 32 + 4 * g4, r_hi = r_lo + 16;
+                Frag<bf16> bf[MST];
+#pragma unroll
+                for (int m = 0; m < MST; ++m) {
+                    const int st = st0 + WPT * m;
+                    const bf16x4 a = lds_col4(s_b, BS, r_lo, st * 16, lane);
+                    const bf16x4 q = lds_col4(s_b, BS, r_hi, st * 16, lane);
+                    bf[m].v = __builtin_shufflevector(a, q, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+                const f32x4 w_lo = *(const f32x4*)(bw + r_lo);
+                const f32x4 w_hi = *(const f32x4*)(bw + r_hi);
+                const bf16x4 a = lds_col4(bx, XS, r_lo, pt * 16, lane);
+                const bf16x4 q = lds_col4(bx, XS, r_hi, pt * 16, lane);
+                Frag<bf16> hi, lo;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float x0 = to_f32(a[v]) * w_lo[v], x1 = to_f32(q[v]) * w_hi[v];
+                    hi.v[v] = from_f32<bf16>(x0);
+                    hi.v[v + 4] = from_f32<bf16>(x1);
+                    lo.v[v] = from_f32<bf16>(x0 - to_f32(hi.v[v]));
+                    lo.v[v + 4] = from_f32<bf16>(x1 - to_f32(hi.v[v + 4]));
+                }
+#pragma unroll
+                for (int m = 0; m < MST; ++m) {
+                    mma(acc[hh][m], bf[m], hi);
+                    mma(acc[hh][m], bf[m], lo);
+                }
+            }
+
+            if (hh + 1 < NH) {
+                store_head(h + 1, kb ^ 1);  // the other buffer is free
+                __syncthreads();
+            } else if (more) {
+                __syncthreads();  // every wave is done with this chunk's B rows
+                store_b();
+                store_head(h_first, kb ^ 1);
+                __syncthreads();
+            }
+            kb ^= 1;
+        }
+        rx = rx_next;
+    }
+
+    // ---- the segment's own end state and total decay ------------------------------------
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+        const int h = h_first + hh;
+        float* dst = seg_end + (((size_t)b * H + h) * nseg + seg) * (size_t)P * S;
+#pragma unroll
+        for (int m = 0; m < MST; ++m) {
+            const int s = (st0 + WPT * m) * 16 + 4 * g4;
+            *(f32x4*)(dst + (size_t)p * S + s) = acc[hh][m];
+        }
+        if (tid == 0) dec_seg[((size_t)b * H + h) * nseg + seg] = dacc[hh];
+    }
+}
+
+// Carry across segments: S_in(0) = end of segment 0 (which started from h0);
+// S_in(k+1) = 2^{D_k} S_in(k) + E_k; the state after the last segment is the final state.
+// S_in(k) for k >= 1 is stored in bf16 for the output kernel. One wave per 256 state
+// elements of one (batch, head), 4 per lane.
+__global__ __launch_bounds__(64) void seg_carry_kernel(const float* __restrict__ seg_end,
+                                                       const float* __restrict__ dec_seg,
+                                                       bf16* __restrict__ seg_in,
+                                                       float* __restrict__ fin, int nseg,
+                                                       int PS) {
+    const int per_bh = PS / 256;
+    const size_t bh = blockIdx.x / per_bh;
+    const int e = (blockIdx.x % per_bh) * 256 + threadIdx.x * 4;
+    const float* src = seg_end + bh * nseg * (size_t)PS + e;
+    bf16* dst = seg_in + bh * nseg * (size_t)PS + e;
+    f32x4 hv = *(const f32x4*)src;
+    for (int k = 1; k < nseg; ++k) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = from_f32<bf16>(hv[r]);
+        *(bf16x4*)(dst + (size_t)k * PS) = o;
+        hv = exp2_fast(dec_seg[bh * nseg + k]) * hv + *(const f32x4*)(src + (size_t)k * PS);
+    }
+    if (fin) *(f32x4*)(fin + bh * PS + e) = hv;
+}
+
+}  // namespace ssd

@@ -23,7 +23,7 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE"
 EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_bytes",
            "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
            "ssd_state_scan", "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
-           "ssd_backward")
+           "ssd_backward", "ssd_state_seg_workspace_bytes", "ssd_state_seg", "ssd_chunk_out_seg")
 
 
 class SSDError(RuntimeError):
@@ -70,6 +70,9 @@ def load_library():
     lib.ssd_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_backward_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
     lib.ssd_backward.argtypes = [sp] + [vp] * 17 + [sz, vp]
+    lib.ssd_state_seg_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
+    lib.ssd_state_seg.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_chunk_out_seg.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -166,6 +169,27 @@ def ssd_chunk_out(shape, x, B, C, G, dt_t, states, D, y, stream=None):
     _check(load_library().ssd_chunk_out(ctypes.byref(shape), _p(x), _p(B), _p(C), _p(G),
                                         _p(dt_t), _p(states), _p(D), _p(y), _stream(stream)),
            "ssd_chunk_out")
+
+
+def state_seg_workspace_bytes(shape: ssd_shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_state_seg_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)),
+           "ssd_state_seg_workspace_bytes")
+    return int(n.value)
+
+
+def ssd_state_seg(shape, x, A, B, G, dt_t, h0, states, final_state, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ssd_state_seg(ctypes.byref(shape), _p(x), _p(A), _p(B), _p(G), _p(dt_t),
+                                        _p(h0), _p(states), _p(final_state), _p(workspace),
+                                        nbytes, _stream(stream)), "ssd_state_seg")
+
+
+def ssd_chunk_out_seg(shape, x, B, C, G, dt_t, states, D, y, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().ssd_chunk_out_seg(ctypes.byref(shape), _p(x), _p(B), _p(C), _p(G),
+                                            _p(dt_t), _p(states), _p(D), _p(y), _p(workspace),
+                                            nbytes, _stream(stream)), "ssd_chunk_out_seg")
 
 
 def ssd_forward(shape, x, dt, A, B, C, D, h0, y, final_state, workspace, stream=None):

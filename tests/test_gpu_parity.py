@@ -223,9 +223,13 @@ def test_chunk_size_invariance(chunk, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_split_resume_is_exact(dtype):
-    """Forward over [0, L) equals forward over [0, L1) then [L1, L) from the returned
-    final state, bit for bit, when L1 is a chunk boundary."""
+def test_split_resume(dtype):
+    """Forward over [0, L) against forward over [0, L1) then [L1, L) from the returned
+    final state, L1 a chunk boundary. fp32 inputs (the two-kernel state pass): bit for
+    bit. bf16 inputs take the segmented state pass, whose one-pass run forms the later
+    chunk states as (state from the segment's start) + (decayed state entering it) while
+    the resumed run starts from the fp32 h0, so the rounding differs: both runs within the
+    parity bound of the oracle and of each other."""
     w = gen.Workload("split", 2, 1024, 4, 64, 128, 1, 256, dtype, True, 7)
     cpu, d = make(w)
     y, fin = gpu_forward(w, d)
@@ -235,8 +239,17 @@ def test_split_resume_is_exact(dtype):
     y1, f1 = gpu_forward(w, d1)
     d2["h0"] = f1
     y2, f2 = gpu_forward(w, d2)
-    assert torch.equal(torch.cat([y1, y2], dim=1), y)
-    assert torch.equal(f2, fin)
+    ys = torch.cat([y1, y2], dim=1)
+    if dtype == "fp32":
+        assert torch.equal(ys, y)
+        assert torch.equal(f2, fin)
+        return
+    ref = oracle_forward(cpu)
+    for got in (ys, y):
+        assert max_rel_rms(got, ref["y"]) <= TOL[dtype]
+    for got in (f2, fin):
+        assert max_rel_rms(got, ref["final"]) <= TOL[dtype]
+    assert max_rel_rms(ys, y) <= TOL[dtype] and max_rel_rms(f2, fin) <= TOL[dtype]
 
 
 def test_run_to_run_bitwise_deterministic():

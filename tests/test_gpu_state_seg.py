@@ -1,0 +1,151 @@
+"""The segmented state pass (ssd_state_seg + ssd_chunk_out_seg, which ssd_forward takes
+for bf16 inputs with bf16 states at headdim 64, dstate 64 or 128) against the fp64 oracle
+on the GPU.
+
+The shapes are chosen so that the library's segment plan differs between them: 1 to 6
+heads per workgroup, 2 to 8 chunks per segment, a short last segment, a partial last
+chunk, a single partial chunk, groups, with and without h0. Every element of y and of the
+final state is compared."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import SSM_RMS_TOL, TOL, make, needs_gpu, oracle_forward
+from metrics import max_rel_rms, rms_rel
+from state_space_sequence_chunk_amd import inputs as gen
+from state_space_sequence_chunk_amd import ssd
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _w(name, batch, seqlen, nheads, ngroups, dstate, chunk, h0, seed):
+    return gen.Workload(name, batch, seqlen, nheads, 64, dstate, ngroups, chunk, "bf16", h0, seed)
+
+
+# (plan the library picks for the shape: heads per workgroup x chunks per segment, segments)
+CASES = {
+    # 1 x 2, 8 segments; the last chunk holds 160 of 256 tokens
+    "ragged-1x2": _w("ragged-1x2", 1, 4000, 10, 1, 128, 256, True, 11),
+    # 1 x 3, 8 segments; chunk 128, two groups, partial last chunk
+    "groups-1x3": _w("groups-1x3", 2, 3000, 12, 2, 128, 128, True, 12),
+    # 2 x 2, 64 segments; chunk 64
+    "t64-2x2": _w("t64-2x2", 1, 8192, 8, 1, 128, 64, False, 13),
+    # 3 x 3, 7 segments, the last of 2 chunks; dstate 64; partial last chunk
+    "short-seg-3x3": _w("short-seg-3x3", 3, 5000, 36, 1, 64, 256, False, 14),
+    # 4 x 4, 8 segments
+    "nh4-4x4": _w("nh4-4x4", 4, 8192, 32, 1, 128, 256, False, 15),
+    # 5 x 8, 4 segments; dstate 64, chunk 128
+    "nh5-5x8": _w("nh5-5x8", 8, 4096, 40, 1, 64, 128, True, 16),
+    # 6 x 8, 2 segments; four groups
+    "nh6-6x8": _w("nh6-6x8", 16, 2048, 48, 4, 128, 128, True, 17),
+    # one partial chunk: one segment
+    "one-chunk": _w("one-chunk", 1, 200, 4, 1, 128, 256, True, 18),
+}
+
+
+def _print(msg):
+    print(msg, flush=True)
+
+
+def _forward(w, d, D="given"):
+    Dv = d["D"] if D == "given" else D
+    y, fin = ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], Dv, d["h0"], chunk=w.chunk)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_segmented_all_elements(name):
+    w = CASES[name]
+    cpu, d = make(w)
+    _print(f"{name}: {w}")
+    y, fin = _forward(w, d)
+    ref = oracle_forward(cpu)
+    ey, ef = max_rel_rms(y, ref["y"]), max_rel_rms(fin, ref["final"])
+    _print(f"{name}: y max/rms {ey:.2e}  final max/rms {ef:.2e}")
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["ragged-1x2", "short-seg-3x3", "nh6-6x8"])
+def test_forward_segmented_ssm_only(name):
+    """D = 0: the state path alone, where the skip term cannot hide an error."""
+    w = CASES[name]
+    cpu, d = make(w, zero_D=True)
+    _print(f"{name}: SSM only")
+    y, fin = _forward(w, d)
+    ref = oracle_forward(cpu)
+    e = rms_rel(y, ref["y"])
+    _print(f"{name}: SSM-only y rms-rel {e:.2e}")
+    assert e <= SSM_RMS_TOL["bf16"]
+
+
+def test_staged_segmented_equals_forward():
+    """cumsum -> ssd_state_seg -> ssd_chunk_out_seg gives ssd_forward's y and final state
+    bit for bit (the same kernels in the same order)."""
+    w = CASES["nh5-5x8"]
+    cpu, d = make(w)
+    y1, f1 = _forward(w, d)
+    sh = ssd.shape_of(d["x"], d["B"], w.chunk)
+    b, L, H, P = d["x"].shape
+    S = d["B"].shape[3]
+    nC = -(-L // w.chunk)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    G = torch.empty((b, H, L), **f32)
+    dtt = torch.empty((b, H, L), **f32)
+    st = torch.empty((b, H, nC, P, S), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((b, H, P, S), **f32)
+    y = torch.empty((b, L, H, P), **f32)
+    ws = torch.empty(ssd.state_seg_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dtt)
+    ssd.ssd_state_seg(sh, d["x"], d["A"], d["B"], G, dtt, d["h0"], st, fin, ws)
+    ssd.ssd_chunk_out_seg(sh, d["x"], d["B"], d["C"], G, dtt, st, d["D"], y, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1) and torch.equal(fin, f1)
+
+
+def _within_bf16_rounding(got, ref):
+    """Every element within bf16's round-to-nearest bound (half an ulp: 2^-8 of the value)
+    plus 1e-4 of the rms for the fp32 arithmetic before the rounding; returns the worst
+    ratio of error to that bound."""
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-4 * np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(got - ref) / bound))
+
+
+def test_segmented_recorded_states_are_segment_relative():
+    """ssd_state_seg's recorded states: the true chunk-initial state minus the part
+    carried in from before the segment. In the first segment (which starts from h0) they
+    are the true states; at the first chunk of every later segment they are zero."""
+    w = CASES["ragged-1x2"]  # two chunks per segment
+    cpu, d = make(w)
+    sh = ssd.shape_of(d["x"], d["B"], w.chunk)
+    b, L, H, P = d["x"].shape
+    S = d["B"].shape[3]
+    nC = -(-L // w.chunk)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    G = torch.empty((b, H, L), **f32)
+    dtt = torch.empty((b, H, L), **f32)
+    st = torch.empty((b, H, nC, P, S), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ssd.state_seg_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dtt)
+    ssd.ssd_state_seg(sh, d["x"], d["A"], d["B"], G, dtt, d["h0"], st, None, ws)
+    torch.cuda.synchronize()
+    ref = oracle_forward(cpu, emit_every=w.chunk)
+    true = ref["states"]  # [b, H, nC, P, S] fp64: the state entering each chunk
+    got = st.double().cpu().numpy()
+    # chunks 0 and 1 form segment 0 (h0 included): the true states, to bf16 rounding
+    r = _within_bf16_rounding(got[:, :, :2], true[:, :, :2])
+    _print(f"segment 0 states: worst error / bf16 rounding bound {r:.3f}")
+    assert r <= 1.0
+    # the first chunk of each later segment records the zero state
+    assert np.all(got[:, :, 2::2] == 0.0)
+    # the second chunk of a segment records that segment's first chunk's own increment:
+    # true S_{c+1} - 2^{g_c} S_c, with g_c the chunk's total log2 decay
+    A = cpu["A"].double().numpy()
+    dtv = cpu["dt"].double().numpy()  # [b, L, H]
+    T = w.chunk
+    for c in range(2, nC - 1, 2):
+        a = np.exp(A[None, :] * dtv[:, c * T:(c + 1) * T, :].sum(axis=1))  # [b, H]
+        inc = true[:, :, c + 1] - a[:, :, None, None] * true[:, :, c]
+        r = _within_bf16_rounding(got[:, :, c + 1], inc)
+        _print(f"chunk {c + 1}: worst error / bf16 rounding bound {r:.3f}")
+        assert r <= 1.0, (c, r)
