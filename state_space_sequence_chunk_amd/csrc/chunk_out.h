@@ -294,7 +294,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     load_head(h_first);  // in flight while the tiles are built
     if constexpr (Cfg::SHARED) {
         // build this wave's interaction tiles once for all heads of the workgroup
-        if constexpr (Cfg::B_IN_LDS) __syncthreads();
+        if constexpr (Cfg::B_IN_LDS) lds_barrier();
         const int itmax = its[1];
         for (int jt = 0; jt <= itmax; ++jt) {
             f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -319,10 +319,10 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) z[r] = from_f32<TIn>(0.f);
         }
-        __syncthreads();  // tiles written; the B rows (if staged) may now be overwritten
+        lds_barrier();  // tiles written; the B rows (if staged) may now be overwritten
     }
     store_head();
-    __syncthreads();
+    lds_barrier();
 
     // y offsets (bytes) of this lane's 8 rows within the chunk, for column l16 of head 0
     uint32_t yoff[2][4];
@@ -495,10 +495,10 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
                             yoff[q][r] + pt * 16 * (uint32_t)sizeof(TY), yh);
             }
 
-        __syncthreads();  // every wave is done with this head's LDS copies
+        lds_barrier();  // every wave is done with this head's LDS copies
         if (hh + 1 < NH) {
             store_head();
-            __syncthreads();
+            lds_barrier();
         }
     }
 }

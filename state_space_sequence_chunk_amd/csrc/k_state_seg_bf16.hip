@@ -74,8 +74,8 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 }  // namespace
 
-// Plan: heads per workgroup (a divisor of the heads per group, at most 96 state
-// registers per lane) and chunks per segment (at least 2 unless the sequence has one
+// Plan: heads per workgroup (a divisor of the heads per group whose running states fit
+// in registers) and chunks per segment (at least 2 unless the sequence has one
 // chunk). A workgroup holds one compute unit (its LDS plan takes most of the 160 KB), so
 // the grid runs in rounds of 256; the cost of a plan is its rounds times one workgroup's
 // work, counted in (chunk, head) steps plus a fixed share per workgroup, per chunk (B rows,
@@ -91,7 +91,9 @@ bool state_seg_plan(int in_dtype, int states_dtype, const Dims& d, SegPlan* out)
     double best = 1e300;
     SegPlan bp{0, 0, 0};
     for (int nh : kSegHeads) {
-        if (hpg % nh != 0 || nh * regs_per_head > 96) continue;
+        // register budget of the two-step prefetch: at most 80 state registers per lane,
+        // and eight heads only with chunks shorter than 256 tokens (no spills)
+        if (hpg % nh != 0 || nh * regs_per_head > 80 || (nh == 8 && d.chunk == 256)) continue;
         for (int k = (nC == 1 ? 1 : 2); k <= nC; ++k) {
             const int nseg = (nC + k - 1) / k;
             const long wgs = (long)d.batch * nseg * (d.nheads / nh);

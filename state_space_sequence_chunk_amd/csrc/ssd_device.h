@@ -132,6 +132,15 @@ __device__ __forceinline__ float buf_load_f32(BufRsrc r, uint32_t voff, uint32_t
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// Workgroup barrier that orders LDS only: this wave's global loads and stores in flight
+// stay in flight (__syncthreads' workgroup-scope release fence would first wait for all
+// of them to complete). For barriers that only hand over data staged in LDS.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Map a linear workgroup id so that consecutive logical ids run on the same XCD:
 // hardware hands workgroups to the 8 XCDs round-robin, so logical id
 // (xcd * per_xcd + k) is given to hardware id (k * 8 + xcd). Consecutive logical ids

@@ -102,14 +102,6 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds) {
         : "memory");
 }
 
-// Workgroup barrier that orders LDS only: global loads and stores in flight stay in
-// flight (a full __syncthreads would wait for all of them).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <typename TIn, typename TS, int P, int S, int T, int PT, int TB, int R>
 struct ScanCfg {
     static constexpr int NTHR = 512, NWAVE = 8;

@@ -32,6 +32,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -39,6 +40,18 @@
 namespace ssd {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int V> using IntC = std::integral_constant<int, V>;
+
+// f(IntC<I>{}) for I = B .. E-1, unrolled at compile time.
+template <int B, int E> struct StaticFor {
+    template <class F> __device__ __forceinline__ static void run(F&& f) {
+        if constexpr (B < E) {
+            f(IntC<B>{});
+            StaticFor<B + 1, E>::run(f);
+        }
+    }
+};
 
 template <int P, int S, int T>
 struct SegCfg {
@@ -101,6 +114,7 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
 
     const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
     const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
+    const BufRsrc rdec = make_rsrc(dec_in + (size_t)b * H * nC, (uint32_t)((size_t)H * nC * sizeof(float)));
     auto rows_of = [&](int c) { return min(T, L - c * T); };
     // x rows past a chunk's real tokens lie outside its descriptor and load as zeros
     auto x_rsrc = [&](int c) {
@@ -108,29 +122,37 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
                          (uint32_t)(rows_of(c) * HP * sizeof(bf16)));
     };
 
-    // ---- staging: global -> registers (prefetch) -> LDS ---------------------------------
-    Vec16 px[Cfg::NXV], pb[Cfg::NBV];
-    float pdt[PER];
-    float gl_next = 0.f;  // the prefetched step's chunk decay g (log2), G at its last real token
-    auto load_head = [&](int c, int h, BufRsrc rx) {
+    // ---- staging: global -> registers (prefetch, two steps deep) -> LDS -----------------
+    // A step is one (chunk, head) of the segment, in order. Step j's x rows, dt and chunk
+    // decay are loaded into register set j % 2 at the start of step j-2 and moved to LDS
+    // buffer j % 2 (wave 0 turning dt into the weights) at the start of step j-1, after
+    // that step's own loads are issued; so the staging overlaps the products and the end
+    // of a step is a single barrier. The next chunk's B rows are loaded during a chunk's
+    // last head and replace the current ones between two barriers at its end.
+    Vec16 px[2][Cfg::NXV], pb[Cfg::NBV];
+    float pdt[2][PER];
+    float gls[2] = {0.f, 0.f};  // each set's chunk decay g (log2): G at the chunk's last real token
+    auto load_head = [&](auto set_c, int c, int h) {
+        constexpr int q = decltype(set_c)::value;
         const int rows = rows_of(c);
+        const BufRsrc rx = x_rsrc(c);
 #pragma unroll
         for (int i = 0; i < Cfg::NXV; ++i) {
             const int v = tid + i * NTHR;
             if (v < T * P / VE) {
                 const int r = v / (P / VE), col = (v % (P / VE)) * VE;
-                px[i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(bf16)),
-                                   (uint32_t)(h * P * sizeof(bf16)));
+                px[q][i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(bf16)),
+                                      (uint32_t)(h * P * sizeof(bf16)));
             }
         }
         const uint32_t o = (uint32_t)(((size_t)h * L + (size_t)c * T) * sizeof(float));
-        gl_next = buf_load_f32(rg, (uint32_t)((rows - 1) * 4), o);
-        if (wave == 0) {  // wave 0 scans the head's decay; lane holds tokens T-1-(PER*lane+k)
+        gls[q] = buf_load_f32(rg, (uint32_t)((rows - 1) * 4), o);
+        // dt for wave 0's scan (lane holds tokens T-1-(PER*lane+k)); every wave issues the
+        // same loads so that all waves count the same memory operations per step
 #pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int t = T - 1 - (PER * lane + k);
-                pdt[k] = t < rows ? buf_load_f32(rdt, t * 4, o) : 0.f;
-            }
+        for (int k = 0; k < PER; ++k) {
+            const int t = T - 1 - (PER * lane + k);
+            pdt[q][k] = buf_load_f32(rdt, (uint32_t)(t < rows ? t * 4 : 0x80000000u), o);
         }
     };
     // B rows of chunk c through a descriptor over its real rows (padded rows read zeros)
@@ -157,14 +179,16 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
             }
         }
     };
-    auto store_head = [&](int h, int kb) {
-        bf16* bx = s_x(kb);
+    // register set q -> LDS buffer q (x rows; wave 0 turns dt into the weights)
+    auto store_head = [&](auto set_c, int h) {
+        constexpr int q = decltype(set_c)::value;
+        bf16* bx = s_x(q);
 #pragma unroll
         for (int i = 0; i < Cfg::NXV; ++i) {
             const int v = tid + i * NTHR;
             if (v < T * P / VE) {
                 const int r = v / (P / VE), col = (v % (P / VE)) * VE;
-                *(Vec16*)(bx + r * XS + col) = px[i];
+                *(Vec16*)(bx + r * XS + col) = px[q][i];
             }
         }
         if (wave == 0) {
@@ -174,13 +198,13 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
 #pragma unroll
             for (int k = 0; k < PER; ++k) {
                 pre[k] = run;
-                run += ah * pdt[k];
+                run += ah * pdt[q][k];
             }
             const float excl = wave_shift_up1(wave_inclusive_scan(run));
-            float* bw = s_w(kb);
+            float* bw = s_w(q);
 #pragma unroll
             for (int k = 0; k < PER; ++k)
-                bw[T - 1 - (PER * lane + k)] = pdt[k] * exp2_fast((excl + pre[k]) * kLog2e);
+                bw[T - 1 - (PER * lane + k)] = pdt[q][k] * exp2_fast((excl + pre[k]) * kLog2e);
         }
     };
 
@@ -201,94 +225,113 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
         }
     }
 
-    // ---- prologue: the first chunk's B rows and first head ------------------------------
-    BufRsrc rx = x_rsrc(c_first);
-    load_head(c_first, h_first, rx);
-    load_b(c_first);
-    store_b();
-    store_head(h_first, 0);
-    __syncthreads();
-
-    int kb = 0;  // buffer of the current step
-    for (int ci = 0; ci < nck; ++ci) {
-        const int c = c_first + ci;
+    // ---- one step: head hh of chunk ci of the segment, register set / LDS buffer q ------
+    auto step = [&](auto hh_c, auto q_c, int ci) {
+        constexpr int hh = decltype(hh_c)::value, q = decltype(q_c)::value;
+        constexpr int h2 = (hh + 2) % NH, dc2 = (hh + 2) / NH;  // the step two ahead
+        const int c = c_first + ci, h = h_first + hh;
         const bool more = ci + 1 < nck;
-        const BufRsrc rx_next = more ? x_rsrc(c + 1) : rx;
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-            const int h = h_first + hh;
-            const float gl = gl_next;  // this step's chunk decay
-            // the next step's loads are in flight while this step's products run
-            if (hh + 1 < NH) {
-                load_head(c, h + 1, rx);
-            } else if (more) {
-                load_head(c + 1, h_first, rx_next);
-                load_b(c + 1);
-            }
+        const float gl = gls[q];  // this step's chunk decay, before set q is reloaded
+        // Every step issues the same memory operations (past the segment's end they repeat
+        // its last chunk and are never used), so the compiler's wait before each use counts
+        // exactly the operations issued since, and the loads two steps ahead stay in flight.
+        load_head(q_c, min(c + dc2, c_first + nck - 1), h_first + h2);
+        if constexpr (hh == NH - 1) load_b(more ? c + 1 : c);
+        // stage the next step now (its loads were issued a step ago): LDS buffer q^1 was
+        // last read by the previous step, which ended at a barrier; the next step reads
+        // it after this step's barrier. Past the segment's end the copy is never read.
+        constexpr IntC<q ^ 1> q1{};
+        store_head(q1, hh + 1 < NH ? h + 1 : h_first);
 
-            // record the state entering chunk c (from the segment's start), then advance it
-            const BufRsrc rst = make_rsrc(states + (((size_t)b * H + h) * nC + c) * (size_t)P * S,
-                                          (uint32_t)(P * S * sizeof(bf16)));
+        // record the state entering chunk c (from the segment's start), then advance it
+        const BufRsrc rst = make_rsrc(states + (((size_t)b * H + h) * nC + c) * (size_t)P * S,
+                                      (uint32_t)(P * S * sizeof(bf16)));
+#pragma unroll
+        for (int m = 0; m < MST; ++m) {
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = from_f32<bf16>(acc[hh][m][r]);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), rst, st_off,
+                                                  (uint32_t)(WPT * m * 16 * sizeof(bf16)), 0);
+        }
+        // dec_in[b, h, c] from thread 0; the other lanes' offsets are out of range (dropped)
+        buf_store_f32(dacc[hh], rdec, tid == 0 ? (uint32_t)(((size_t)h * nC + c) * 4) : 0x80000000u,
+                      0u);
+        dacc[hh] += gl;
+        const float dec = exp2_fast(gl);
+#pragma unroll
+        for (int m = 0; m < MST; ++m) acc[hh][m] *= dec;
+
+        const bf16* bx = s_x(q);
+        const float* bw = s_w(q);
+        // slot (g4, v) carries token 32 ks + 16 (v/4) + 4 g4 + v%4 (two column reads)
+#pragma unroll 2
+        for (int ks = 0; ks < T / 32; ++ks) {
+            const int r_lo = ks * 32 + 4 * g4, r_hi = r_lo + 16;
+            Frag<bf16> bf[MST];
 #pragma unroll
             for (int m = 0; m < MST; ++m) {
-                bf16x4 o;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = from_f32<bf16>(acc[hh][m][r]);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), rst, st_off,
-                                                      (uint32_t)(WPT * m * 16 * sizeof(bf16)), 0);
+                const int st = st0 + WPT * m;
+                const bf16x4 a = lds_col4(s_b, BS, r_lo, st * 16, lane);
+                const bf16x4 q4 = lds_col4(s_b, BS, r_hi, st * 16, lane);
+                bf[m].v = __builtin_shufflevector(a, q4, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            if (tid == 0) dec_in[((size_t)b * H + h) * nC + c] = dacc[hh];
-            dacc[hh] += gl;
-            const float dec = exp2_fast(gl);
+            const f32x4 w_lo = *(const f32x4*)(bw + r_lo);
+            const f32x4 w_hi = *(const f32x4*)(bw + r_hi);
+            const bf16x4 a = lds_col4(bx, XS, r_lo, pt * 16, lane);
+            const bf16x4 q4 = lds_col4(bx, XS, r_hi, pt * 16, lane);
+            Frag<bf16> hi, lo;
 #pragma unroll
-            for (int m = 0; m < MST; ++m) acc[hh][m] *= dec;
-
-            const bf16* bx = s_x(kb);
-            const float* bw = s_w(kb);
-            // slot (g4, v) carries token 32 ks + 16 (v/4) + 4 g4 + v%4 (two column reads)
-#pragma unroll 1
-            for (int ks = 0; ks < T / 32; ++ks) {
-                const int r_lo = ks * 32 + 4 * g4, r_hi = r_lo + 16;
-                Frag<bf16> bf[MST];
-#pragma unroll
-                for (int m = 0; m < MST; ++m) {
-                    const int st = st0 + WPT * m;
-                    const bf16x4 a = lds_col4(s_b, BS, r_lo, st * 16, lane);
-                    const bf16x4 q = lds_col4(s_b, BS, r_hi, st * 16, lane);
-                    bf[m].v = __builtin_shufflevector(a, q, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-                const f32x4 w_lo = *(const f32x4*)(bw + r_lo);
-                const f32x4 w_hi = *(const f32x4*)(bw + r_hi);
-                const bf16x4 a = lds_col4(bx, XS, r_lo, pt * 16, lane);
-                const bf16x4 q = lds_col4(bx, XS, r_hi, pt * 16, lane);
-                Frag<bf16> hi, lo;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float x0 = to_f32(a[v]) * w_lo[v], x1 = to_f32(q[v]) * w_hi[v];
-                    hi.v[v] = from_f32<bf16>(x0);
-                    hi.v[v + 4] = from_f32<bf16>(x1);
-                    lo.v[v] = from_f32<bf16>(x0 - to_f32(hi.v[v]));
-                    lo.v[v + 4] = from_f32<bf16>(x1 - to_f32(hi.v[v + 4]));
-                }
-#pragma unroll
-                for (int m = 0; m < MST; ++m) {
-                    mma(acc[hh][m], bf[m], hi);
-                    mma(acc[hh][m], bf[m], lo);
-                }
+            for (int v = 0; v < 4; ++v) {
+                const float x0 = to_f32(a[v]) * w_lo[v], x1 = to_f32(q4[v]) * w_hi[v];
+                hi.v[v] = from_f32<bf16>(x0);
+                hi.v[v + 4] = from_f32<bf16>(x1);
+                lo.v[v] = from_f32<bf16>(x0 - to_f32(hi.v[v]));
+                lo.v[v + 4] = from_f32<bf16>(x1 - to_f32(hi.v[v + 4]));
             }
-
-            if (hh + 1 < NH) {
-                store_head(h + 1, kb ^ 1);  // the other buffer is free
-                __syncthreads();
-            } else if (more) {
-                __syncthreads();  // every wave is done with this chunk's B rows
-                store_b();
-                store_head(h_first, kb ^ 1);
-                __syncthreads();
+#pragma unroll
+            for (int m = 0; m < MST; ++m) {
+                mma(acc[hh][m], bf[m], hi);
+                mma(acc[hh][m], bf[m], lo);
             }
-            kb ^= 1;
         }
-        rx = rx_next;
+
+        // hand over to the next step (at a chunk's end, after the B rows are replaced)
+        if constexpr (hh + 1 < NH) {
+            lds_barrier();
+        } else {
+            if (more) {
+                lds_barrier();  // every wave is done with this chunk's B rows
+                store_b();
+                lds_barrier();
+            }
+        }
+    };
+
+    // ---- prologue: the first chunk's B rows, steps 0 and 1 loaded, step 0 in LDS --------
+    load_head(IntC<0>{}, c_first, h_first);
+    load_head(IntC<1>{}, min(c_first + 1 / NH, c_first + nck - 1), h_first + 1 % NH);
+    load_b(c_first);
+    store_b();
+    store_head(IntC<0>{}, h_first);
+    lds_barrier();
+
+    // ---- main loop: each step's set known at compile time (one chunk per pass when NH is
+    // even, two when it is odd) --------------------------------------------------------
+    constexpr int CPP = NH % 2 == 0 ? 1 : 2;  // chunks per pass
+    for (int ci = 0; ci < nck; ci += CPP) {
+        StaticFor<0, NH>::run([&](auto hh_c) {
+            constexpr int hh = decltype(hh_c)::value;
+            step(hh_c, IntC<(hh & 1)>{}, ci);
+        });
+        if constexpr (CPP == 2) {
+            if (ci + 1 < nck) {
+                StaticFor<0, NH>::run([&](auto hh_c) {
+                    constexpr int hh = decltype(hh_c)::value;
+                    step(hh_c, IntC<((NH + hh) & 1)>{}, ci + 1);
+                });
+            }
+        }
     }
 
     // ---- the segment's own end state and total decay ------------------------------------

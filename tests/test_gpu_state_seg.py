@@ -2,8 +2,8 @@
 for bf16 inputs with bf16 states at headdim 64, dstate 64 or 128) against the fp64 oracle
 on the GPU.
 
-The shapes are chosen so that the library's segment plan differs between them: 1 to 6
-heads per workgroup, 2 to 8 chunks per segment, a short last segment, a partial last
+The shapes are chosen so that the library's segment plan differs between them: 1 to 8
+heads per workgroup, 2 to 16 chunks per segment, a short last segment, a partial last
 chunk, a single partial chunk, groups, with and without h0. Every element of y and of the
 final state is compared."""
 import numpy as np
@@ -36,8 +36,12 @@ CASES = {
     "nh4-4x4": _w("nh4-4x4", 4, 8192, 32, 1, 128, 256, False, 15),
     # 5 x 8, 4 segments; dstate 64, chunk 128
     "nh5-5x8": _w("nh5-5x8", 8, 4096, 40, 1, 64, 128, True, 16),
-    # 6 x 8, 2 segments; four groups
-    "nh6-6x8": _w("nh6-6x8", 16, 2048, 48, 4, 128, 128, True, 17),
+    # 6 x 8, 8 segments; four groups, dstate 64, chunk 64
+    "nh6-6x8": _w("nh6-6x8", 4, 4096, 48, 4, 64, 64, True, 17),
+    # 8 x 8, 8 segments; dstate 64, chunk 64
+    "nh8-8x8": _w("nh8-8x8", 2, 4096, 128, 1, 64, 64, False, 19),
+    # 3 x 16, one segment; four groups
+    "one-seg-3x16": _w("one-seg-3x16", 16, 2048, 48, 4, 128, 128, True, 20),
     # one partial chunk: one segment
     "one-chunk": _w("one-chunk", 1, 200, 4, 1, 128, 256, True, 18),
 }
