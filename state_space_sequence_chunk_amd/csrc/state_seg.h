@@ -105,12 +105,20 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
     const int HP = H * P;
     const size_t grow = (size_t)ngroups * S;
     const int pt = wave / WPT;   // this wave's p-tile
-    const int st0 = wave % WPT;  // first s-tile; stride WPT
+    // this wave's s-tiles: MST adjacent ones, so that each 128-byte piece of a recorded
+    // state row comes from one wave's back-to-back stores (whole lines reach L2 together,
+    // never two waves' halves of one line)
+    const int st0 = (wave % WPT) * MST;
     const int c_first = seg * K;
     const int nck = min(K, nC - c_first);  // chunks of this segment
     const int p = pt * 16 + l16;           // this lane's state row (accumulator column)
-    // byte offset of this lane's four state columns of its first s-tile in a P x S block
-    const uint32_t st_off = (uint32_t)((p * S + st0 * 16 + 4 * g4) * sizeof(bf16));
+    // byte offset of this lane's 8 recorded columns for the first tile pair (see the record
+    // step: even slot groups take columns 16 st0 + 4 g4 .., odd ones 16 (st0+1) + 4 (g4-1) ..)
+    const bool odd_g4 = (g4 & 1) != 0;
+    const uint32_t st_off =
+        (uint32_t)((p * S + (odd_g4 ? (st0 + 1) * 16 + 4 * (g4 - 1) : st0 * 16 + 4 * g4)) *
+                   sizeof(bf16));
+    static_assert(MST % 2 == 0, "recorded states are written as tile pairs");
 
     const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
     const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
         dacc[hh] = 0.f;
 #pragma unroll
         for (int m = 0; m < MST; ++m) {
-            const int s = (st0 + WPT * m) * 16 + 4 * g4;
+            const int s = (st0 + m) * 16 + 4 * g4;
             if (seg == 0 && h0)
                 acc[hh][m] = *(const f32x4*)(h0 + (((size_t)b * H + h_first + hh) * P + p) * S + s);
             else
@@ -243,16 +251,30 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
         constexpr IntC<q ^ 1> q1{};
         store_head(q1, hh + 1 < NH ? h + 1 : h_first);
 
-        // record the state entering chunk c (from the segment's start), then advance it
+        // record the state entering chunk c (from the segment's start), then advance it.
+        // For each pair of adjacent tiles (m, m+1) the lanes 16 apart (slot groups 2k and
+        // 2k+1) swap one tile's four values, so that the even lane holds columns
+        // 16(st0+m) + 4 g4 .. +7 and the odd one 16(st0+m+1) + 4(g4-1) .. +7: one 16-byte
+        // store per lane writes 64 contiguous bytes of each of the 16 rows.
         const BufRsrc rst = make_rsrc(states + (((size_t)b * H + h) * nC + c) * (size_t)P * S,
                                       (uint32_t)(P * S * sizeof(bf16)));
 #pragma unroll
-        for (int m = 0; m < MST; ++m) {
-            bf16x4 o;
+        for (int m = 0; m < MST; m += 2) {
+            bf16x4 o0, o1;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = from_f32<bf16>(acc[hh][m][r]);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), rst, st_off,
-                                                  (uint32_t)(WPT * m * 16 * sizeof(bf16)), 0);
+            for (int r = 0; r < 4; ++r) {
+                o0[r] = from_f32<bf16>(acc[hh][m][r]);
+                o1[r] = from_f32<bf16>(acc[hh][m + 1][r]);
+            }
+            const u32x2 a = __builtin_bit_cast(u32x2, o0), a1 = __builtin_bit_cast(u32x2, o1);
+            const u32x2 send = odd_g4 ? a : a1;
+            u32x2 recv;
+            recv[0] = (uint32_t)__shfl_xor((int)send[0], 16);
+            recv[1] = (uint32_t)__shfl_xor((int)send[1], 16);
+            const u32x2 first = odd_g4 ? recv : a, second = odd_g4 ? a1 : recv;
+            const Vec16 out = Vec16{first[0], first[1], second[0], second[1]};
+            __builtin_amdgcn_raw_buffer_store_b128(out, rst, st_off,
+                                                   (uint32_t)(m * 16 * sizeof(bf16)), 0);
         }
         // dec_in[b, h, c] from thread 0; the other lanes' offsets are out of range (dropped)
         buf_store_f32(dacc[hh], rdec, tid == 0 ? (uint32_t)(((size_t)h * nC + c) * 4) : 0x80000000u,
@@ -271,7 +293,7 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
             Frag<bf16> bf[MST];
 #pragma unroll
             for (int m = 0; m < MST; ++m) {
-                const int st = st0 + WPT * m;
+                const int st = st0 + m;
                 const bf16x4 a = lds_col4(s_b, BS, r_lo, st * 16, lane);
                 const bf16x4 q4 = lds_col4(s_b, BS, r_hi, st * 16, lane);
                 bf[m].v = __builtin_shufflevector(a, q4, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -341,7 +363,7 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
         float* dst = seg_end + (((size_t)b * H + h) * nseg + seg) * (size_t)P * S;
 #pragma unroll
         for (int m = 0; m < MST; ++m) {
-            const int s = (st0 + WPT * m) * 16 + 4 * g4;
+            const int s = (st0 + m) * 16 + 4 * g4;
             *(f32x4*)(dst + (size_t)p * S + s) = acc[hh][m];
         }
         if (tid == 0) dec_seg[((size_t)b * H + h) * nseg + seg] = dacc[hh];
