@@ -582,7 +582,7 @@ hipError_t out_by_p(const void* x, const void* Bm, const void* Cm, const float* 
 }
 
 // Segment-relative chunk states (bf16 inputs and states), for the shapes the segmented
-// state pass is built for (headdim 64, dstate 64 or 128).
+// state pass is built for (headdim 64, dstate 64, 128 or 256).
 template <typename TY>
 hipError_t out_seg(const void* x, const void* Bm, const void* Cm, const float* G,
                    const float* dt_t, const void* st, const void* seg_in, const float* dec_in,
@@ -593,6 +593,7 @@ hipError_t out_seg(const void* x, const void* Bm, const void* Cm, const float* G
                                                        seg_in, dec_in, seg_chunks);
     SSD_OUT_SEG(64, 64, 64) SSD_OUT_SEG(64, 64, 128) SSD_OUT_SEG(64, 64, 256)
     SSD_OUT_SEG(64, 128, 64) SSD_OUT_SEG(64, 128, 128) SSD_OUT_SEG(64, 128, 256)
+    SSD_OUT_SEG(64, 256, 64) SSD_OUT_SEG(64, 256, 128) SSD_OUT_SEG(64, 256, 256)
 #undef SSD_OUT_SEG
     return hipErrorInvalidValue;
 }

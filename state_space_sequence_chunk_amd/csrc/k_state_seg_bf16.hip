@@ -8,12 +8,18 @@ namespace {
 
 constexpr int kSegHeads[] = {1, 2, 3, 4, 5, 6, 8};  // instantiated heads per workgroup
 
+// Tokens per step: the whole chunk, or 128-token sub-blocks where the chunk's B rows
+// (dstate 256) would not fit in LDS next to the x buffers.
+template <int S, int T> constexpr int seg_tb() { return S >= 256 && T > 128 ? 128 : T; }
+template <int P, int S, int T> using SegCfgFor = SegCfg<P, S, T, seg_tb<S, T>()>;
+
 bool seg_shape_fits(int P, int S, int T) {
     switch (P * 1000000 + S * 1000 + T) {
 #define SSD_SEG_FITS(p, s, t) \
-    case p * 1000000 + s * 1000 + t: return SegCfg<p, s, t>::FITS;
+    case p * 1000000 + s * 1000 + t: return SegCfgFor<p, s, t>::FITS;
         SSD_SEG_FITS(64, 64, 64) SSD_SEG_FITS(64, 64, 128) SSD_SEG_FITS(64, 64, 256)
         SSD_SEG_FITS(64, 128, 64) SSD_SEG_FITS(64, 128, 128) SSD_SEG_FITS(64, 128, 256)
+        SSD_SEG_FITS(64, 256, 64) SSD_SEG_FITS(64, 256, 128) SSD_SEG_FITS(64, 256, 256)
 #undef SSD_SEG_FITS
     }
     return false;
@@ -23,8 +29,8 @@ template <int P, int S, int T, int NH>
 hipError_t run_seg(const void* x, const void* Bm, const float* A, const float* G,
                    const float* dt_t, const float* h0, void* states, const SegPlan& pl,
                    const SegBuffers& sb, const Dims& d, hipStream_t stream) {
-    using Cfg = SegCfg<P, S, T>;
-    auto kern = state_seg_kernel<P, S, T, NH>;
+    using Cfg = SegCfgFor<P, S, T>;
+    auto kern = state_seg_kernel<P, S, T, seg_tb<S, T>(), NH>;
     if (Cfg::LDS_BYTES > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -42,7 +48,7 @@ template <int P, int S, int T>
 hipError_t seg_by_nh(const void* x, const void* Bm, const float* A, const float* G,
                      const float* dt_t, const float* h0, void* st, const SegPlan& pl,
                      const SegBuffers& sb, const Dims& d, hipStream_t s) {
-    if constexpr (!SegCfg<P, S, T>::FITS) {
+    if constexpr (!SegCfgFor<P, S, T>::FITS) {
         return hipErrorInvalidValue;
     } else {
         switch (pl.heads) {
@@ -140,6 +146,7 @@ hipError_t launch_state_seg(const void* x, const void* Bm, const float* A, const
     switch (d.headdim * 1000 + d.dstate) {
         case 64064: e = seg_by_t<64, 64>(x, Bm, A, G, dt_t, h0, states, pl, sb, d, stream); break;
         case 64128: e = seg_by_t<64, 128>(x, Bm, A, G, dt_t, h0, states, pl, sb, d, stream); break;
+        case 64256: e = seg_by_t<64, 256>(x, Bm, A, G, dt_t, h0, states, pl, sb, d, stream); break;
     }
     if (e != hipSuccess) return e;
     if (pl.nseg == 1 && !final_state) return hipSuccess;

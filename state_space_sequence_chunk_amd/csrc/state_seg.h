@@ -53,41 +53,51 @@ template <int B, int E> struct StaticFor {
     }
 };
 
-template <int P, int S, int T>
+// TB: tokens per step (a sub-block of the chunk; TB = T unless the chunk's B rows would not
+// fit in LDS next to the x buffers).
+template <int P, int S, int T, int TB>
 struct SegCfg {
     static constexpr int NTHR = 512, NWAVE = 8;
+    static constexpr int NSUB = T / TB;  // sub-blocks per chunk
     static constexpr int NPT = P / 16, NST = S / 16;
     static constexpr int WPT = NPT >= NWAVE ? 1 : NWAVE / NPT;  // waves per p-tile
     static constexpr int MST = (NST + WPT - 1) / WPT;           // s-tiles per wave
     static constexpr int VE = 8;                                // bf16 per 16 bytes
     static constexpr int XS = col_stride<bf16>(P), BS = col_stride<bf16>(S);
-    static constexpr int NXV = (T * P / VE + NTHR - 1) / NTHR;  // x vectors per thread
-    static constexpr int NBV = (T * S / VE + NTHR - 1) / NTHR;  // B vectors per thread
+    static constexpr int NXV = (TB * P / VE + NTHR - 1) / NTHR;  // x vectors per thread
+    static constexpr int NBV = (TB * S / VE + NTHR - 1) / NTHR;  // B vectors per thread
     static constexpr int PER = T / 64;                          // tokens per lane in the scan
-    static constexpr size_t X_BYTES = (size_t)T * XS * sizeof(bf16);
-    static constexpr size_t W_BYTES = (size_t)T * sizeof(float);
-    static constexpr size_t B_BYTES = (size_t)T * BS * sizeof(bf16);
-    static constexpr size_t LDS_BYTES = B_BYTES + 2 * (X_BYTES + W_BYTES);
+    static constexpr size_t X_BYTES = (size_t)TB * XS * sizeof(bf16);
+    static constexpr size_t W_BYTES = (size_t)T * sizeof(float);  // one chunk's weights
+    static constexpr size_t B_BYTES = (size_t)TB * BS * sizeof(bf16);
+    // weight slots: one per x buffer when a step is a whole chunk; otherwise one per head
+    // of the block (up to 8) and chunk parity, since a head's weights serve all its
+    // sub-blocks
+    static constexpr int NWS = NSUB == 1 ? 2 : 16;
+    static constexpr size_t LDS_BYTES = B_BYTES + 2 * X_BYTES + NWS * W_BYTES;
     // registers per head for the running state (fp32 per lane)
     static constexpr int STATE_REGS = MST * 4;
-    static constexpr bool FITS = LDS_BYTES <= 163840 && NPT <= NWAVE && NST % WPT == 0;
+    static constexpr bool FITS = LDS_BYTES <= 163840 && NPT <= NWAVE && NST % WPT == 0 &&
+                                 T % TB == 0 && TB % 32 == 0;
 };
 
-template <int P, int S, int T, int NH>
+template <int P, int S, int T, int TB, int NH>
 __global__ __launch_bounds__(512) void state_seg_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ A,
     const float* __restrict__ G, const float* __restrict__ dt_t, const float* __restrict__ h0,
     bf16* __restrict__ states, float* __restrict__ seg_end, float* __restrict__ dec_in,
     float* __restrict__ dec_seg, int L, int H, int ngroups, int K) {
-    using Cfg = SegCfg<P, S, T>;
+    using Cfg = SegCfg<P, S, T, TB>;
     constexpr int VE = Cfg::VE, XS = Cfg::XS, BS = Cfg::BS, NTHR = Cfg::NTHR, PER = Cfg::PER;
-    constexpr int MST = Cfg::MST, WPT = Cfg::WPT;
+    constexpr int MST = Cfg::MST, WPT = Cfg::WPT, NSUB = Cfg::NSUB;
+    constexpr int SPC = NSUB * NH;  // steps per chunk
+    static_assert(NSUB == 1 || NH <= Cfg::NWS / 2, "weight slots");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    bf16* s_b = (bf16*)smem;  // [T][BS]
-    auto s_x = [&](int k) { return (bf16*)(smem + Cfg::B_BYTES + k * (Cfg::X_BYTES + Cfg::W_BYTES)); };
-    auto s_w = [&](int k) {
-        return (float*)(smem + Cfg::B_BYTES + k * (Cfg::X_BYTES + Cfg::W_BYTES) + Cfg::X_BYTES);
+    bf16* s_b = (bf16*)smem;  // [TB][BS] B rows of the current sub-block
+    auto s_x = [&](int k) { return (bf16*)(smem + Cfg::B_BYTES + k * Cfg::X_BYTES); };  // [TB][XS]
+    auto s_w = [&](int k) {  // [T] weights of one (chunk, head)
+        return (float*)(smem + Cfg::B_BYTES + 2 * Cfg::X_BYTES + k * Cfg::W_BYTES);
     };
 
     const int nC = (L + T - 1) / T;
@@ -131,24 +141,25 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
     };
 
     // ---- staging: global -> registers (prefetch, two steps deep) -> LDS -----------------
-    // A step is one (chunk, head) of the segment, in order. Step j's x rows, dt and chunk
+    // A step is one (chunk, sub-block, head) of the segment, heads fastest, in order (with
+    // TB = T: one (chunk, head)). Step j's x rows, dt and chunk
     // decay are loaded into register set j % 2 at the start of step j-2 and moved to LDS
     // buffer j % 2 (wave 0 turning dt into the weights) at the start of step j-1, after
     // that step's own loads are issued; so the staging overlaps the products and the end
-    // of a step is a single barrier. The next chunk's B rows are loaded during a chunk's
-    // last head and replace the current ones between two barriers at its end.
+    // of a step is a single barrier. The next sub-block's B rows are loaded during a
+    // sub-block's last head and replace the current ones between two barriers at its end.
     Vec16 px[2][Cfg::NXV], pb[Cfg::NBV];
     float pdt[2][PER];
     float gls[2] = {0.f, 0.f};  // each set's chunk decay g (log2): G at the chunk's last real token
-    auto load_head = [&](auto set_c, int c, int h) {
+    auto load_head = [&](auto set_c, int c, int sub, int h) {
         constexpr int q = decltype(set_c)::value;
         const int rows = rows_of(c);
         const BufRsrc rx = x_rsrc(c);
 #pragma unroll
         for (int i = 0; i < Cfg::NXV; ++i) {
             const int v = tid + i * NTHR;
-            if (v < T * P / VE) {
-                const int r = v / (P / VE), col = (v % (P / VE)) * VE;
+            if (v < TB * P / VE) {
+                const int r = sub * TB + v / (P / VE), col = (v % (P / VE)) * VE;
                 px[q][i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(bf16)),
                                       (uint32_t)(h * P * sizeof(bf16)));
             }
@@ -163,16 +174,17 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
             pdt[q][k] = buf_load_f32(rdt, (uint32_t)(t < rows ? t * 4 : 0x80000000u), o);
         }
     };
-    // B rows of chunk c through a descriptor over its real rows (padded rows read zeros)
-    auto load_b = [&](int c) {
+    // B rows of sub-block sub of chunk c through a descriptor over the chunk's real rows
+    // (padded rows read zeros)
+    auto load_b = [&](int c, int sub) {
         const int rows = rows_of(c);
         const BufRsrc rb = make_rsrc(Bm + (((size_t)b * L + (size_t)c * T) * ngroups + g) * S,
                                      (uint32_t)(((size_t)(rows - 1) * grow + S) * sizeof(bf16)));
 #pragma unroll
         for (int i = 0; i < Cfg::NBV; ++i) {
             const int v = tid + i * NTHR;
-            if (v < T * S / VE) {
-                const int r = v / (S / VE), col = (v % (S / VE)) * VE;
+            if (v < TB * S / VE) {
+                const int r = sub * TB + v / (S / VE), col = (v % (S / VE)) * VE;
                 pb[i] = buf_load16(rb, (uint32_t)(((size_t)r * grow + col) * sizeof(bf16)), 0u);
             }
         }
@@ -181,25 +193,26 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
 #pragma unroll
         for (int i = 0; i < Cfg::NBV; ++i) {
             const int v = tid + i * NTHR;
-            if (v < T * S / VE) {
+            if (v < TB * S / VE) {
                 const int r = v / (S / VE), col = (v % (S / VE)) * VE;
                 *(Vec16*)(s_b + r * BS + col) = pb[i];
             }
         }
     };
-    // register set q -> LDS buffer q (x rows; wave 0 turns dt into the weights)
-    auto store_head = [&](auto set_c, int h) {
+    // register set q -> LDS buffer q (x rows); at a chunk's first sub-block wave 0 also
+    // turns the chunk's dt into the head's weights, in weight slot ws
+    auto store_head = [&](auto set_c, int h, bool first_sub, int ws) {
         constexpr int q = decltype(set_c)::value;
         bf16* bx = s_x(q);
 #pragma unroll
         for (int i = 0; i < Cfg::NXV; ++i) {
             const int v = tid + i * NTHR;
-            if (v < T * P / VE) {
+            if (v < TB * P / VE) {
                 const int r = v / (P / VE), col = (v % (P / VE)) * VE;
                 *(Vec16*)(bx + r * XS + col) = px[q][i];
             }
         }
-        if (wave == 0) {
+        if (wave == 0 && first_sub) {
             // w_t = dt_t 2^{log2(e) sum_{k>t} A dt_k}: scanned from the chunk's end
             const float ah = A[h];
             float pre[PER], run = 0.f;
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
                 run += ah * pdt[q][k];
             }
             const float excl = wave_shift_up1(wave_inclusive_scan(run));
-            float* bw = s_w(q);
+            float* bw = s_w(ws);
 #pragma unroll
             for (int k = 0; k < PER; ++k)
                 bw[T - 1 - (PER * lane + k)] = pdt[q][k] * exp2_fast((excl + pre[k]) * kLog2e);
@@ -233,62 +246,74 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
         }
     }
 
-    // ---- one step: head hh of chunk ci of the segment, register set / LDS buffer q ------
-    auto step = [&](auto hh_c, auto q_c, int ci) {
-        constexpr int hh = decltype(hh_c)::value, q = decltype(q_c)::value;
-        constexpr int h2 = (hh + 2) % NH, dc2 = (hh + 2) / NH;  // the step two ahead
+    // weight slot of head hh in chunk c: per x buffer q when a step is a whole chunk,
+    // otherwise per (chunk parity, head)
+    auto wslot = [&](int q, int hh, int c) { return NSUB == 1 ? q : (c & 1) * NH + hh; };
+
+    // ---- one step: step u of chunk ci (sub-block u / NH, head u % NH), set / buffer q ----
+    auto step = [&](auto u_c, auto q_c, int ci) {
+        constexpr int u = decltype(u_c)::value, q = decltype(q_c)::value;
+        constexpr int hh = u % NH, sub = u / NH;
+        constexpr int u1 = (u + 1) % SPC, dc1 = (u + 1) / SPC;  // the next step
+        constexpr int u2 = (u + 2) % SPC, dc2 = (u + 2) / SPC;  // the step two ahead
         const int c = c_first + ci, h = h_first + hh;
-        const bool more = ci + 1 < nck;
+        const bool next = ci + dc1 < nck;  // a next step in this segment
         const float gl = gls[q];  // this step's chunk decay, before set q is reloaded
         // Every step issues the same memory operations (past the segment's end they repeat
         // its last chunk and are never used), so the compiler's wait before each use counts
         // exactly the operations issued since, and the loads two steps ahead stay in flight.
-        load_head(q_c, min(c + dc2, c_first + nck - 1), h_first + h2);
-        if constexpr (hh == NH - 1) load_b(more ? c + 1 : c);
+        load_head(q_c, min(c + dc2, c_first + nck - 1), u2 / NH, h_first + u2 % NH);
+        if constexpr (hh == NH - 1) {  // the next sub-block's B rows
+            if constexpr (sub + 1 < NSUB) load_b(c, sub + 1);
+            else load_b(next ? c + 1 : c, 0);
+        }
         // stage the next step now (its loads were issued a step ago): LDS buffer q^1 was
         // last read by the previous step, which ended at a barrier; the next step reads
         // it after this step's barrier. Past the segment's end the copy is never read.
         constexpr IntC<q ^ 1> q1{};
-        store_head(q1, hh + 1 < NH ? h + 1 : h_first);
+        store_head(q1, h_first + u1 % NH, u1 / NH == 0, wslot(q ^ 1, u1 % NH, c + dc1));
 
-        // record the state entering chunk c (from the segment's start), then advance it.
-        // For each pair of adjacent tiles (m, m+1) the lanes 16 apart (slot groups 2k and
-        // 2k+1) swap one tile's four values, so that the even lane holds columns
-        // 16(st0+m) + 4 g4 .. +7 and the odd one 16(st0+m+1) + 4(g4-1) .. +7: one 16-byte
-        // store per lane writes 64 contiguous bytes of each of the 16 rows.
-        const BufRsrc rst = make_rsrc(states + (((size_t)b * H + h) * nC + c) * (size_t)P * S,
-                                      (uint32_t)(P * S * sizeof(bf16)));
-#pragma unroll
-        for (int m = 0; m < MST; m += 2) {
-            bf16x4 o0, o1;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                o0[r] = from_f32<bf16>(acc[hh][m][r]);
-                o1[r] = from_f32<bf16>(acc[hh][m + 1][r]);
+        if constexpr (sub == 0) {
+            // record the state entering chunk c (from the segment's start), then advance it.
+            // For each pair of adjacent tiles (m, m+1) the lanes 16 apart (slot groups 2k and
+            // 2k+1) swap one tile's four values, so that the even lane holds columns
+            // 16(st0+m) + 4 g4 .. +7 and the odd one 16(st0+m+1) + 4(g4-1) .. +7: one 16-byte
+            // store per lane writes 64 contiguous bytes of each of the 16 rows.
+            const BufRsrc rst = make_rsrc(states + (((size_t)b * H + h) * nC + c) * (size_t)P * S,
+                                          (uint32_t)(P * S * sizeof(bf16)));
+    #pragma unroll
+            for (int m = 0; m < MST; m += 2) {
+                bf16x4 o0, o1;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    o0[r] = from_f32<bf16>(acc[hh][m][r]);
+                    o1[r] = from_f32<bf16>(acc[hh][m + 1][r]);
+                }
+                const u32x2 a = __builtin_bit_cast(u32x2, o0), a1 = __builtin_bit_cast(u32x2, o1);
+                const u32x2 send = odd_g4 ? a : a1;
+                u32x2 recv;
+                recv[0] = (uint32_t)__shfl_xor((int)send[0], 16);
+                recv[1] = (uint32_t)__shfl_xor((int)send[1], 16);
+                const u32x2 first = odd_g4 ? recv : a, second = odd_g4 ? a1 : recv;
+                const Vec16 out = Vec16{first[0], first[1], second[0], second[1]};
+                __builtin_amdgcn_raw_buffer_store_b128(out, rst, st_off,
+                                                       (uint32_t)(m * 16 * sizeof(bf16)), 0);
             }
-            const u32x2 a = __builtin_bit_cast(u32x2, o0), a1 = __builtin_bit_cast(u32x2, o1);
-            const u32x2 send = odd_g4 ? a : a1;
-            u32x2 recv;
-            recv[0] = (uint32_t)__shfl_xor((int)send[0], 16);
-            recv[1] = (uint32_t)__shfl_xor((int)send[1], 16);
-            const u32x2 first = odd_g4 ? recv : a, second = odd_g4 ? a1 : recv;
-            const Vec16 out = Vec16{first[0], first[1], second[0], second[1]};
-            __builtin_amdgcn_raw_buffer_store_b128(out, rst, st_off,
-                                                   (uint32_t)(m * 16 * sizeof(bf16)), 0);
+            // dec_in[b, h, c] from thread 0; the other lanes' offsets are out of range (dropped)
+            buf_store_f32(dacc[hh], rdec, tid == 0 ? (uint32_t)(((size_t)h * nC + c) * 4) : 0x80000000u,
+                          0u);
+            dacc[hh] += gl;
+            const float dec = exp2_fast(gl);
+    #pragma unroll
+            for (int m = 0; m < MST; ++m) acc[hh][m] *= dec;
+
         }
-        // dec_in[b, h, c] from thread 0; the other lanes' offsets are out of range (dropped)
-        buf_store_f32(dacc[hh], rdec, tid == 0 ? (uint32_t)(((size_t)h * nC + c) * 4) : 0x80000000u,
-                      0u);
-        dacc[hh] += gl;
-        const float dec = exp2_fast(gl);
-#pragma unroll
-        for (int m = 0; m < MST; ++m) acc[hh][m] *= dec;
 
         const bf16* bx = s_x(q);
-        const float* bw = s_w(q);
+        const float* bw = s_w(wslot(q, hh, c)) + sub * TB;
         // slot (g4, v) carries token 32 ks + 16 (v/4) + 4 g4 + v%4 (two column reads)
 #pragma unroll 2
-        for (int ks = 0; ks < T / 32; ++ks) {
+        for (int ks = 0; ks < TB / 32; ++ks) {
             const int r_lo = ks * 32 + 4 * g4, r_hi = r_lo + 16;
             Frag<bf16> bf[MST];
 #pragma unroll
@@ -318,39 +343,40 @@ __global__ __launch_bounds__(512) void state_seg_kernel(
             }
         }
 
-        // hand over to the next step (at a chunk's end, after the B rows are replaced)
+        // hand over to the next step (at a sub-block's end, after the B rows are replaced)
         if constexpr (hh + 1 < NH) {
             lds_barrier();
         } else {
-            if (more) {
-                lds_barrier();  // every wave is done with this chunk's B rows
+            if (next) {
+                lds_barrier();  // every wave is done with this sub-block's B rows
                 store_b();
                 lds_barrier();
             }
         }
     };
 
-    // ---- prologue: the first chunk's B rows, steps 0 and 1 loaded, step 0 in LDS --------
-    load_head(IntC<0>{}, c_first, h_first);
-    load_head(IntC<1>{}, min(c_first + 1 / NH, c_first + nck - 1), h_first + 1 % NH);
-    load_b(c_first);
+    // ---- prologue: the first sub-block's B rows, steps 0 and 1 loaded, step 0 in LDS ----
+    load_head(IntC<0>{}, c_first, 0, h_first);
+    load_head(IntC<1>{}, min(c_first + 1 / SPC, c_first + nck - 1), (1 % SPC) / NH,
+              h_first + (1 % SPC) % NH);
+    load_b(c_first, 0);
     store_b();
-    store_head(IntC<0>{}, h_first);
+    store_head(IntC<0>{}, h_first, true, wslot(0, 0, c_first));
     lds_barrier();
 
-    // ---- main loop: each step's set known at compile time (one chunk per pass when NH is
-    // even, two when it is odd) --------------------------------------------------------
-    constexpr int CPP = NH % 2 == 0 ? 1 : 2;  // chunks per pass
+    // ---- main loop: each step's set known at compile time (one chunk per pass when a
+    // chunk has an even number of steps, two when it is odd) ------------------------------
+    constexpr int CPP = SPC % 2 == 0 ? 1 : 2;  // chunks per pass
     for (int ci = 0; ci < nck; ci += CPP) {
-        StaticFor<0, NH>::run([&](auto hh_c) {
-            constexpr int hh = decltype(hh_c)::value;
-            step(hh_c, IntC<(hh & 1)>{}, ci);
+        StaticFor<0, SPC>::run([&](auto u_c) {
+            constexpr int u = decltype(u_c)::value;
+            step(u_c, IntC<(u & 1)>{}, ci);
         });
         if constexpr (CPP == 2) {
             if (ci + 1 < nck) {
-                StaticFor<0, NH>::run([&](auto hh_c) {
-                    constexpr int hh = decltype(hh_c)::value;
-                    step(hh_c, IntC<((NH + hh) & 1)>{}, ci + 1);
+                StaticFor<0, SPC>::run([&](auto u_c) {
+                    constexpr int u = decltype(u_c)::value;
+                    step(u_c, IntC<((SPC + u) & 1)>{}, ci + 1);
                 });
             }
         }

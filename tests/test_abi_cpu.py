@@ -83,10 +83,13 @@ def test_workspace_sizes():
     with pytest.raises(ssd.SSDError):
         ssd.forward_workspace_bytes(shape(ngroups=3))
     for kw in (dict(states_dtype=ssd.SSD_F32), dict(in_dtype=ssd.SSD_F32, states_dtype=ssd.SSD_F32),
-               dict(headdim=128), dict(dstate=256)):
+               dict(headdim=128)):
         with pytest.raises(ssd.SSDError) as e:
             ssd.state_seg_workspace_bytes(shape(**kw))
         assert e.value.code == 4, kw
+    # dstate 256 (128-token sub-blocks inside the kernel) has a plan at every chunk length
+    for t in (64, 128, 256):
+        assert ssd.state_seg_workspace_bytes(shape(dstate=256, chunk=t)) > 0
     assert ssd.state_seg_workspace_bytes(shape(seqlen=0)) == 0
 
 

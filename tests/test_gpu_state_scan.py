@@ -117,11 +117,12 @@ def test_state_scan_full_size_final_state():
 
 def test_forward_through_state_scan():
     # 4 x 128 heads of headdim 64: 512 workgroups of 64 rows (two full rounds over the
-    # compute units), where ssd_forward takes the single-pass state kernel; y and the
-    # final state against the oracle, every element
+    # compute units), where ssd_forward takes the single-pass state kernel for fp32 chunk
+    # states (bf16 ones go to the segmented pass); y and the final state against the
+    # oracle, every element
     w = gen.Workload("wide", 4, 512, 128, 64, 64, 4, 64, "bf16", True, 54)
     cpu, d = make(w)
-    y, fin = gpu_forward(w, d)
+    y, fin = gpu_forward(w, d, states_dtype=torch.float32)
     ref = oracle_forward(cpu)
     ey, ef = max_rel_rms(y, ref["y"]), max_rel_rms(fin, ref["final"])
     _print(f"wide forward: y max/rms {ey:.2e}  final max/rms {ef:.2e}")

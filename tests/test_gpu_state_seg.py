@@ -1,6 +1,6 @@
 """The segmented state pass (ssd_state_seg + ssd_chunk_out_seg, which ssd_forward takes
-for bf16 inputs with bf16 states at headdim 64, dstate 64 or 128) against the fp64 oracle
-on the GPU.
+for bf16 inputs with bf16 states at headdim 64, dstate 64, 128 or 256) against the fp64
+oracle on the GPU.
 
 The shapes are chosen so that the library's segment plan differs between them: 1 to 8
 heads per workgroup, 2 to 16 chunks per segment, a short last segment, a partial last
@@ -44,6 +44,14 @@ CASES = {
     "one-seg-3x16": _w("one-seg-3x16", 16, 2048, 48, 4, 128, 128, True, 20),
     # one partial chunk: one segment
     "one-chunk": _w("one-chunk", 1, 200, 4, 1, 128, 256, True, 18),
+    # dstate 256 (the long-context layer's per-head shape): 2 x 3 with two 128-token
+    # sub-blocks per chunk; four groups
+    "s256-2x3": _w("s256-2x3", 2, 4096, 40, 4, 256, 256, True, 21),
+    # dstate 256, 1 x 2, sub-blocks, partial last chunk, no h0
+    "s256-ragged-1x2": _w("s256-ragged-1x2", 1, 4000, 20, 2, 256, 256, False, 22),
+    # dstate 256 at chunk 128 (one step per chunk and head) and chunk 64
+    "s256-t128-1x3": _w("s256-t128-1x3", 2, 2048, 20, 2, 256, 128, True, 23),
+    "s256-t64-1x2": _w("s256-t64-1x2", 1, 3000, 10, 1, 256, 64, True, 24),
 }
 
 
@@ -70,7 +78,7 @@ def test_forward_segmented_all_elements(name):
     assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("name", ["ragged-1x2", "short-seg-3x3", "nh6-6x8"])
+@pytest.mark.parametrize("name", ["ragged-1x2", "short-seg-3x3", "nh6-6x8", "s256-2x3"])
 def test_forward_segmented_ssm_only(name):
     """D = 0: the state path alone, where the skip term cannot hide an error."""
     w = CASES[name]
