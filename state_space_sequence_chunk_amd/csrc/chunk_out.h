@@ -76,7 +76,7 @@ template <> struct StateFrag<bf16, float> {
     }
 };
 
-template <typename TIn, typename TS, int P, int S, int T>
+template <typename TIn, typename TS, int P, int S, int T, bool SEGC = false>
 struct OutCfg {
     static constexpr int NW = T / 32, NTHR = 2 * T, NIT = T / 16;
     static constexpr int NPT = P / 16, NKS = (S + 31) / 32;
@@ -95,7 +95,9 @@ struct OutCfg {
     static constexpr size_t B_BYTES = (size_t)T * BS * sizeof(TIn);
     // the tiles plus one all-zero tile that stands in for tiles above the diagonal
     static constexpr size_t TILE_BYTES = (size_t)(NTILE + 1) * 256 * sizeof(TIn);
-    static constexpr size_t LDS_MAX = 163840;
+    // SEGC: each head's log2 decay from its segment's start (up to 256 heads) after the rest
+    static constexpr size_t DEC_BYTES = SEGC ? 256 * sizeof(float) : 0;
+    static constexpr size_t LDS_MAX = 163840 - DEC_BYTES;
     // interaction tiles shared by the heads of a workgroup
     static constexpr bool SHARED = HEAD_BYTES + TILE_BYTES <= LDS_MAX;
     // B staged in LDS: in SHARED mode only while the tiles are built (over the per-head
@@ -105,8 +107,9 @@ struct OutCfg {
                : HEAD_BYTES + B_BYTES <= LDS_MAX;
     static constexpr size_t REGION0 =
         SHARED ? (B_IN_LDS && B_BYTES > HEAD_BYTES ? B_BYTES : HEAD_BYTES) : HEAD_BYTES;
-    static constexpr size_t LDS_BYTES =
+    static constexpr size_t BASE_BYTES =
         SHARED ? REGION0 + TILE_BYTES : HEAD_BYTES + (B_IN_LDS ? B_BYTES : 0);
+    static constexpr size_t LDS_BYTES = BASE_BYTES + DEC_BYTES;
 };
 
 // y element store through a buffer descriptor: fp32, or bf16 rounded to nearest even.
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const float* __restrict__ G, const float* __restrict__ dt_t, const TS* __restrict__ states,
     const float* __restrict__ Dv, TY* __restrict__ y, int L, int H, int ngroups, int NH,
     const TS* __restrict__ seg_in, const float* __restrict__ dec_in, int seg_chunks) {
-    using Cfg = OutCfg<TIn, TS, P, S, T>;
+    using Cfg = OutCfg<TIn, TS, P, S, T, SEGC>;
     static_assert(!SEGC || sizeof(TS) == 2, "segment-relative states are bf16");
     constexpr int NPT = Cfg::NPT, NKS = Cfg::NKS, XS = Cfg::XS, SS = Cfg::SS, BS = Cfg::BS;
     constexpr int VE = Cfg::VE, VES = Cfg::VES, NTHR = Cfg::NTHR;
@@ -141,6 +144,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     // B rows: over the per-head region (SHARED, prologue only) or after it
     TIn* s_b = (TIn*)(smem + (Cfg::SHARED ? 0 : Cfg::HEAD_BYTES));         // [T][BS]
     TIn* s_tiles = (TIn*)(smem + Cfg::REGION0);                            // [NTILE+1][64][4]
+    float* s_dec = (float*)(smem + Cfg::BASE_BYTES);                       // [NH] (SEGC)
 
     const int nC = (L + T - 1) / T;
     const int nhb = H / NH;
@@ -182,6 +186,9 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const int nseg = SEGC ? (nC + seg_chunks - 1) / seg_chunks : 0;
     Vec16 psi[SEGC ? Cfg::NSV : 1];
     float pdec = 0.f;
+    // Below this log2 decay 2^{D_c} is exactly 0 in fp32 (even as a denormal), so the
+    // correction adds exactly nothing and the entering state is not read at all.
+    constexpr float kSegCut = -160.f;
     auto load_head = [&](int h) {
 #pragma unroll
         for (int i = 0; i < Cfg::NXV; ++i) {
@@ -199,14 +206,18 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         }
         if constexpr (SEGC) {
             if (corr) {
-                const BufRsrc rsi = make_rsrc(seg_in + (((size_t)b * H + h) * nseg + seg) * P * S,
-                                              (uint32_t)(P * S * sizeof(TS)));
+                // the first head's decay from global memory, the others' from LDS (staged
+                // by the prologue)
+                pdec = h == h_first ? dec_in[((size_t)b * H + h) * nC + c] : s_dec[h - h_first];
+                if (pdec >= kSegCut) {
+                    const BufRsrc rsi = make_rsrc(seg_in + (((size_t)b * H + h) * nseg + seg) * P * S,
+                                                  (uint32_t)(P * S * sizeof(TS)));
 #pragma unroll
-                for (int i = 0; i < Cfg::NSV; ++i) {
-                    const int v = tid + i * NTHR;
-                    if (v < P * S / VES) psi[i] = buf_load16(rsi, (uint32_t)(v * 16), 0u);
+                    for (int i = 0; i < Cfg::NSV; ++i) {
+                        const int v = tid + i * NTHR;
+                        if (v < P * S / VES) psi[i] = buf_load16(rsi, (uint32_t)(v * 16), 0u);
+                    }
                 }
-                pdec = dec_in[((size_t)b * H + h) * nC + c];
             }
         }
         if (tid < T) {
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             *(Vec16*)(s_x + r * XS + col) = px[i];
         }
         if constexpr (SEGC) {
-            if (corr) {
+            if (corr && pdec >= kSegCut) {
                 const float f = exp2_fast(pdec);
 #pragma unroll
                 for (int i = 0; i < Cfg::NSV; ++i) {
@@ -292,6 +303,10 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         return s_tiles + ((size_t)k * 64 + lane) * 4;
     };
     load_head(h_first);  // in flight while the tiles are built
+    if constexpr (SEGC) {
+        // the block's decays from the segment's start, read by the later heads' loads
+        if (corr && tid < NH) s_dec[tid] = dec_in[((size_t)b * H + h_first + tid) * nC + c];
+    }
     if constexpr (Cfg::SHARED) {
         // build this wave's interaction tiles once for all heads of the workgroup
         if constexpr (Cfg::B_IN_LDS) lds_barrier();
@@ -507,7 +522,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
 // interaction tiles), so it should serve as many heads as possible -- but the grid must
 // still cover every CU with as many resident workgroups as fit. Pick the largest divisor
 // of the heads per group whose grid still gives every CU its resident workgroups.
-inline int heads_per_block(const Dims& d, size_t lds_bytes) {
+inline int heads_per_block(const Dims& d, size_t lds_bytes, int max_nh = 1 << 30) {
     const int hpg = d.nheads / d.ngroups;
     const long units = (long)d.batch * d.nchunks() * d.nheads;
     const long per_cu = std::max<long>(1, std::min<long>(163840 / (long)std::max<size_t>(lds_bytes, 1),
@@ -515,7 +530,7 @@ inline int heads_per_block(const Dims& d, size_t lds_bytes) {
     const long want = 256L * per_cu;  // workgroups that fill 256 CUs once
     int best = 1;
     for (int nh = 1; nh <= hpg; ++nh)
-        if (hpg % nh == 0 && units / nh >= want) best = nh;
+        if (hpg % nh == 0 && units / nh >= want && nh <= max_nh) best = nh;
     return best;
 }
 
@@ -524,7 +539,7 @@ hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G
                    const float* dt_t, const void* states, const float* D, void* y,
                    const Dims& d, hipStream_t stream, const void* seg_in = nullptr,
                    const float* dec_in = nullptr, int seg_chunks = 0) {
-    using Cfg = OutCfg<TIn, TS, P, S, T>;
+    using Cfg = OutCfg<TIn, TS, P, S, T, SEGC>;
     auto kern = chunk_out_kernel<TIn, TS, TY, P, S, T, SEGC>;
     if (Cfg::LDS_BYTES > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -532,7 +547,8 @@ hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G
                                            (int)Cfg::LDS_BYTES);
         if (e != hipSuccess) return e;
     }
-    const int nh = heads_per_block(d, Cfg::LDS_BYTES);
+    // SEGC: the block's decays are staged in LDS for at most 256 heads
+    const int nh = heads_per_block(d, Cfg::LDS_BYTES, SEGC ? 256 : 1 << 30);
     const int nblocks = d.batch * d.nchunks() * (d.nheads / nh);
     kern<<<nblocks, 2 * T, Cfg::LDS_BYTES, stream>>>((const TIn*)x, (const TIn*)Bm,
                                                      (const TIn*)Cm, G, dt_t,
