@@ -287,7 +287,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
     if constexpr (OP == kOpX) stk.store(s_k, nullptr, KS, tid);
     else stv.store(s_v, nullptr, VS, tid);
     store_head();
-    __syncthreads();
+    lds_barrier();
 
     const uint32_t row0s[2] = {(uint32_t)(wave * 16 + 4 * g4),
                                (uint32_t)((NIT - 1 - wave) * 16 + 4 * g4)};
@@ -528,7 +528,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
                 }
             }
         }
-        __syncthreads();  // every wave is done with this head's LDS and partials
+        lds_barrier();  // every wave is done with this head's LDS and partials
         if constexpr (OP != kOpB) {
             const size_t bhl = bhl_of(h);
             if (tid < rows) {
@@ -547,7 +547,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
             }
         }
         if (hh + 1 < NH) store_head();
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- dC, dB: the sum over this workgroup's heads, [B, L, H / NH, S] (the output itself
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(2 * T) void bwd_dR_mfma_kernel(BwdArgs a) {
         *(bf16x8*)(s_yl + r * YS + col) = lo;
     }
     stc.store(s_c, nullptr, CS, tid);
-    __syncthreads();
+    lds_barrier();
 
     float* out = a.R + (((size_t)b * H + h) * nC + c) * P * S;
 #pragma unroll 1
