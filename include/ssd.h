@@ -133,7 +133,8 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
  * or 128, dstate 64, 128 or 256, and seqlen a positive multiple of chunk; other shapes
  * return SSD_ERR_UNSUPPORTED. The fused state operand dt_j 2^{G_last - G_j} x_j enters the
  * matrix cores as a bf16 high/low pair, as in ssd_state_pass. ssd_forward takes this kernel
- * instead of the two-kernel pass for the shapes where it measured faster.
+ * instead of the two-kernel pass for the shapes where it measured faster and the segmented
+ * pass below has no plan.
  */
 ssd_status ssd_state_scan(const ssd_shape* shape, const void* x, const float* A, const void* B,
                           const float* dt_t, const float* h0, void* states, float* final_state,
@@ -168,8 +169,8 @@ ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, c
  * the true states, adding 2^{D_c} S_in(k) while it stages each chunk's state (fp32 sum,
  * one bf16 rounding). The per-chunk state increments never go to HBM. ssd_forward runs
  * these two (after stage 1) whenever the shape has a segment plan.
- * Built for bf16 inputs with bf16 states (states_dtype SSD_BF16), headdim 64, dstate 64
- * or 128; other shapes return SSD_ERR_UNSUPPORTED (as does the workspace query). Inputs
+ * Built for bf16 inputs with bf16 states (states_dtype SSD_BF16), headdim 64, dstate 64,
+ * 128 or 256; other shapes return SSD_ERR_UNSUPPORTED (as does the workspace query). Inputs
  * as for ssd_state_pass and ssd_chunk_out; the workspace must hold
  * ssd_state_seg_workspace_bytes bytes and is passed unchanged from ssd_state_seg to
  * ssd_chunk_out_seg on the same stream (it carries S_in and D_c between them).

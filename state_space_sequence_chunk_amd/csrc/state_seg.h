@@ -19,16 +19,19 @@
 //
 // gfx950 mapping: one workgroup of 8 waves per (batch, segment, block of NH heads of one
 // B group). Each head's running state (P x S fp32) is spread over the waves in the MFMA
-// accumulator layout and stays in registers for the whole segment. Per chunk the group's
-// B rows are staged in LDS once and shared by the NH heads; per (chunk, head) the x rows
-// and the decay weights are double-buffered in LDS, the next step's 16-byte loads (and,
-// at a chunk's last head, the next chunk's B rows) in flight while the current products
-// run. The contraction over the chunk's tokens is dS^T = B^T (w o x) on bf16 MFMA
+// accumulator layout and stays in registers for the whole segment. A step is one (chunk,
+// sub-block of TB tokens, head); TB is the whole chunk unless the chunk's B rows would not
+// fit in LDS (dstate 256 with 256-token chunks: TB = 128). Per sub-block the group's B
+// rows are staged in LDS once and shared by the NH heads; per step the x rows and the
+// decay weights are double-buffered in LDS, the loads two steps ahead (and, at a
+// sub-block's last head, the next sub-block's B rows) in flight while the current
+// products run. The contraction over the tokens is dS^T = B^T (w o x) on bf16 MFMA
 // 16x16x32 with both operands from the transposing LDS read; the fused operand w_j x_j is
 // formed in fp32 and split into a bf16 high part and a bf16 remainder (two MFMAs against
 // the exact bf16 B). The accumulator holds four consecutive state columns s of one row p
-// per lane, so each recorded state leaves as one 8-byte store per lane and tile. Wave 0
-// forms each head's weights with a single-wave DPP suffix scan.
+// per lane; a swap between lanes 16 apart gives each lane eight, so each recorded state
+// leaves as 16-byte stores (64 contiguous bytes of each of 16 rows per instruction). Wave
+// 0 forms each head's weights, once per chunk, with a single-wave DPP suffix scan.
 #pragma once
 
 #include <algorithm>
