@@ -32,9 +32,11 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
 
 
-def algorithmic(w):
+def algorithmic(w, nseg=None):
     """Bytes each stage must move (inputs read once, outputs written once) and the
-    per-head dense flop count of the matrix stages."""
+    per-head dense flop count of the matrix stages. With nseg (the segmented state pass's
+    segment count), chunk_out's bytes include the states entering segments 1.. (bf16), which
+    it reads to complete the segment-relative chunk states."""
     B, L, H, P, S, G, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     e = 2 if w.dtype == "bf16" else 4
     es = e  # chunk-initial states are stored in the input dtype
@@ -54,6 +56,8 @@ def algorithmic(w):
         "state_seg": x + bc + dec + H * 4 + h0 + n_states * es + fin,
         "chunk_out": x + 2 * bc + 2 * dec + n_states * es + H * 4 + B * L * H * P * 4,
     }
+    if nseg:
+        by["chunk_out"] += (nseg - 1) * B * H * P * S * 2
     fl = {
         "chunk_state": 2.0 * B * nC * H * T * P * S,
         "chunk_out": B * nC * H * (2.0 * T * T * S + 2.0 * T * S * P + 2.0 * T * T * P),
@@ -442,7 +446,7 @@ def main():
     except Exception as exc:  # reported, never silently replaced
         decode = {"error": f"{type(exc).__name__}: {exc}"}
 
-    by, fl = algorithmic(w)
+    by, fl = algorithmic(w, ssd.state_seg_plan(sh)[2] if segmented else None)
     kernels = {
         "cumsum": {"ms": stage_ms["cumsum"], "bytes": by["cumsum"]},
         "state_pass": {"ms": stage_ms["state_pass"],

@@ -176,6 +176,11 @@ ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, c
  * ssd_chunk_out_seg on the same stream (it carries S_in and D_c between them).
  */
 ssd_status ssd_state_seg_workspace_bytes(const ssd_shape* shape, size_t* bytes);
+/* The segment plan the library takes for a shape (host-only): heads per workgroup,
+ * chunks per segment K and the number of segments. SSD_ERR_UNSUPPORTED where the shape
+ * has no plan (or seqlen is 0). Any of the outputs may be NULL. */
+ssd_status ssd_state_seg_plan(const ssd_shape* shape, int32_t* heads_per_workgroup,
+                              int32_t* chunks_per_segment, int32_t* segments);
 ssd_status ssd_state_seg(const ssd_shape* shape, const void* x, const float* A, const void* B,
                          const float* G, const float* dt_t, const float* h0, void* states,
                          float* final_state, void* workspace, size_t workspace_bytes,

@@ -215,6 +215,18 @@ ssd_status ssd_state_seg_workspace_bytes(const ssd_shape* shape, size_t* bytes) 
     return SSD_OK;
 }
 
+ssd_status ssd_state_seg_plan(const ssd_shape* shape, int32_t* heads_per_workgroup,
+                              int32_t* chunks_per_segment, int32_t* segments) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    ssd::SegPlan pl;
+    SSD_REQUIRE(seg_plan_of(shape, &pl), SSD_ERR_UNSUPPORTED);
+    if (heads_per_workgroup) *heads_per_workgroup = pl.heads;
+    if (chunks_per_segment) *chunks_per_segment = pl.chunks;
+    if (segments) *segments = pl.nseg;
+    return SSD_OK;
+}
+
 ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float* A, float* G,
                             float* dt_t, void* stream) {
     ssd_status st = check_shape(shape);

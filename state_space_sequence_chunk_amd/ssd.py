@@ -23,7 +23,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE"
 EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_bytes",
            "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
            "ssd_state_scan", "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
-           "ssd_backward", "ssd_state_seg_workspace_bytes", "ssd_state_seg", "ssd_chunk_out_seg")
+           "ssd_backward", "ssd_state_seg_workspace_bytes", "ssd_state_seg", "ssd_chunk_out_seg",
+           "ssd_state_seg_plan")
 
 
 class SSDError(RuntimeError):
@@ -73,6 +74,8 @@ def load_library():
     lib.ssd_state_seg_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
     lib.ssd_state_seg.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_chunk_out_seg.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.ssd_state_seg_plan.argtypes = [sp, i32p, i32p, i32p]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -176,6 +179,16 @@ def state_seg_workspace_bytes(shape: ssd_shape) -> int:
     _check(load_library().ssd_state_seg_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)),
            "ssd_state_seg_workspace_bytes")
     return int(n.value)
+
+
+def state_seg_plan(shape: ssd_shape):
+    """(heads per workgroup, chunks per segment, segments) of the segmented state pass;
+    raises SSDError (SSD_ERR_UNSUPPORTED) for shapes without a plan."""
+    h, k, n = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load_library().ssd_state_seg_plan(ctypes.byref(shape), ctypes.byref(h),
+                                             ctypes.byref(k), ctypes.byref(n)),
+           "ssd_state_seg_plan")
+    return int(h.value), int(k.value), int(n.value)
 
 
 def ssd_state_seg(shape, x, A, B, G, dt_t, h0, states, final_state, workspace, stream=None):

@@ -93,6 +93,21 @@ def test_workspace_sizes():
     assert ssd.state_seg_workspace_bytes(shape(seqlen=0)) == 0
 
 
+def test_segment_plan_query():
+    # the 2.7B layer: 5 heads per workgroup, 8 chunks per segment, 8 segments (256 workgroups)
+    s = ssd.make_shape(2, 16384, 80, 64, 128, 1, 256, ssd.SSD_BF16)
+    assert ssd.state_seg_plan(s) == (5, 8, 8)
+    # the long layer at dstate 256: 2 heads x 43 chunks, 6 segments (240 workgroups)
+    assert ssd.state_seg_plan(ssd.make_shape(1, 65536, 80, 64, 256, 8, 256, ssd.SSD_BF16)) == (2, 43, 6)
+    lib = ssd.load_library()
+    assert lib.ssd_state_seg_plan(ctypes.byref(s), None, None, None) == 0
+    for kw in (dict(states_dtype=ssd.SSD_F32), dict(headdim=128), dict(seqlen=0)):
+        with pytest.raises(ssd.SSDError) as e:
+            ssd.state_seg_plan(shape(**kw))
+        assert e.value.code == 4, kw
+    assert lib.ssd_state_seg_plan(ctypes.byref(shape(ngroups=3)), None, None, None) == 2
+
+
 def test_segmented_entry_points_reject_before_launch():
     lib = ssd.load_library()
     s = shape()

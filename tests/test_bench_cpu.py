@@ -28,6 +28,9 @@ def test_algorithmic_bytes_at_the_bench_shape():
     dec = 2 * 80 * 16384 * 4             # G or dt_t
     states = 2 * 80 * 64 * 64 * 128      # chunk-initial states, elements
     assert by["chunk_out"] == x + 2 * bc + 2 * dec + states * 2 + 80 * 4 + y
+    # over segment-relative states (8 segments): plus the 7 states entering segments 1..
+    by8, _ = bench.algorithmic(w, 8)
+    assert by8["chunk_out"] == by["chunk_out"] + 7 * 2 * 80 * 64 * 128 * 2
     assert by["chunk_state"] == x + bc + dec + 80 * 4 + states * 4
     # the page's per-head dense flops: 2 T^2 S + 2 T S P + 2 T^2 P per (batch, chunk, head)
     assert fl["chunk_out"] == 2 * 64 * 80 * (2.0 * 256 * 256 * 128 + 2.0 * 256 * 128 * 64
@@ -46,5 +49,13 @@ def test_recorded_traffic_is_consistent():
     assert bench.measured_traffic("no-such-workload") is None
     t = bench.measured_traffic("2.7b-bf16")
     if t is not None:
-        by, _ = bench.algorithmic(gen.WORKLOADS["2.7b-bf16"])
+        w = gen.WORKLOADS["2.7b-bf16"]
+        # the bench shape takes the segmented state pass: chunk_out also reads the states
+        # entering segments 1..
+        from state_space_sequence_chunk_amd import ssd
+        sh = ssd.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                            w.chunk, ssd.SSD_BF16)
+        nseg = ssd.state_seg_plan(sh)[2]
+        assert nseg == 8
+        by, _ = bench.algorithmic(w, nseg)
         assert abs(t - by["chunk_out"]) <= 0.01 * by["chunk_out"]
