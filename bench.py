@@ -77,11 +77,12 @@ def backward_bytes(w):
     return reads + writes
 
 
-# Sources of the chunk-output kernel; the HBM traffic measured with rocprofv3 counters
-# is reported only while they are unchanged since the counters were taken.
+# Sources of the chunk-output kernel (and of the segment plan, which sets how many
+# segment-entering states it reads); the HBM traffic measured with rocprofv3 counters is
+# reported only while they are unchanged since the counters were taken.
 CHUNK_OUT_SOURCES = ("chunk_out.h", "k_chunk_out.cpp", "k_chunk_out_bf16.hip",
                      "k_chunk_out_bf16_f32.hip", "k_chunk_out_f32.hip",
-                     "k_chunk_out_bf16_seg.hip", "ssd_device.h")
+                     "k_chunk_out_bf16_seg.hip", "k_state_seg_bf16.hip", "ssd_device.h")
 
 
 def sources_sha256(names):

@@ -8,29 +8,58 @@ namespace {
 
 constexpr int kSegHeads[] = {1, 2, 3, 4, 5, 6, 8};  // instantiated heads per workgroup
 
-// Tokens per step: the whole chunk, or 128-token sub-blocks where the chunk's B rows
-// (dstate 256) would not fit in LDS next to the x buffers.
-template <int S, int T> constexpr int seg_tb() { return S >= 256 && T > 128 ? 128 : T; }
-template <int P, int S, int T> using SegCfgFor = SegCfg<P, S, T, seg_tb<S, T>()>;
+// The kernel form for a shape: 4 waves and sub-blocks of at most 128 tokens, two
+// workgroups per CU, where that LDS plan fits in half a CU (80 KB); otherwise 8 waves,
+// one workgroup per CU, with the whole chunk per step or 128-token sub-blocks where the
+// chunk's B rows (dstate 256) would not fit in LDS next to the x buffers.
+template <int P, int S, int T>
+struct SegPick {
+    static constexpr int TB4 = T > 128 ? 128 : T;
+    using Cfg4 = SegCfg<P, S, T, TB4, 4>;
+    // (and whose running state takes at most 32 registers per lane and head, so that two
+    // workgroups' waves fit the register file)
+    static constexpr bool DUAL = Cfg4::FITS && Cfg4::LDS_BYTES <= 81920 && P * S <= 64 * 128;
+    static constexpr int NW = DUAL ? 4 : 8;
+    static constexpr int TB = DUAL ? TB4 : (S >= 256 && T > 128 ? 128 : T);
+    using Cfg = SegCfg<P, S, T, TB, NW>;
+    static constexpr int SLOTS = DUAL ? 512 : 256;  // workgroups resident on 256 CUs
+    // running-state registers per lane the plan allows: no spills, and with 4 waves at
+    // most 256 registers per wave so that two workgroups stay resident (at 128-token
+    // chunks and dstate 64 three or four heads' x buffers take more, so 32 there)
+    static constexpr int MAX_STATE_REGS = DUAL ? (S == 64 && T == 128 ? 32 : 64) : 80;
+    // with sub-blocks, one weight slot per head and chunk parity
+    static constexpr int MAX_HEADS = Cfg::NSUB > 1 ? Cfg::NWS / 2 : 8;
+};
+template <int P, int S, int T> using SegCfgFor = typename SegPick<P, S, T>::Cfg;
 
-bool seg_shape_fits(int P, int S, int T) {
+// Whether the shape has a kernel form; its workgroup slots per round, state-register and
+// head limits.
+struct SegForm {
+    bool fits;
+    int slots, max_state_regs, max_heads, nthr;
+};
+SegForm seg_form(int P, int S, int T) {
     switch (P * 1000000 + S * 1000 + T) {
-#define SSD_SEG_FITS(p, s, t) \
-    case p * 1000000 + s * 1000 + t: return SegCfgFor<p, s, t>::FITS;
+#define SSD_SEG_FITS(p, s, t)                                                              \
+    case p * 1000000 + s * 1000 + t:                                                       \
+        return SegForm{SegCfgFor<p, s, t>::FITS, SegPick<p, s, t>::SLOTS,                  \
+                       SegPick<p, s, t>::MAX_STATE_REGS, SegPick<p, s, t>::MAX_HEADS,      \
+                       SegCfgFor<p, s, t>::NTHR};
         SSD_SEG_FITS(64, 64, 64) SSD_SEG_FITS(64, 64, 128) SSD_SEG_FITS(64, 64, 256)
         SSD_SEG_FITS(64, 128, 64) SSD_SEG_FITS(64, 128, 128) SSD_SEG_FITS(64, 128, 256)
         SSD_SEG_FITS(64, 256, 64) SSD_SEG_FITS(64, 256, 128) SSD_SEG_FITS(64, 256, 256)
 #undef SSD_SEG_FITS
     }
-    return false;
+    return SegForm{false, 0, 0, 0, 0};
 }
 
 template <int P, int S, int T, int NH>
 hipError_t run_seg(const void* x, const void* Bm, const float* A, const float* G,
                    const float* dt_t, const float* h0, void* states, const SegPlan& pl,
                    const SegBuffers& sb, const Dims& d, hipStream_t stream) {
-    using Cfg = SegCfgFor<P, S, T>;
-    auto kern = state_seg_kernel<P, S, T, seg_tb<S, T>(), NH>;
+    using Pick = SegPick<P, S, T>;
+    using Cfg = typename Pick::Cfg;
+    auto kern = state_seg_kernel<P, S, T, Pick::TB, Pick::NW, NH>;
     if (Cfg::LDS_BYTES > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -48,17 +77,21 @@ template <int P, int S, int T>
 hipError_t seg_by_nh(const void* x, const void* Bm, const float* A, const float* G,
                      const float* dt_t, const float* h0, void* st, const SegPlan& pl,
                      const SegBuffers& sb, const Dims& d, hipStream_t s) {
-    if constexpr (!SegCfgFor<P, S, T>::FITS) {
+    using Pick = SegPick<P, S, T>;
+    if constexpr (!Pick::Cfg::FITS) {
         return hipErrorInvalidValue;
     } else {
+        // head counts the plan can choose for this form (others are not instantiated)
+        constexpr int RPH = P * S / Pick::Cfg::NTHR;  // state registers per head and lane
         switch (pl.heads) {
-            case 1: return run_seg<P, S, T, 1>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
-            case 2: return run_seg<P, S, T, 2>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
-            case 3: return run_seg<P, S, T, 3>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
-            case 4: return run_seg<P, S, T, 4>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
-            case 5: return run_seg<P, S, T, 5>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
-            case 6: return run_seg<P, S, T, 6>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
-            case 8: return run_seg<P, S, T, 8>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);
+#define SSD_SEG_NH(n)                                                                          \
+    case n:                                                                                    \
+        if constexpr (n <= Pick::MAX_HEADS && n * RPH <= Pick::MAX_STATE_REGS)                 \
+            return run_seg<P, S, T, n>(x, Bm, A, G, dt_t, h0, st, pl, sb, d, s);               \
+        break;
+            SSD_SEG_NH(1) SSD_SEG_NH(2) SSD_SEG_NH(3) SSD_SEG_NH(4) SSD_SEG_NH(5) SSD_SEG_NH(6)
+            SSD_SEG_NH(8)
+#undef SSD_SEG_NH
         }
         return hipErrorInvalidValue;
     }
@@ -82,28 +115,32 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Plan: heads per workgroup (a divisor of the heads per group whose running states fit
 // in registers) and chunks per segment (at least 2 unless the sequence has one
-// chunk). A workgroup holds one compute unit (its LDS plan takes most of the 160 KB), so
-// the grid runs in rounds of 256; the cost of a plan is its rounds times one workgroup's
+// chunk). Workgroups are resident one or two per CU (the form's LDS plan), so the grid
+// runs in rounds of 256 or 512; the cost of a plan is its rounds times one workgroup's
 // work, counted in (chunk, head) steps plus a fixed share per workgroup, per chunk (B rows,
 // one more barrier) and per head (its end state). Ties go to longer segments (fewer
 // corrections downstream).
 bool state_seg_plan(int in_dtype, int states_dtype, const Dims& d, SegPlan* out) {
     if (in_dtype != kBF16 || states_dtype != kBF16) return false;
-    if (!seg_shape_fits(d.headdim, d.dstate, d.chunk)) return false;
+    const SegForm f = seg_form(d.headdim, d.dstate, d.chunk);
+    if (!f.fits) return false;
     const int nC = d.nchunks();
     if (nC < 1) return false;
     const int hpg = d.nheads / d.ngroups;
-    const int regs_per_head = d.headdim * d.dstate / 512;
+    const int regs_per_head = d.headdim * d.dstate / f.nthr;
     double best = 1e300;
     SegPlan bp{0, 0, 0};
     for (int nh : kSegHeads) {
-        // register budget of the two-step prefetch: at most 80 state registers per lane,
-        // and eight heads only with chunks shorter than 256 tokens (no spills)
-        if (hpg % nh != 0 || nh * regs_per_head > 80 || (nh == 8 && d.chunk == 256)) continue;
+        // register budget of the two-step prefetch (no spills): the form's state-register
+        // limit per lane, its weight slots, and, with 8 waves, eight heads only with
+        // chunks shorter than 256 tokens
+        if (hpg % nh != 0 || nh * regs_per_head > f.max_state_regs || nh > f.max_heads ||
+            (f.slots == 256 && nh == 8 && d.chunk == 256))
+            continue;
         for (int k = (nC == 1 ? 1 : 2); k <= nC; ++k) {
             const int nseg = (nC + k - 1) / k;
             const long wgs = (long)d.batch * nseg * (d.nheads / nh);
-            const long rounds = (wgs + 255) / 256;
+            const long rounds = (wgs + f.slots - 1) / f.slots;
             const double cost = (double)rounds * (nh * k + 1.0 + 0.5 * k + 0.7 * nh);
             if (cost < best - 1e-9 || (cost < best + 1e-9 && k > bp.chunks)) {
                 best = cost;

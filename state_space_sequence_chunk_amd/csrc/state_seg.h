@@ -17,8 +17,8 @@
 // across segments (and gives the final state), and the output kernel adds 2^{D_c} S_in(k)
 // while staging each chunk's state. The per-chunk increments never go to HBM.
 //
-// gfx950 mapping: one workgroup of 8 waves per (batch, segment, block of NH heads of one
-// B group). Each head's running state (P x S fp32) is spread over the waves in the MFMA
+// gfx950 mapping: one workgroup of 8 waves (one per CU), or of 4 waves (two per CU) where
+// its LDS plan fits in half a CU, per (batch, segment, block of NH heads of one B group). Each head's running state (P x S fp32) is spread over the waves in the MFMA
 // accumulator layout and stays in registers for the whole segment. A step is one (chunk,
 // sub-block of TB tokens, head); TB is the whole chunk unless the chunk's B rows would not
 // fit in LDS (dstate 256 with 256-token chunks: TB = 128). Per sub-block the group's B
@@ -56,11 +56,13 @@ template <int B, int E> struct StaticFor {
     }
 };
 
-// TB: tokens per step (a sub-block of the chunk; TB = T unless the chunk's B rows would not
-// fit in LDS next to the x buffers).
-template <int P, int S, int T, int TB>
+// TB: tokens per step (a sub-block of the chunk). NW: waves per workgroup, 8 (one
+// workgroup per CU) or 4 (two per CU when the LDS plan takes at most half the CU's 160 KB:
+// two independent workgroups do not run in step, so one's VALU and LDS work overlaps the
+// other's products).
+template <int P, int S, int T, int TB, int NW = 8>
 struct SegCfg {
-    static constexpr int NTHR = 512, NWAVE = 8;
+    static constexpr int NTHR = 64 * NW, NWAVE = NW;
     static constexpr int NSUB = T / TB;  // sub-blocks per chunk
     static constexpr int NPT = P / 16, NST = S / 16;
     static constexpr int WPT = NPT >= NWAVE ? 1 : NWAVE / NPT;  // waves per p-tile
@@ -74,9 +76,9 @@ struct SegCfg {
     static constexpr size_t W_BYTES = (size_t)T * sizeof(float);  // one chunk's weights
     static constexpr size_t B_BYTES = (size_t)TB * BS * sizeof(bf16);
     // weight slots: one per x buffer when a step is a whole chunk; otherwise one per head
-    // of the block (up to 8) and chunk parity, since a head's weights serve all its
-    // sub-blocks
-    static constexpr int NWS = NSUB == 1 ? 2 : 16;
+    // of the block (up to 8 heads with 8 waves, 2 with 4) and chunk parity, since a head's
+    // weights serve all its sub-blocks
+    static constexpr int NWS = NSUB == 1 ? 2 : (NW == 4 ? 4 : 16);
     static constexpr size_t LDS_BYTES = B_BYTES + 2 * X_BYTES + NWS * W_BYTES;
     // registers per head for the running state (fp32 per lane)
     static constexpr int STATE_REGS = MST * 4;
@@ -84,13 +86,13 @@ struct SegCfg {
                                  T % TB == 0 && TB % 32 == 0;
 };
 
-template <int P, int S, int T, int TB, int NH>
-__global__ __launch_bounds__(512) void state_seg_kernel(
+template <int P, int S, int T, int TB, int NW, int NH>
+__global__ __launch_bounds__(64 * NW) void state_seg_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ A,
     const float* __restrict__ G, const float* __restrict__ dt_t, const float* __restrict__ h0,
     bf16* __restrict__ states, float* __restrict__ seg_end, float* __restrict__ dec_in,
     float* __restrict__ dec_seg, int L, int H, int ngroups, int K) {
-    using Cfg = SegCfg<P, S, T, TB>;
+    using Cfg = SegCfg<P, S, T, TB, NW>;
     constexpr int VE = Cfg::VE, XS = Cfg::XS, BS = Cfg::BS, NTHR = Cfg::NTHR, PER = Cfg::PER;
     constexpr int MST = Cfg::MST, WPT = Cfg::WPT, NSUB = Cfg::NSUB;
     constexpr int SPC = NSUB * NH;  // steps per chunk

@@ -94,9 +94,10 @@ def test_workspace_sizes():
 
 
 def test_segment_plan_query():
-    # the 2.7B layer: 5 heads per workgroup, 8 chunks per segment, 8 segments (256 workgroups)
+    # the 2.7B layer: 2 heads per workgroup, 11 chunks per segment, 6 segments (480
+    # 4-wave workgroups, two per CU)
     s = ssd.make_shape(2, 16384, 80, 64, 128, 1, 256, ssd.SSD_BF16)
-    assert ssd.state_seg_plan(s) == (5, 8, 8)
+    assert ssd.state_seg_plan(s) == (2, 11, 6)
     # the long layer at dstate 256: 2 heads x 43 chunks, 6 segments (240 workgroups)
     assert ssd.state_seg_plan(ssd.make_shape(1, 65536, 80, 64, 256, 8, 256, ssd.SSD_BF16)) == (2, 43, 6)
     lib = ssd.load_library()

@@ -2,8 +2,8 @@
 for bf16 inputs with bf16 states at headdim 64, dstate 64, 128 or 256) against the fp64
 oracle on the GPU.
 
-The shapes are chosen so that the library's segment plan differs between them: 1 to 8
-heads per workgroup, 2 to 16 chunks per segment, a short last segment, a partial last
+The shapes are chosen so that the library's segment plan differs between them: 1 to 4
+heads per workgroup, 2 to 11 chunks per segment, both workgroup forms, a short last segment, a partial last
 chunk, a single partial chunk, groups, with and without h0. Every element of y and of the
 final state is compared."""
 import numpy as np
@@ -22,34 +22,37 @@ def _w(name, batch, seqlen, nheads, ngroups, dstate, chunk, h0, seed):
     return gen.Workload(name, batch, seqlen, nheads, 64, dstate, ngroups, chunk, "bf16", h0, seed)
 
 
-# (plan the library picks for the shape: heads per workgroup x chunks per segment, segments)
+# (plan the library picks for the shape: heads per workgroup x chunks per segment, segments;
+# dstate 64 and 128 run 4-wave workgroups two per CU, dstate 256 8-wave ones)
 CASES = {
     # 1 x 2, 8 segments; the last chunk holds 160 of 256 tokens
     "ragged-1x2": _w("ragged-1x2", 1, 4000, 10, 1, 128, 256, True, 11),
-    # 1 x 3, 8 segments; chunk 128, two groups, partial last chunk
-    "groups-1x3": _w("groups-1x3", 2, 3000, 12, 2, 128, 128, True, 12),
-    # 2 x 2, 64 segments; chunk 64
-    "t64-2x2": _w("t64-2x2", 1, 8192, 8, 1, 128, 64, False, 13),
-    # 3 x 3, 7 segments, the last of 2 chunks; dstate 64; partial last chunk
-    "short-seg-3x3": _w("short-seg-3x3", 3, 5000, 36, 1, 64, 256, False, 14),
-    # 4 x 4, 8 segments
-    "nh4-4x4": _w("nh4-4x4", 4, 8192, 32, 1, 128, 256, False, 15),
-    # 5 x 8, 4 segments; dstate 64, chunk 128
-    "nh5-5x8": _w("nh5-5x8", 8, 4096, 40, 1, 64, 128, True, 16),
-    # 6 x 8, 8 segments; four groups, dstate 64, chunk 64
-    "nh6-6x8": _w("nh6-6x8", 4, 4096, 48, 4, 64, 64, True, 17),
-    # 8 x 8, 8 segments; dstate 64, chunk 64
-    "nh8-8x8": _w("nh8-8x8", 2, 4096, 128, 1, 64, 64, False, 19),
-    # 3 x 16, one segment; four groups
-    "one-seg-3x16": _w("one-seg-3x16", 16, 2048, 48, 4, 128, 128, True, 20),
+    # 1 x 2, 12 segments; chunk 128, two groups, partial last chunk
+    "groups-1x2": _w("groups-1x2", 2, 3000, 12, 2, 128, 128, True, 12),
+    # 1 x 2, 64 segments; chunk 64
+    "t64-1x2": _w("t64-1x2", 1, 8192, 8, 1, 128, 64, False, 13),
+    # 1 x 5, 4 segments; dstate 64; partial last chunk
+    "s64-1x5": _w("s64-1x5", 3, 5000, 36, 1, 64, 256, False, 14),
+    # 2 x 4, 8 segments
+    "nh2-2x4": _w("nh2-2x4", 4, 8192, 32, 1, 128, 256, False, 15),
+    # 2 x 11, 3 segments, the last of 10 chunks; dstate 64, chunk 128
+    "short-seg-2x11": _w("short-seg-2x11", 8, 4096, 40, 1, 64, 128, True, 16),
+    # 3 x 8, 8 segments; four groups, dstate 64, chunk 64
+    "nh3-3x8": _w("nh3-3x8", 4, 4096, 48, 4, 64, 64, True, 17),
+    # 4 x 8, 8 segments; dstate 64, chunk 64
+    "nh4-4x8": _w("nh4-4x8", 2, 4096, 128, 1, 64, 64, False, 19),
+    # 2 x 4, 4 segments; four groups, chunk 128
+    "groups4-2x4": _w("groups4-2x4", 16, 2048, 48, 4, 128, 128, True, 20),
+    # 1 x 2, one segment of two chunks; two groups
+    "one-seg": _w("one-seg", 2, 512, 8, 2, 128, 256, True, 25),
     # one partial chunk: one segment
     "one-chunk": _w("one-chunk", 1, 200, 4, 1, 128, 256, True, 18),
-    # dstate 256 (the long-context layer's per-head shape): 2 x 3 with two 128-token
-    # sub-blocks per chunk; four groups
+    # dstate 256 (the long-context layer's per-head shape), 8-wave workgroups: 2 x 3 with
+    # two 128-token sub-blocks per chunk; four groups
     "s256-2x3": _w("s256-2x3", 2, 4096, 40, 4, 256, 256, True, 21),
     # dstate 256, 1 x 2, sub-blocks, partial last chunk, no h0
     "s256-ragged-1x2": _w("s256-ragged-1x2", 1, 4000, 20, 2, 256, 256, False, 22),
-    # dstate 256 at chunk 128 (one step per chunk and head) and chunk 64
+    # dstate 256 at chunk 128 (one step per chunk and head) and chunk 64 (4-wave form)
     "s256-t128-1x3": _w("s256-t128-1x3", 2, 2048, 20, 2, 256, 128, True, 23),
     "s256-t64-1x2": _w("s256-t64-1x2", 1, 3000, 10, 1, 256, 64, True, 24),
 }
@@ -78,7 +81,7 @@ def test_forward_segmented_all_elements(name):
     assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("name", ["ragged-1x2", "short-seg-3x3", "nh6-6x8", "s256-2x3"])
+@pytest.mark.parametrize("name", ["ragged-1x2", "short-seg-2x11", "nh3-3x8", "s256-2x3"])
 def test_forward_segmented_ssm_only(name):
     """D = 0: the state path alone, where the skip term cannot hide an error."""
     w = CASES[name]
@@ -94,7 +97,7 @@ def test_forward_segmented_ssm_only(name):
 def test_staged_segmented_equals_forward():
     """cumsum -> ssd_state_seg -> ssd_chunk_out_seg gives ssd_forward's y and final state
     bit for bit (the same kernels in the same order)."""
-    w = CASES["nh5-5x8"]
+    w = CASES["short-seg-2x11"]
     cpu, d = make(w)
     y1, f1 = _forward(w, d)
     sh = ssd.shape_of(d["x"], d["B"], w.chunk)
