@@ -264,9 +264,9 @@ __global__ __launch_bounds__(64 * NW) void state_seg_kernel(
         const int c = c_first + ci, h = h_first + hh;
         const bool next = ci + dc1 < nck;  // a next step in this segment
         const float gl = gls[q];  // this step's chunk decay, before set q is reloaded
-        // Every step issues the same memory operations (past the segment's end they repeat
-        // its last chunk and are never used), so the compiler's wait before each use counts
-        // exactly the operations issued since, and the loads two steps ahead stay in flight.
+        // Every step issues its loads unconditionally (past the segment's end they repeat its
+        // last chunk and are never used), so no wait before a use depends on a runtime branch
+        // and the loads two steps ahead stay in flight.
         load_head(q_c, min(c + dc2, c_first + nck - 1), u2 / NH, h_first + u2 % NH);
         if constexpr (hh == NH - 1) {  // the next sub-block's B rows
             if constexpr (sub + 1 < NSUB) load_b(c, sub + 1);
