@@ -138,7 +138,8 @@ def cpu_baseline(w, cpu, budget_s=15.0):
     k = max(k_cal, min(w.nheads, (k // hpg) * hpg))
     dt = run(subset(k)) if k != k_cal else t_cal
     value = (k / w.nheads) * w.tokens / dt
-    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": value, "unit": "tokens/s", "cores": cores, "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"heads 0..{k - 1} of {w.nheads} (all {w.batch} batch rows, all "
                       f"{w.seqlen} tokens) in {dt:.2f} s wall; fp64 token recurrence on "
                       f"{cores} threads, scaled to the whole workload's tokens"}
@@ -159,6 +160,47 @@ def measure_copy_bandwidth(torch, nbytes=1 << 30, reps=10):
     ms = e0.elapsed_time(e1) / reps
     del src, dst
     return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
+def measure_hbm_ceiling(torch, ssd, stream, nbytes=1 << 30, reps=10, workgroups=0):
+    """The library's own stream kernels (include/ssd_probe.h) over 1 GiB buffers, four
+    times the 256 MB Infinity Cache: read-only, write-only and copy, with ordinary and
+    non-temporal accesses, timed with HIP events on the launch stream. GB/s of DRAM
+    traffic (a copy counts its read and its write)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for mode, tag in ((0, "plain"), (1, "nontemporal")):
+        kw = dict(mode=mode, workgroups=workgroups, stream=stream)
+        calls = {"read": (lambda: ssd.probe_read(src, sink, **kw), 1),
+                 "write": (lambda: ssd.probe_write(dst, **kw), 1),
+                 "copy": (lambda: ssd.probe_copy(src, dst, **kw), 2)}
+        for kind, (fn, k) in calls.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[f"{kind}_{tag}"] = k * nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    for kind in ("read", "write", "copy"):
+        out[kind] = max(out[f"{kind}_plain"], out[f"{kind}_nontemporal"])
+    del src, dst, sink
+    return {"unit": "GB/s", "bytes": nbytes, **out}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def time_decode(torch, ssd, d, state, stream, steps=32, replays=8):
@@ -301,6 +343,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--min-warmup-s", type=float, default=1.0,
+                    help="keep warming up until this much device time has passed, whatever "
+                         "--warmup says (clocks settle during the first dispatches)")
     ap.add_argument("--workload", default="2.7b-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -308,6 +353,8 @@ def main():
                          "used to calibrate the HBM byte counters")
     ap.add_argument("--sources-sha256", action="store_true",
                     help="print the hash of the chunk-output kernel sources and exit")
+    ap.add_argument("--hbm-sweep", action="store_true",
+                    help="only run the HBM stream probes over several grid sizes")
     ap.add_argument("--state-pass-sweep", action="store_true",
                     help="only time the two state-pass kernels over layers of growing batch")
     args = ap.parse_args()
@@ -337,7 +384,14 @@ def main():
     if args.state_pass_sweep:
         state_pass_sweep(torch, ssd, gen)
         return
+    if args.hbm_sweep:
+        for wg in (256, 512, 1024, 2048, 4096, 8192, 16384):
+            r = measure_hbm_ceiling(torch, ssd, torch.cuda.current_stream(), workgroups=wg)
+            print(json.dumps({"workgroups": wg, **{k: round(v, 1) if isinstance(v, float) else v
+                                                   for k, v in r.items()}}), flush=True)
+        return
     copy_gbps = measure_copy_bandwidth(torch)
+    hbm_ceiling = measure_hbm_ceiling(torch, ssd, torch.cuda.current_stream())
     w = gen.WORKLOADS[args.workload]
     cpu = gen.make_inputs(w)
     d = {k: (None if v is None else v.cuda().contiguous()) for k, v in cpu.items()}
@@ -386,10 +440,18 @@ def main():
     def forward_step():
         fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], stream)
 
-    for _ in range(args.warmup):
+    # warm-up: at least --warmup steps and at least --min-warmup-s seconds (synchronised
+    # every few steps, so the time counted is the device's)
+    t_w0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w0 < args.min_warmup_s:
         forward_step()
         step()
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warmup_run = {"steps": n_warm, "s": round(time.perf_counter() - t_w0, 3)}
 
     # timed region: K one-call forward steps
     K = args.steps
@@ -482,6 +544,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_run": warmup_run,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -494,6 +557,7 @@ def main():
         "ms_per_step_staged": ms_staged,
         "variants": variants,
         "copy_GBps": copy_gbps,
+        "hbm_ceiling": hbm_ceiling,
         "wall_ms_per_step": wall / K * 1e3,
     }
     if not args.no_cpu_baseline:

@@ -22,7 +22,7 @@ SOURCES = ["ssd_api.cpp", "k_cumsum.hip", "k_chunk_state.hip", "k_chunk_state_mh
            "k_state_scan_bf16.hip", "k_state_scan_bf16_f32.hip", "k_state_seg_bf16.hip", "k_decode.hip",
            "k_backward.hip", "k_backward_bf16.hip", "k_backward_f32.hip", "k_backward_mfma.hip",
            "k_chunk_out.cpp", "k_chunk_out_bf16.hip", "k_chunk_out_bf16_f32.hip", "k_chunk_out_bf16_ybf16.hip",
-           "k_chunk_out_f32.hip", "k_chunk_out_bf16_seg.hip"]
+           "k_chunk_out_f32.hip", "k_chunk_out_bf16_seg.hip", "k_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -46,6 +46,15 @@ def _compile(src: str, extra) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    if src.endswith(".hip"):
+        # the gfx950 assembly of the same source, for the instruction-level checks of the
+        # test suite (tests/test_kernel_asm.py)
+        asm = os.path.join(OBJ, os.path.basename(src) + ".s")
+        cmd_s = [hipcc()] + common_flags() + list(extra) + lang + [
+            "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
+        rs = subprocess.run(cmd_s, capture_output=True, text=True)
+        if rs.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed for {src}:\n{rs.stdout}\n{rs.stderr}")
     if r.stderr.strip():
         # keep the compiler's warnings visible, minus hipcc's note that the host pass does
         # not know the device-only feature flag

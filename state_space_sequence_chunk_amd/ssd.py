@@ -25,6 +25,8 @@ EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_byt
            "ssd_state_scan", "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
            "ssd_backward", "ssd_state_seg_workspace_bytes", "ssd_state_seg", "ssd_chunk_out_seg",
            "ssd_state_seg_plan")
+# HBM stream probes declared in include/ssd_probe.h (measurement only).
+PROBE_EXPORTS = ("ssd_probe_read", "ssd_probe_write", "ssd_probe_copy")
 
 
 class SSDError(RuntimeError):
@@ -76,7 +78,10 @@ def load_library():
     lib.ssd_chunk_out_seg.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.ssd_state_seg_plan.argtypes = [sp, i32p, i32p, i32p]
-    for name in EXPORTS[1:]:
+    lib.ssd_probe_read.argtypes = [vp, sz, vp, i32, i32, vp]
+    lib.ssd_probe_write.argtypes = [vp, sz, i32, i32, vp]
+    lib.ssd_probe_copy.argtypes = [vp, vp, sz, i32, i32, vp]
+    for name in EXPORTS[1:] + PROBE_EXPORTS:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -216,6 +221,24 @@ def ssd_decode_step(shape, x, dt, A, B, C, D, state, y, stream=None):
     _check(load_library().ssd_decode_step(ctypes.byref(shape), _p(x), _p(dt), _p(A), _p(B),
                                           _p(C), _p(D), _p(state), _p(y), _stream(stream)),
            "ssd_decode_step")
+
+
+def probe_read(src, sink, *, mode=0, workgroups=0, stream=None):
+    """Stream `src` (a contiguous device tensor) through a read-only kernel."""
+    _check(load_library().ssd_probe_read(_p(src), src.numel() * src.element_size(), _p(sink),
+                                         mode, workgroups, _stream(stream)), "ssd_probe_read")
+
+
+def probe_write(dst, *, mode=0, workgroups=0, stream=None):
+    _check(load_library().ssd_probe_write(_p(dst), dst.numel() * dst.element_size(), mode,
+                                          workgroups, _stream(stream)), "ssd_probe_write")
+
+
+def probe_copy(src, dst, *, mode=0, workgroups=0, stream=None):
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("probe_copy: src and dst sizes differ")
+    _check(load_library().ssd_probe_copy(_p(src), _p(dst), src.numel() * src.element_size(),
+                                         mode, workgroups, _stream(stream)), "ssd_probe_copy")
 
 
 def decode_step(x, dt, A, B, C, D, state, *, stream=None):

@@ -10,15 +10,19 @@ from state_space_sequence_chunk_amd import ssd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssd.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(ssd.LIB_PATH),
                                 reason="HIP library not built (run __graft_entry__.build())")
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+def declared_functions(paths=(HEADER,)):
+    names = set()
+    for path in paths:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_four_stages():
@@ -29,11 +33,12 @@ def test_header_declares_the_four_stages():
 
 def test_library_exports_every_declared_symbol():
     lib = ssd.load_library()
-    names = declared_functions()
+    names = declared_functions(HEADERS)
     assert names, "no declarations parsed"
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
-    assert sorted(ssd.EXPORTS) == names
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert sorted(ssd.EXPORTS + ssd.PROBE_EXPORTS) == names
+    assert sorted(ssd.EXPORTS) == declared_functions()
 
 
 def test_shape_struct_matches_header():
@@ -361,3 +366,19 @@ def test_backward_chunk_stays_within_size_limits():
     # four times the chunk states
     s16 = shape(batch=1, seqlen=L, nheads=16, ngroups=1, headdim=64, dstate=256, chunk=256)
     assert ssd.backward_workspace_bytes(s16) > 2 * 16 * (L // 64) * 64 * 256 * 4
+
+
+# --- HBM stream probes (include/ssd_probe.h): host-side validation only ---------------------
+@pytest.mark.parametrize("call,code", [
+    (lambda L: L.ssd_probe_read(None, 1024, 4096, 0, 0, None), 1),
+    (lambda L: L.ssd_probe_read(4096, 0, 8192, 0, 0, None), 2),
+    (lambda L: L.ssd_probe_read(4096, 1000, 8192, 0, 0, None), 2),
+    (lambda L: L.ssd_probe_read(4100, 1024, 8192, 0, 0, None), 6),
+    (lambda L: L.ssd_probe_read(4096, 1024, 8192, 2, 0, None), 4),
+    (lambda L: L.ssd_probe_write(None, 1024, 0, 0, None), 1),
+    (lambda L: L.ssd_probe_write(4096, 1024, 0, -1, None), 2),
+    (lambda L: L.ssd_probe_copy(4096, 8200, 1024, 0, 0, None), 6),
+    (lambda L: L.ssd_probe_copy(4096, 8192, 1024, 5, 0, None), 4),
+])
+def test_probe_argument_checks(call, code):
+    assert call(ssd.load_library()) == code
