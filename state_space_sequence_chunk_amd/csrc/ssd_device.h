@@ -125,6 +125,17 @@ __device__ __forceinline__ void buf_store_f32(float v, BufRsrc r, uint32_t voff,
 
 // 16-byte vector type for cooperative global<->LDS copies.
 typedef uint32_t Vec16 __attribute__((ext_vector_type(4)));
+
+// 16-byte buffer store with the whole byte offset in the per-lane offset and a constant 0
+// in the uniform (SGPR) offset field. A store of more than 8 bytes reads its data
+// registers after issue, so they must not be rewritten for two wait states. The compiler
+// inserts those wait states only when the uniform offset is not a register; with a
+// register there it let the next VALU or MFMA instruction overwrite the data registers
+// at once, and on gfx950 that corrupted what the store wrote (seen in the segmented state
+// kernel's recorded states). Keeping the uniform offset 0 keeps the wait states.
+__device__ __forceinline__ void buf_store16(Vec16 v, BufRsrc r, uint32_t voff) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0u, 0);
+}
 __device__ __forceinline__ Vec16 buf_load16(BufRsrc r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }

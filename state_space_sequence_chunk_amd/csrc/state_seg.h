@@ -137,7 +137,6 @@ __global__ __launch_bounds__(64 * NW) void state_seg_kernel(
 
     const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
     const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
-    const BufRsrc rdec = make_rsrc(dec_in + (size_t)b * H * nC, (uint32_t)((size_t)H * nC * sizeof(float)));
     auto rows_of = [&](int c) { return min(T, L - c * T); };
     // x rows past a chunk's real tokens lie outside its descriptor and load as zeros
     auto x_rsrc = [&](int c) {
@@ -301,12 +300,9 @@ __global__ __launch_bounds__(64 * NW) void state_seg_kernel(
                 recv[1] = (uint32_t)__shfl_xor((int)send[1], 16);
                 const u32x2 first = odd_g4 ? recv : a, second = odd_g4 ? a1 : recv;
                 const Vec16 out = Vec16{first[0], first[1], second[0], second[1]};
-                __builtin_amdgcn_raw_buffer_store_b128(out, rst, st_off,
-                                                       (uint32_t)(m * 16 * sizeof(bf16)), 0);
+                buf_store16(out, rst, st_off + (uint32_t)(m * 16 * sizeof(bf16)));
             }
-            // dec_in[b, h, c] from thread 0; the other lanes' offsets are out of range (dropped)
-            buf_store_f32(dacc[hh], rdec, tid == 0 ? (uint32_t)(((size_t)h * nC + c) * 4) : 0x80000000u,
-                          0u);
+            if (tid == 0) dec_in[((size_t)b * H + h) * nC + c] = dacc[hh];
             dacc[hh] += gl;
             const float dec = exp2_fast(gl);
     #pragma unroll
