@@ -63,3 +63,52 @@ def oracle_forward(cpu: dict, *, D="given", emit_every=None):
 
 def np64(t):
     return t.detach().double().cpu().numpy()
+
+
+def _blocks(H: int, G: int, heads: int):
+    """Head ranges [h0, h1) of at most ``heads`` heads that keep whole B/C groups (with
+    one group, any range does)."""
+    hpg = H // G
+    if G > 1:
+        heads = max(hpg, heads // hpg * hpg)
+    return [(h0, min(H, h0 + heads)) for h0 in range(0, H, heads)]
+
+
+def full_errors(y, fin, cpu: dict, *, D="given", heads: int = 16):
+    """Every element of y [b, L, h, P] and of the final state [b, h, P, S] (GPU tensors)
+    against the fp64 oracle, which runs on blocks of heads so that host memory stays
+    bounded. Returns max|got - ref| / rms(ref) of y and of the final state, and the
+    rms-relative error of y, each over the whole tensor."""
+    H = cpu["A"].shape[0]
+    G = cpu["B"].shape[2]
+    hpg = H // G
+    Dv = cpu["D"] if D == "given" else D
+    acc = {"y_max": 0.0, "y_ref2": 0.0, "y_err2": 0.0, "y_n": 0,
+           "f_max": 0.0, "f_ref2": 0.0, "f_n": 0}
+    for h0, h1 in _blocks(H, G, heads):
+        g0, g1 = h0 // hpg, (h1 - 1) // hpg + 1
+        ref = oracle.forward(cpu["x"][:, :, h0:h1], cpu["dt"][:, :, h0:h1], cpu["A"][h0:h1],
+                             cpu["B"][:, :, g0:g1], cpu["C"][:, :, g0:g1],
+                             None if Dv is None else Dv[h0:h1],
+                             None if cpu["h0"] is None else cpu["h0"][:, h0:h1])
+        gy = np64(y[:, :, h0:h1])
+        e = gy - ref["y"]
+        acc["y_max"] = max(acc["y_max"], float(np.max(np.abs(e))))
+        acc["y_ref2"] += float(np.sum(ref["y"] * ref["y"]))
+        acc["y_err2"] += float(np.sum(e * e))
+        acc["y_n"] += e.size
+        if not np.isfinite(gy).all():
+            acc["y_max"] = float("inf")
+        del gy, e
+        gf = np64(fin[:, h0:h1])
+        ef = gf - ref["final"]
+        acc["f_max"] = max(acc["f_max"], float(np.max(np.abs(ef))))
+        acc["f_ref2"] += float(np.sum(ref["final"] * ref["final"]))
+        acc["f_n"] += ef.size
+        del ref, gf, ef
+    y_rms = (acc["y_ref2"] / acc["y_n"]) ** 0.5
+    f_rms = (acc["f_ref2"] / acc["f_n"]) ** 0.5
+    return {"y": acc["y_max"] / y_rms,
+            "y_rms_rel": (acc["y_err2"] / acc["y_n"]) ** 0.5 / y_rms,
+            "final": acc["f_max"] / f_rms if f_rms > 0 else (0.0 if acc["f_max"] == 0 else
+                                                             float("inf"))}

@@ -1,0 +1,134 @@
+"""Whole-output parity at full size, and the decay-free and frozen-state limits, on the GPU.
+
+Every element of y and of the final state of the three layer-shaped workloads, launched
+through ssd_forward as the benchmark launches it, is compared with the fp64 oracle; the
+oracle runs on blocks of heads (whole B/C groups) so that host memory stays bounded. The
+SSM-only output (D = 0) is gated at the same sizes, since y is about 99% D x and the skip
+term would hide an error in the state path. Two limits of the method that the
+"Mamba-2 architecture" section of the article spells out run on both state-pass paths (the segmented
+one taken for bf16 inputs, the two-kernel one for fp32): A = 0, where nothing decays and
+the method is causal linear attention, and dt = 0, where the state stays at h0.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (SSM_MAX_TOL_FP32, SSM_RMS_TOL, TOL, dev, full_errors, gpu_forward,
+                        make, needs_gpu, np64, oracle_forward)
+from metrics import max_rel_rms, rms_rel
+from state_space_sequence_chunk_amd import inputs as gen
+from state_space_sequence_chunk_amd import ssd
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+W = gen.WORKLOADS
+LARGE = ["780m-bf16", "2.7b-bf16", "long-bf16"]
+# heads per oracle block: enough (batch, head) pairs for the host threads, few enough
+# that the block's fp64 output stays under a GB
+BLOCK = {"780m-bf16": 8, "2.7b-bf16": 16, "long-bf16": 20}
+
+
+def _print(msg):
+    print(msg, flush=True)
+
+
+def _plan(w, chunk=None):
+    sh = ssd.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                        chunk or w.chunk, gen.torch_dtype(w.dtype))
+    try:
+        return ssd.state_seg_plan(sh)
+    except ssd.SSDError:
+        return None
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_forward_full_size_every_element(name):
+    w = W[name]
+    _print(f"{name}: full size, every element (segment plan {_plan(w)})")
+    cpu, d = make(w)
+    y, fin = gpu_forward(w, d)
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(fin).all())
+    e = full_errors(y, fin, cpu, heads=BLOCK[name])
+    _print(f"{name}: y max/rms {e['y']:.2e} (rms-rel {e['y_rms_rel']:.2e})  "
+           f"final max/rms {e['final']:.2e}")
+    assert e["y"] <= TOL[w.dtype] and e["final"] <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_forward_full_size_ssm_only(name):
+    """D = 0 at full size: the state path's share of y, every element."""
+    w = W[name]
+    cpu, d = make(w, zero_D=True)
+    y, fin = gpu_forward(w, d, D=None)
+    e = full_errors(y, fin, cpu, D=None, heads=BLOCK[name])
+    _print(f"{name}: SSM-only rms-rel {e['y_rms_rel']:.2e}  max/rms {e['y']:.2e}  "
+           f"final max/rms {e['final']:.2e}")
+    assert e["y_rms_rel"] <= SSM_RMS_TOL[w.dtype]
+    assert e["final"] <= TOL[w.dtype]
+
+
+def test_forward_states_past_32bit_offsets():
+    """The long workload at 64-token chunks: one batch row's bf16 chunk states take 2.7 GB,
+    more than 32-bit byte offsets reach; each head's state has a descriptor of its own.
+    Every element of y and the final state."""
+    w = W["long-bf16"]
+    cpu, d = make(w)
+    y, fin = gpu_forward(w, d, chunk=64)
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(fin).all())
+    e = full_errors(y, fin, cpu, heads=BLOCK["long-bf16"])
+    _print(f"long-bf16 T=64 (plan {_plan(w, 64)}): y max/rms {e['y']:.2e}  "
+           f"final max/rms {e['final']:.2e}")
+    assert e["y"] <= TOL["bf16"] and e["final"] <= TOL["bf16"]
+
+
+# --- limits of the method ----------------------------------------------------------------
+# 16 chunks of 256 tokens: for bf16 inputs the segment plan cuts them into several
+# segments, so the correction that adds each segment's entering state runs (with A = 0
+# every decay factor is 1 and it adds the whole state)
+def _limit_workload(dtype, seed):
+    return gen.Workload(f"limit-{dtype}", 2, 4096, 8, 64, 128, 2, 256, dtype, True, seed)
+
+
+def _check_limit(w, cpu, d, label):
+    if w.dtype == "bf16":
+        plan = _plan(w)
+        _print(f"{label}: segment plan {plan}")
+        assert plan is not None and plan[2] > 1
+    y, fin = gpu_forward(w, d)
+    ref = oracle_forward(cpu)
+    ey, ef = max_rel_rms(y, ref["y"]), max_rel_rms(fin, ref["final"])
+    y0, _ = gpu_forward(w, d, D=None)
+    ref0 = oracle_forward(cpu, D=None)
+    er, em = rms_rel(y0, ref0["y"]), max_rel_rms(y0, ref0["y"])
+    _print(f"{label}: y max/rms {ey:.2e}  final max/rms {ef:.2e}  SSM-only rms-rel {er:.2e} "
+           f"max/rms {em:.2e}")
+    assert np.isfinite(np64(y)).all() and np.isfinite(np64(fin)).all()
+    assert ey <= TOL[w.dtype] and ef <= TOL[w.dtype]
+    assert er <= SSM_RMS_TOL[w.dtype]
+    if w.dtype == "fp32":
+        assert em <= SSM_MAX_TOL_FP32
+    return fin
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decay_free_limit(dtype):
+    """A = 0: every cumulative decay is 0, every decay factor 1; y is causal linear
+    attention over dt-scaled keys plus the carried initial state."""
+    w = _limit_workload(dtype, 21)
+    cpu, d = make(w)
+    cpu["A"] = torch.zeros_like(cpu["A"])
+    d["A"] = dev(cpu["A"])
+    _check_limit(w, cpu, d, f"A=0 {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_frozen_state_limit(dtype):
+    """dt = 0: no token adds to the state and nothing decays, so the state stays h0 at
+    every token: y = C h0 + D x and the final state is h0."""
+    w = _limit_workload(dtype, 22)
+    cpu, d = make(w)
+    cpu["dt"] = torch.zeros_like(cpu["dt"])
+    d["dt"] = dev(cpu["dt"])
+    fin = _check_limit(w, cpu, d, f"dt=0 {dtype}")
+    _print(f"dt=0 {dtype}: final state bitwise h0: {bool(torch.equal(fin, d['h0']))}")
+    assert max_rel_rms(fin, cpu["h0"]) <= TOL[dtype]
