@@ -32,7 +32,8 @@
  *    then be NULL.
  *  - Ownership: the caller allocates and frees every buffer, including the workspace.
  *    The library never allocates device memory, keeps no pointer after returning and
- *    holds no global state, so concurrent calls on different buffers are safe.
+ *    holds no global state, so concurrent calls on different buffers are safe. (The one
+ *    exception is ssd_forward_noalloc below, which works in a scratch array of its own.)
  *  - Execution: kernels are enqueued on `stream` (a hipStream_t; NULL means the null
  *    stream) and the call returns without synchronising. Outputs are valid once the
  *    caller synchronises that stream. Inputs must not alias outputs.
@@ -65,7 +66,8 @@ typedef enum ssd_status {
     SSD_ERR_UNSUPPORTED = 4, /* chunk, headdim, dstate, dtype pair or size outside the supported sets */
     SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
     SSD_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
-    SSD_ERR_HIP = 7          /* the HIP runtime reported an error for a launch */
+    SSD_ERR_HIP = 7,         /* the HIP runtime reported an error for a launch */
+    SSD_ERR_TOO_LARGE = 8    /* ssd_forward_noalloc: the problem needs more scratch than it holds */
 } ssd_status;
 
 typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -200,6 +202,27 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
                        const void* B, const void* C, const float* D, const float* h0, void* y,
                        float* final_state, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * The whole forward pass without any allocation, for callers that cannot allocate device
+ * memory or be handed a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, results and execution as ssd_forward
+ * (bitwise: it runs the same kernels), minus the workspace: the intermediates (cumulative
+ * decays, state-pass buffers, chunk states) live in a device array of
+ * SSD_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs this call on,
+ * until the process ends. A problem whose ssd_forward_workspace_bytes exceeds that size
+ * returns SSD_ERR_TOO_LARGE before anything is enqueued (256 MiB covers, for example,
+ * batch 2 x 16384 tokens x 80 heads at headdim 64, dstate 128, chunk 256).
+ * The first call on a device resolves that device's array (hipGetSymbolAddress, which may
+ * load the library's code object there); make one call before capturing a graph. Every
+ * call on one GPU uses the same array, whose contents persist between calls: calls that
+ * overlap on one GPU (on different streams, or from several threads) race and must be
+ * serialised by the caller. Nothing in the array needs to start at zero.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+ssd_status ssd_forward_noalloc(const ssd_shape* shape, const void* x, const void* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* h0, void* y, float* final_state, void* stream);
 
 /*
  * Recurrent decode step (section "Mamba-2 architecture": the recurrent form, which takes

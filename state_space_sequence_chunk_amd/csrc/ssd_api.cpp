@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/ssd.h"
 #include "ssd_launch.h"
@@ -164,11 +165,38 @@ BwdSizes bwd_sizes(const ssd_shape* shape) {
 
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+
+
 #define SSD_REQUIRE(cond, code) \
     do {                        \
         if (!(cond)) return code; \
     } while (0)
 
+}  // namespace
+
+// ssd_forward_noalloc's scratch (see ssd.h): one array per device, each device's address
+// resolved once with that device current and kept in g_scratch. On the host `scratch`
+// names only a stand-in for the symbol, never a device address, so host code passes the
+// resolved pointers to the kernels.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+ssd_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSD_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return SSD_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -183,6 +211,9 @@ const char* ssd_status_string(int status) {
         case SSD_ERR_WORKSPACE: return "workspace missing or too small";
         case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case SSD_ERR_HIP: return "HIP runtime error";
+        case SSD_ERR_TOO_LARGE:
+            return "the problem needs more scratch than ssd_forward_noalloc holds "
+                   "(SSD_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
@@ -339,10 +370,11 @@ ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, c
                                             (hipStream_t)stream));
 }
 
-ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, const float* A,
-                       const void* B, const void* C, const float* D, const float* h0, void* y,
-                       float* final_state, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+// Argument checks of ssd_forward and ssd_forward_noalloc (everything but the workspace).
+static ssd_status check_forward_args(const ssd_shape* shape, const void* x, const void* dt,
+                                     const float* A, const void* B, const void* C,
+                                     const float* D, const float* h0, const void* y,
+                                     const float* final_state) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
     const bool empty = shape->seqlen == 0;  // only the final state (= h0) is written
@@ -350,10 +382,15 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
     SSD_REQUIRE(aligned16(x) && aligned16(dt) && aligned16(A) && aligned16(B) && aligned16(C) &&
                     aligned16(D) && aligned16(h0) && aligned16(y) && aligned16(final_state),
                 SSD_ERR_ALIGN);
-    const size_t need = forward_ws(shape);
-    SSD_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), SSD_ERR_WORKSPACE);
-    SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
+    return SSD_OK;
+}
 
+// The forward pass on checked arguments and a workspace of at least forward_ws bytes.
+static ssd_status forward_impl(const ssd_shape* shape, const void* x, const void* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* h0, void* y, float* final_state, void* workspace,
+                               void* stream) {
+    const bool empty = shape->seqlen == 0;
     const Dims d = dims_of(shape);
     hipStream_t s = (hipStream_t)stream;
     if (empty) return final_state ? hip_status(ssd::launch_state_init(h0, final_state, d, s)) : SSD_OK;
@@ -385,6 +422,30 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, co
     return hip_status(ssd::launch_chunk_out(shape->in_dtype, shape->states_dtype,
                                             shape->out_dtype, x, B, C, G,
                                             dt_t, states, D, y, d, s));
+}
+
+ssd_status ssd_forward(const ssd_shape* shape, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, const float* h0, void* y,
+                       float* final_state, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    ssd_status st = check_forward_args(shape, x, dt, A, B, C, D, h0, y, final_state);
+    if (st != SSD_OK) return st;
+    const size_t need = forward_ws(shape);
+    SSD_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), SSD_ERR_WORKSPACE);
+    SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
+    return forward_impl(shape, x, dt, A, B, C, D, h0, y, final_state, workspace, stream);
+}
+
+ssd_status ssd_forward_noalloc(const ssd_shape* shape, const void* x, const void* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* h0, void* y, float* final_state, void* stream) {
+    ssd_status st = check_forward_args(shape, x, dt, A, B, C, D, h0, y, final_state);
+    if (st != SSD_OK) return st;
+    SSD_REQUIRE(forward_ws(shape) <= SSD_NOALLOC_SCRATCH_BYTES, SSD_ERR_TOO_LARGE);
+    void* ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != SSD_OK) return st;
+    return forward_impl(shape, x, dt, A, B, C, D, h0, y, final_state, ws, stream);
 }
 
 ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const void* dt, const float* A,

@@ -17,14 +17,17 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libssd_mi355x.so")
 
 SSD_F32, SSD_BF16 = 0, 1
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
-          4: "SSD_ERR_UNSUPPORTED", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_ALIGN", 7: "SSD_ERR_HIP"}
+          4: "SSD_ERR_UNSUPPORTED", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_ALIGN", 7: "SSD_ERR_HIP",
+          8: "SSD_ERR_TOO_LARGE"}
+# Bytes of the scratch array behind ssd_forward_noalloc (SSD_NOALLOC_SCRATCH_BYTES in ssd.h).
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 # Entry points declared in include/ssd.h.
 EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_bytes",
            "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
            "ssd_state_scan", "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
            "ssd_backward", "ssd_state_seg_workspace_bytes", "ssd_state_seg", "ssd_chunk_out_seg",
-           "ssd_state_seg_plan")
+           "ssd_state_seg_plan", "ssd_forward_noalloc")
 # HBM stream probes declared in include/ssd_probe.h (measurement only).
 PROBE_EXPORTS = ("ssd_probe_read", "ssd_probe_write", "ssd_probe_copy")
 
@@ -70,6 +73,7 @@ def load_library():
     lib.ssd_state_scan.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_out.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_forward_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_backward_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
     lib.ssd_backward.argtypes = [sp] + [vp] * 17 + [sz, vp]
@@ -215,6 +219,14 @@ def ssd_forward(shape, x, dt, A, B, C, D, h0, y, final_state, workspace, stream=
     _check(load_library().ssd_forward(ctypes.byref(shape), _p(x), _p(dt), _p(A), _p(B), _p(C),
                                       _p(D), _p(h0), _p(y), _p(final_state), _p(workspace),
                                       nbytes, _stream(stream)), "ssd_forward")
+
+
+def ssd_forward_noalloc(shape, x, dt, A, B, C, D, h0, y, final_state, stream=None):
+    """ssd_forward without a workspace: the library's own per-device scratch array holds
+    the intermediates (no allocation; calls that overlap on one GPU race)."""
+    _check(load_library().ssd_forward_noalloc(ctypes.byref(shape), _p(x), _p(dt), _p(A), _p(B),
+                                              _p(C), _p(D), _p(h0), _p(y), _p(final_state),
+                                              _stream(stream)), "ssd_forward_noalloc")
 
 
 def ssd_decode_step(shape, x, dt, A, B, C, D, state, y, stream=None):

@@ -382,3 +382,23 @@ def test_backward_chunk_stays_within_size_limits():
 ])
 def test_probe_argument_checks(call, code):
     assert call(ssd.load_library()) == code
+
+
+# --- ssd_forward_noalloc: the size check happens on the host, before any HIP call ---------
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SSD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ssd.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_too_large_on_host():
+    lib = ssd.load_library()
+    big = shape(batch=1, seqlen=65536, nheads=80, headdim=64, dstate=256, ngroups=8, chunk=256)
+    assert ssd.forward_workspace_bytes(big) > ssd.NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(4096)
+    rc = lib.ssd_forward_noalloc(ctypes.byref(big), p, p, p, p, p, p, p, p, p, None)
+    assert rc == 8
+    assert b"scratch" in lib.ssd_status_string(8)
+    # the bench shape fits
+    bench = shape(batch=2, seqlen=16384, nheads=80, headdim=64, dstate=128, ngroups=1, chunk=256)
+    assert ssd.forward_workspace_bytes(bench) <= ssd.NOALLOC_SCRATCH_BYTES
