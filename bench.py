@@ -35,8 +35,9 @@ FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
 def algorithmic(w, nseg=None):
     """Bytes each stage must move (inputs read once, outputs written once) and the
     per-head dense flop count of the matrix stages. With nseg (the segmented state pass's
-    segment count), chunk_out's bytes include the states entering segments 1.. (bf16), which
-    it reads to complete the segment-relative chunk states."""
+    segment count), chunk_out's bytes include the states entering segments 1.. (bf16) and
+    each chunk's decay from its segment's start, which it reads to complete the
+    segment-relative chunk states."""
     B, L, H, P, S, G, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     e = 2 if w.dtype == "bf16" else 4
     es = e  # chunk-initial states are stored in the input dtype
@@ -53,11 +54,11 @@ def algorithmic(w, nseg=None):
         "state_carry": n_states * 4 + B * H * nC * 4 + h0 + n_states * es + fin,
         # the segmented pass: inputs once, the (segment-relative) chunk states and the
         # final state once; its per-segment states are not counted (a few % at most)
-        "state_seg": x + bc + dec + H * 4 + h0 + n_states * es + fin,
+        "state_seg": x + bc + 2 * dec + H * 4 + h0 + n_states * es + fin,
         "chunk_out": x + 2 * bc + 2 * dec + n_states * es + H * 4 + B * L * H * P * 4,
     }
     if nseg:
-        by["chunk_out"] += (nseg - 1) * B * H * P * S * 2
+        by["chunk_out"] += (nseg - 1) * B * H * P * S * 2 + B * H * nC * 4
     fl = {
         "chunk_state": 2.0 * B * nC * H * T * P * S,
         "chunk_out": B * nC * H * (2.0 * T * T * S + 2.0 * T * S * P + 2.0 * T * T * P),
@@ -321,13 +322,13 @@ def state_pass_sweep(torch, ssd, gen, reps=20, warmup=5):
                                              stream))
         rec = {}
         try:
-            wseg = torch.empty(ssd.state_seg_workspace_bytes(sh), dtype=torch.uint8,
+            wseg = torch.empty(ssd.state_pass_segmented_workspace_bytes(sh), dtype=torch.uint8,
                                device="cuda")
         except ssd.SSDError:
             wseg = None
         if wseg is not None:
-            tg = t_ms(lambda: ssd.ssd_state_seg(sh, d["x"], d["A"], d["B"], Gc, dtt, d["h0"], st,
-                                                fin, wseg, stream))
+            tg = t_ms(lambda: ssd.ssd_state_pass_segmented(sh, d["x"], d["A"], d["B"], Gc, dtt,
+                                                           d["h0"], st, fin, wseg, stream))
             rec = {"state_seg_ms": round(tg, 4), "seg_over_pass": round(tg / tp, 3)}
         blocks = B * H * (P // 64)
         print(json.dumps({"layer": name, "batch": B, "seqlen": L, "nheads": H, "headdim": P,
@@ -407,7 +408,8 @@ def main():
     # the stages as ssd_forward runs them: the segmented state pass (with its output
     # kernel) where the shape has a segment plan, else the two-kernel state pass
     try:
-        ws_sp = torch.empty(ssd.state_seg_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+        ws_sp = torch.empty(ssd.state_pass_segmented_workspace_bytes(sh), dtype=torch.uint8,
+                            device=dev)
         segmented = True
     except ssd.SSDError:
         ws_sp = torch.empty(ssd.state_pass_workspace_bytes(sh), dtype=torch.uint8, device=dev)
@@ -422,16 +424,16 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if segmented:
-            ssd.ssd_state_seg(sh, d["x"], d["A"], d["B"], G, dt_t, d["h0"], states, fin, ws_sp,
-                              stream)
+            ssd.ssd_state_pass_segmented(sh, d["x"], d["A"], d["B"], G, dt_t, d["h0"], states,
+                                         fin, ws_sp, stream)
         else:
             ssd.ssd_state_pass(sh, d["x"], d["A"], d["B"], G, dt_t, d["h0"], states, fin,
                                ws_sp, stream)
         if ev is not None:
             ev[2].record(stream)
         if segmented:
-            ssd.ssd_chunk_out_seg(sh, d["x"], d["B"], d["C"], G, dt_t, states, d["D"], y, ws_sp,
-                                  stream)
+            ssd.ssd_chunk_out_segmented(sh, d["x"], d["B"], d["C"], G, dt_t, d["D"], states, y,
+                                        ws_sp, stream)
         else:
             ssd.ssd_chunk_out(sh, d["x"], d["B"], d["C"], G, dt_t, states, d["D"], y, stream)
         if ev is not None:
@@ -509,7 +511,7 @@ def main():
     except Exception as exc:  # reported, never silently replaced
         decode = {"error": f"{type(exc).__name__}: {exc}"}
 
-    by, fl = algorithmic(w, ssd.state_seg_plan(sh)[2] if segmented else None)
+    by, fl = algorithmic(w, ssd.segment_plan(sh)[2] if segmented else None)
     kernels = {
         "cumsum": {"ms": stage_ms["cumsum"], "bytes": by["cumsum"]},
         "state_pass": {"ms": stage_ms["state_pass"],

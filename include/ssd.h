@@ -91,7 +91,7 @@ const char* ssd_status_string(int status);
 /* Host-only check of a shape against the supported sets; enqueues nothing. */
 ssd_status ssd_validate_shape(const ssd_shape* shape);
 
-/* Workspace sizes in bytes for ssd_forward and ssd_state_pass (ssd_state_seg's below).
+/* Workspace sizes in bytes for ssd_forward and ssd_state_pass (the segmented pair's below).
  * Host-only. */
 ssd_status ssd_forward_workspace_bytes(const ssd_shape* shape, size_t* bytes);
 ssd_status ssd_state_pass_workspace_bytes(const ssd_shape* shape, size_t* bytes);
@@ -120,6 +120,13 @@ ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float*
  * is not NULL, final_state[b,h] = S_nchunks in fp32.
  * Inputs: x, B in in_dtype; A fp32 [nheads]; G and dt_t as produced by ssd_chunk_cumsum;
  * h0 fp32. The workspace must hold ssd_state_pass_workspace_bytes bytes.
+ * How: where the shape has a segment plan (bf16 inputs and states; see
+ * ssd_state_pass_segmented) the chunks are walked by segments with the running states on
+ * chip, the states entering the segments are carried, and each recorded state is then
+ * completed in place to the true S_c, with the arithmetic ssd_chunk_out_segmented uses for
+ * the same sum, so ssd_chunk_cumsum -> ssd_state_pass -> ssd_chunk_out returns the bits
+ * ssd_forward returns; otherwise per-chunk increments on the matrix cores and a
+ * sequential carry.
  */
 ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A, const void* B,
                           const float* G, const float* dt_t, const float* h0, void* states,
@@ -156,41 +163,42 @@ ssd_status ssd_chunk_out(const ssd_shape* shape, const void* x, const void* B, c
                          void* y, void* stream);
 
 /*
- * Stage 2 by segments, with stage 3 to match (the linearity of the recurrence of section
- * "Mamba-2 architecture" applied to the state kernel of section "Kernel 2:
- * fwd_pass_state"). The chunks are cut into segments of K consecutive chunks (K and the
- * heads per workgroup are the library's choice for the shape). Each segment is walked from
- * a zero state (segment 0 from h0), so what ssd_state_seg records in states[b,h,c] is the
- * state entering chunk c minus the part carried in from before its segment; the true
- * state is
- *     S_c = states[b,h,c] + 2^{D_c} S_in(k),   k = c / K,  D_c = sum of G_last over the
- *                                              segment's chunks before c,
- * with S_in(k) the state entering segment k (S_in(0) adds nothing). ssd_state_seg also
- * writes S_in(k) (bf16), D_c and the final state (fp32, when final_state is not NULL)
- * into / from its workspace, and ssd_chunk_out_seg computes y as ssd_chunk_out does from
- * the true states, adding 2^{D_c} S_in(k) while it stages each chunk's state (fp32 sum,
- * one bf16 rounding). The per-chunk state increments never go to HBM. ssd_forward runs
- * these two (after stage 1) whenever the shape has a segment plan.
+ * Stage 2 by segments, and stage 3 over its output (the linearity of the recurrence of
+ * section "Mamba-2 architecture" applied to the state kernel of section "Kernel 2:
+ * fwd_pass_state"); the pair ssd_forward runs whenever the shape has a segment plan.
+ * The chunks are cut into segments of K consecutive chunks (K and the heads per workgroup
+ * are the library's choice for the shape, see ssd_segment_plan). Each segment is walked
+ * from a zero state (segment 0 from h0), so what ssd_state_pass_segmented records in
+ * seg_relative_states[b,h,c] is NOT the state entering chunk c but that state minus the
+ * part carried in from before the chunk's segment; the true state is
+ *     S_c = seg_relative_states[b,h,c] + 2^{D_c} S_in(k),   k = c / K,
+ *     D_c = sum of G_last over the segment's chunks before c,
+ * with S_in(k) the state entering segment k (S_in(0) adds nothing). G and dt_t are
+ * ssd_chunk_cumsum's. ssd_state_pass_segmented writes S_in(k) (bf16) and D_c to the
+ * workspace, and the final state (fp32) to final_state when it is not NULL; the per-chunk
+ * state increments never go to HBM. ssd_chunk_out_segmented then computes y exactly as
+ * ssd_chunk_out does from the true states, forming each chunk's S_c (fp32 sum, one bf16
+ * rounding) while it stages it; it reads S_in and D_c from the same workspace, which must
+ * be passed unchanged between the two calls on the same stream.
  * Built for bf16 inputs with bf16 states (states_dtype SSD_BF16), headdim 64, dstate 64,
- * 128 or 256; other shapes return SSD_ERR_UNSUPPORTED (as does the workspace query). Inputs
- * as for ssd_state_pass and ssd_chunk_out; the workspace must hold
- * ssd_state_seg_workspace_bytes bytes and is passed unchanged from ssd_state_seg to
- * ssd_chunk_out_seg on the same stream (it carries S_in and D_c between them).
+ * 128 or 256; other shapes return SSD_ERR_UNSUPPORTED (as do the queries). The workspace
+ * must hold ssd_state_pass_segmented_workspace_bytes bytes.
  */
-ssd_status ssd_state_seg_workspace_bytes(const ssd_shape* shape, size_t* bytes);
+ssd_status ssd_state_pass_segmented_workspace_bytes(const ssd_shape* shape, size_t* bytes);
 /* The segment plan the library takes for a shape (host-only): heads per workgroup,
  * chunks per segment K and the number of segments. SSD_ERR_UNSUPPORTED where the shape
  * has no plan (or seqlen is 0). Any of the outputs may be NULL. */
-ssd_status ssd_state_seg_plan(const ssd_shape* shape, int32_t* heads_per_workgroup,
-                              int32_t* chunks_per_segment, int32_t* segments);
-ssd_status ssd_state_seg(const ssd_shape* shape, const void* x, const float* A, const void* B,
-                         const float* G, const float* dt_t, const float* h0, void* states,
-                         float* final_state, void* workspace, size_t workspace_bytes,
-                         void* stream);
-ssd_status ssd_chunk_out_seg(const ssd_shape* shape, const void* x, const void* B, const void* C,
-                             const float* G, const float* dt_t, const void* states,
-                             const float* D, void* y, const void* workspace,
-                             size_t workspace_bytes, void* stream);
+ssd_status ssd_segment_plan(const ssd_shape* shape, int32_t* heads_per_workgroup,
+                            int32_t* chunks_per_segment, int32_t* segments);
+ssd_status ssd_state_pass_segmented(const ssd_shape* shape, const void* x, const float* A,
+                                    const void* B, const float* G, const float* dt_t,
+                                    const float* h0, void* seg_relative_states,
+                                    float* final_state, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+ssd_status ssd_chunk_out_segmented(const ssd_shape* shape, const void* x, const void* B,
+                                   const void* C, const float* G, const float* dt_t,
+                                   const float* D, const void* seg_relative_states, void* y,
+                                   const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The whole forward pass: stage 1, stage 2, stage 3 on one stream. Returns y (out_dtype) and,

@@ -186,9 +186,7 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
     const int nseg = SEGC ? (nC + seg_chunks - 1) / seg_chunks : 0;
     Vec16 psi[SEGC ? Cfg::NSV : 1];
     float pdec = 0.f;
-    // Below this log2 decay 2^{D_c} is exactly 0 in fp32 (even as a denormal), so the
-    // correction adds exactly nothing and the entering state is not read at all.
-    constexpr float kSegCut = -160.f;
+    // (below kSegCut the correction adds exactly nothing and seg_in is not read at all)
     auto load_head = [&](int h) {
 #pragma unroll
         for (int i = 0; i < Cfg::NXV; ++i) {

@@ -107,21 +107,10 @@ __global__ __launch_bounds__(kCumsumThreads) void cumsum_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     for (int hh = wave; hh < nh; hh += kCumsumThreads / 64) {
         const int h = h0 + hh;
-        const float ah = A[h];
-        float d[PER], part[PER];
-        float run = 0.f;
+        float d[PER], g[PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            d[k] = s_dt[hh * LD + lane * PER + k];
-            run += ah * d[k];
-            part[k] = run;
-        }
-        const float incl = wave_inclusive_scan(run);
-        // exclusive prefix = inclusive prefix of the previous lane (DPP wave_shr:1)
-        const float excl = wave_shift_up1(incl);
-        float g[PER];
-#pragma unroll
-        for (int k = 0; k < PER; ++k) g[k] = (excl + part[k]) * kLog2e;
+        for (int k = 0; k < PER; ++k) d[k] = s_dt[hh * LD + lane * PER + k];
+        chunk_log2_decay<PER>(d, A[h], g);
         const size_t o = ((size_t)b * H + h) * L + t0 + lane * PER;
         if (rows < T || (L & 3) != 0) {
             // partial chunk, or rows not 16-byte aligned: element stores of the real tokens

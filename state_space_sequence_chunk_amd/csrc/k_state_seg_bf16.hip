@@ -194,4 +194,14 @@ hipError_t launch_state_seg(const void* x, const void* Bm, const float* A, const
     return hipGetLastError();
 }
 
+hipError_t launch_seg_correct(void* states, const SegPlan& pl, const SegBuffers& sb,
+                              const Dims& d, hipStream_t stream) {
+    if (pl.nseg == 1) return hipSuccess;  // every chunk is in segment 0: already true states
+    const long nblocks = (long)d.batch * d.nheads * d.nchunks();
+    seg_correct_kernel<<<(unsigned)nblocks, 256, 0, stream>>>(
+        (bf16*)states, (const bf16*)sb.seg_in, sb.dec_in, d.nchunks(), pl.chunks, pl.nseg,
+        d.headdim * d.dstate);
+    return hipGetLastError();
+}
+
 }  // namespace ssd

@@ -97,7 +97,7 @@ size_t decay_bytes(const ssd_shape* s) {  // one [batch, nheads, seqlen] fp32 ar
 size_t chunk_states_elems(const ssd_shape* s) {
     return (size_t)s->batch * s->nheads * nchunks_of(s) * s->headdim * s->dstate;
 }
-size_t state_pass_ws(const ssd_shape* s) {  // per-chunk state increments, fp32
+size_t pair_ws(const ssd_shape* s) {  // per-chunk state increments, fp32
     return round_up(chunk_states_elems(s) * sizeof(float));
 }
 // Segment plan of the segmented state pass, when the shape has one.
@@ -108,12 +108,14 @@ size_t state_seg_ws(const ssd_shape* s) {  // 0 when the shape has no segment pl
     ssd::SegPlan pl;
     return seg_plan_of(s, &pl) ? round_up(ssd::state_seg_ws_bytes(dims_of(s), pl)) : 0;
 }
-// G, dt_t, then the state pass's own buffers (the segmented pass's, else the increments),
-// then the chunk-initial states
-size_t forward_mid_ws(const ssd_shape* s) {
+// The state pass's own buffers: the segmented pass's where the shape has a plan, else the
+// per-chunk increments.
+size_t state_pass_ws(const ssd_shape* s) {
     ssd::SegPlan pl;
-    return seg_plan_of(s, &pl) ? state_seg_ws(s) : state_pass_ws(s);
+    return seg_plan_of(s, &pl) ? state_seg_ws(s) : pair_ws(s);
 }
+// Forward workspace: G, dt_t, then the state pass's buffers, then the chunk-initial states.
+size_t forward_mid_ws(const ssd_shape* s) { return state_pass_ws(s); }
 size_t forward_ws(const ssd_shape* s) {
     return 2 * decay_bytes(s) + forward_mid_ws(s) +
            round_up(chunk_states_elems(s) * esize(s->states_dtype));
@@ -236,18 +238,18 @@ ssd_status ssd_state_pass_workspace_bytes(const ssd_shape* shape, size_t* bytes)
     return SSD_OK;
 }
 
-ssd_status ssd_state_seg_workspace_bytes(const ssd_shape* shape, size_t* bytes) {
+ssd_status ssd_state_pass_segmented_workspace_bytes(const ssd_shape* shape, size_t* bytes) {
     SSD_REQUIRE(bytes, SSD_ERR_NULL);
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
     ssd::SegPlan pl;
     SSD_REQUIRE(shape->seqlen == 0 || seg_plan_of(shape, &pl), SSD_ERR_UNSUPPORTED);
-    *bytes = state_seg_ws(shape);
+    *bytes = shape->seqlen == 0 ? 0 : state_seg_ws(shape);
     return SSD_OK;
 }
 
-ssd_status ssd_state_seg_plan(const ssd_shape* shape, int32_t* heads_per_workgroup,
-                              int32_t* chunks_per_segment, int32_t* segments) {
+ssd_status ssd_segment_plan(const ssd_shape* shape, int32_t* heads_per_workgroup,
+                            int32_t* chunks_per_segment, int32_t* segments) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
     ssd::SegPlan pl;
@@ -287,6 +289,15 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
     const Dims d = dims_of(shape);
     hipStream_t s = (hipStream_t)stream;
     if (empty) return final_state ? hip_status(ssd::launch_state_init(h0, final_state, d, s)) : SSD_OK;
+    ssd::SegPlan pl;
+    if (seg_plan_of(shape, &pl)) {
+        // segmented walk, carry, then the recorded states completed to the true ones
+        const ssd::SegBuffers sb = ssd::state_seg_buffers(workspace, d, pl);
+        hipError_t e = ssd::launch_state_seg(x, B, A, G, dt_t, h0, states, final_state, pl, sb,
+                                             d, s);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+        return hip_status(ssd::launch_seg_correct(states, pl, sb, d, s));
+    }
     float* dS = (float*)workspace;
     hipError_t e = ssd::launch_chunk_state(shape->in_dtype, x, B, A, dt_t, dS, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
@@ -294,49 +305,52 @@ ssd_status ssd_state_pass(const ssd_shape* shape, const void* x, const float* A,
                                               final_state, d, s));
 }
 
-ssd_status ssd_state_seg(const ssd_shape* shape, const void* x, const float* A, const void* B,
-                         const float* G, const float* dt_t, const float* h0, void* states,
-                         float* final_state, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+ssd_status ssd_state_pass_segmented(const ssd_shape* shape, const void* x, const float* A,
+                                    const void* B, const float* G, const float* dt_t,
+                                    const float* h0, void* seg_relative_states,
+                                    float* final_state, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
     const bool empty = shape->seqlen == 0;  // only the final state (= h0) is written
     ssd::SegPlan pl;
     SSD_REQUIRE(empty || seg_plan_of(shape, &pl), SSD_ERR_UNSUPPORTED);
-    SSD_REQUIRE(A && (empty || (x && B && G && dt_t && states)), SSD_ERR_NULL);
+    SSD_REQUIRE(A && (empty || (x && B && G && dt_t && seg_relative_states)), SSD_ERR_NULL);
     SSD_REQUIRE(aligned16(x) && aligned16(A) && aligned16(B) && aligned16(G) && aligned16(dt_t) &&
-                    aligned16(h0) && aligned16(states) && aligned16(final_state),
+                    aligned16(h0) && aligned16(seg_relative_states) && aligned16(final_state),
                 SSD_ERR_ALIGN);
-    const size_t need = state_seg_ws(shape);
+    const size_t need = empty ? 0 : state_seg_ws(shape);
     SSD_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), SSD_ERR_WORKSPACE);
     SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
     const Dims d = dims_of(shape);
     hipStream_t s = (hipStream_t)stream;
     if (empty) return final_state ? hip_status(ssd::launch_state_init(h0, final_state, d, s)) : SSD_OK;
-    return hip_status(ssd::launch_state_seg(x, B, A, G, dt_t, h0, states, final_state, pl,
-                                            ssd::state_seg_buffers(workspace, d, pl), d, s));
+    const ssd::SegBuffers sb = ssd::state_seg_buffers(workspace, d, pl);
+    return hip_status(ssd::launch_state_seg(x, B, A, G, dt_t, h0, seg_relative_states,
+                                            final_state, pl, sb, d, s));
 }
 
-ssd_status ssd_chunk_out_seg(const ssd_shape* shape, const void* x, const void* B, const void* C,
-                             const float* G, const float* dt_t, const void* states,
-                             const float* D, void* y, const void* workspace,
-                             size_t workspace_bytes, void* stream) {
+ssd_status ssd_chunk_out_segmented(const ssd_shape* shape, const void* x, const void* B,
+                                   const void* C, const float* G, const float* dt_t,
+                                   const float* D, const void* seg_relative_states, void* y,
+                                   const void* workspace, size_t workspace_bytes, void* stream) {
     ssd_status st = check_shape(shape);
     if (st != SSD_OK) return st;
     if (shape->seqlen == 0) return SSD_OK;  // empty sequence: no output rows
     ssd::SegPlan pl;
     SSD_REQUIRE(seg_plan_of(shape, &pl), SSD_ERR_UNSUPPORTED);
-    SSD_REQUIRE(x && B && C && G && dt_t && states && y, SSD_ERR_NULL);
+    SSD_REQUIRE(x && B && C && G && dt_t && seg_relative_states && y, SSD_ERR_NULL);
     SSD_REQUIRE(aligned16(x) && aligned16(B) && aligned16(C) && aligned16(G) &&
-                    aligned16(dt_t) && aligned16(states) && aligned16(D) && aligned16(y),
+                    aligned16(dt_t) && aligned16(D) && aligned16(seg_relative_states) &&
+                    aligned16(y),
                 SSD_ERR_ALIGN);
     SSD_REQUIRE(workspace && workspace_bytes >= state_seg_ws(shape), SSD_ERR_WORKSPACE);
     SSD_REQUIRE(aligned16(workspace), SSD_ERR_ALIGN);
     const Dims d = dims_of(shape);
     const ssd::SegBuffers sb = ssd::state_seg_buffers(const_cast<void*>(workspace), d, pl);
-    return hip_status(ssd::launch_chunk_out_seg(shape->out_dtype, x, B, C, G, dt_t, states,
-                                                sb.seg_in, sb.dec_in, pl.chunks, D, y, d,
-                                                (hipStream_t)stream));
+    return hip_status(ssd::launch_chunk_out_seg(shape->out_dtype, x, B, C, G, dt_t,
+                                                seg_relative_states, sb.seg_in, sb.dec_in,
+                                                pl.chunks, D, y, d, (hipStream_t)stream));
 }
 
 ssd_status ssd_state_scan(const ssd_shape* shape, const void* x, const float* A, const void* B,
@@ -398,19 +412,19 @@ static ssd_status forward_impl(const ssd_shape* shape, const void* x, const void
     float* G = (float*)w;
     float* dt_t = (float*)(w + decay_bytes(shape));
     void* mid = (void*)(w + 2 * decay_bytes(shape));
-    float* dS = (float*)mid;
     void* states = (void*)(w + 2 * decay_bytes(shape) + forward_mid_ws(shape));
-
     hipError_t e = ssd::launch_cumsum(shape->in_dtype, dt, A, G, dt_t, d, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
     ssd::SegPlan pl;
     if (seg_plan_of(shape, &pl)) {
+        // segment-relative states; the output kernel completes them while staging
         const ssd::SegBuffers sb = ssd::state_seg_buffers(mid, d, pl);
         e = ssd::launch_state_seg(x, B, A, G, dt_t, h0, states, final_state, pl, sb, d, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
         return hip_status(ssd::launch_chunk_out_seg(shape->out_dtype, x, B, C, G, dt_t, states,
                                                     sb.seg_in, sb.dec_in, pl.chunks, D, y, d, s));
     }
+    float* dS = (float*)mid;
     if (ssd::state_scan_supported(shape->in_dtype, d) && ssd::state_scan_preferred(shape->in_dtype, d)) {
         e = ssd::launch_state_scan(shape->states_dtype, x, B, A, dt_t, h0, states, final_state, d, s);
     } else {

@@ -81,6 +81,31 @@ __device__ __forceinline__ float wave_shift_up1(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, false));
 }
 
+// Per-chunk cumulative decay of one head, one wave: lane l holds the chunk's tokens
+// l*PER .. l*PER+PER-1 (d = dt, fp32). G[t] = log2(e) * sum of A dt over the chunk's tokens
+// up to t (inclusive): a serial sum over the lane's tokens, then a DPP scan of the lane
+// totals. Every kernel that forms G calls this, so they agree bit for bit.
+template <int PER>
+__device__ __forceinline__ void chunk_log2_decay(const float (&d)[PER], float ah, float (&g)[PER]) {
+    float part[PER];
+    float run = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        run += ah * d[k];
+        part[k] = run;
+    }
+    // exclusive prefix of the lane totals = inclusive prefix of the previous lane
+    const float excl = wave_shift_up1(wave_inclusive_scan(run));
+    {
+        // G is a rounded product wherever it is used: a caller that goes on to subtract it
+        // must not have the multiply fused into that subtraction (an FMA would skip the
+        // rounding and give other bits than a G read back from memory)
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) g[k] = (excl + part[k]) * kLog2e;
+    }
+}
+
 // LDS row strides (in elements) chosen against bank conflicts on 64 four-byte banks.
 //  - col_stride: for ds_read_b64_tr_b16 column reads, where the 32 lanes served together
 //    read 8 consecutive rows x 32 bytes: the row stride in words must be an odd multiple

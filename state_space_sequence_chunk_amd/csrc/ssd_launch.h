@@ -46,6 +46,10 @@ hipError_t launch_state_scan(int states_dtype, const void* x, const void* Bm, co
 struct SegPlan {
     int heads, chunks, nseg;
 };
+// Below this log2 decay from a segment's start the factor 2^{D_c} is exactly 0 in fp32
+// (even as a denormal), so adding the decayed entering state changes nothing and the
+// kernels that form S_c = L_c + 2^{D_c} S_in skip it (and do not read S_in).
+constexpr float kSegCut = -160.f;
 struct SegBuffers {
     float* seg_end;   // [B, H, nseg, P, S] each segment's end state from its own start
     void* seg_in;     // [B, H, nseg, P, S] bf16 state entering each segment (>= 1)
@@ -59,6 +63,10 @@ hipError_t launch_state_seg(const void* x, const void* Bm, const float* A, const
                             const float* dt_t, const float* h0, void* states,
                             float* final_state, const SegPlan& plan, const SegBuffers& sb,
                             const Dims& d, hipStream_t stream);
+// Segment-relative chunk states -> true chunk-initial states, in place (after the carry),
+// with the arithmetic of launch_chunk_out_seg's completion (the same bits).
+hipError_t launch_seg_correct(void* states, const SegPlan& plan, const SegBuffers& sb,
+                              const Dims& d, hipStream_t stream);
 
 // final_state = h0 (zeros when h0 is NULL): the state after an empty sequence.
 hipError_t launch_state_init(const float* h0, float* final_state, const Dims& d,

@@ -422,4 +422,32 @@ __global__ __launch_bounds__(64) void seg_carry_kernel(const float* __restrict__
     if (fin) *(f32x4*)(fin + bh * PS + e) = hv;
 }
 
+
+// True chunk-initial states from segment-relative ones, in place: for the chunks of
+// segments k >= 1, S_c = bf16(L_c + 2^{D_c} S_in(k)) with the fp32 arithmetic the output
+// kernel uses when it forms the same sum while staging a state, so either route gives the
+// same bits; chunks with D_c below kSegCut are left as they are. One workgroup of 256
+// threads per (batch, head, chunk), 16-byte accesses.
+__global__ __launch_bounds__(256) void seg_correct_kernel(bf16* __restrict__ states,
+                                                          const bf16* __restrict__ seg_in,
+                                                          const float* __restrict__ dec_in,
+                                                          int nC, int K, int nseg, int PS) {
+    const int c = blockIdx.x % nC;
+    const size_t bh = blockIdx.x / nC;
+    const int k = c / K;
+    if (k == 0) return;
+    const float dec = dec_in[bh * nC + c];
+    if (!(dec >= kSegCut)) return;
+    const float f = exp2_fast(dec);
+    bf16x8* st = (bf16x8*)(states + (bh * nC + c) * (size_t)PS);
+    const bf16x8* si = (const bf16x8*)(seg_in + (bh * nseg + k) * (size_t)PS);
+    for (int v = threadIdx.x; v < PS / 8; v += 256) {
+        const bf16x8 l8 = st[v], s8 = si[v];
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(to_f32(l8[e]) + f * to_f32(s8[e]));
+        st[v] = o;
+    }
+}
+
 }  // namespace ssd

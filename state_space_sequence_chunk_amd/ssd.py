@@ -26,8 +26,8 @@ NOALLOC_SCRATCH_BYTES = 256 << 20
 EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_bytes",
            "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
            "ssd_state_scan", "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
-           "ssd_backward", "ssd_state_seg_workspace_bytes", "ssd_state_seg", "ssd_chunk_out_seg",
-           "ssd_state_seg_plan", "ssd_forward_noalloc")
+           "ssd_backward", "ssd_state_pass_segmented_workspace_bytes", "ssd_state_pass_segmented",
+           "ssd_chunk_out_segmented", "ssd_segment_plan", "ssd_forward_noalloc")
 # HBM stream probes declared in include/ssd_probe.h (measurement only).
 PROBE_EXPORTS = ("ssd_probe_read", "ssd_probe_write", "ssd_probe_copy")
 
@@ -77,11 +77,11 @@ def load_library():
     lib.ssd_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_backward_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
     lib.ssd_backward.argtypes = [sp] + [vp] * 17 + [sz, vp]
-    lib.ssd_state_seg_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
-    lib.ssd_state_seg.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.ssd_chunk_out_seg.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_state_pass_segmented_workspace_bytes.argtypes = [sp, ctypes.POINTER(sz)]
+    lib.ssd_state_pass_segmented.argtypes = [sp] + [vp] * 9 + [sz, vp]
+    lib.ssd_chunk_out_segmented.argtypes = [sp] + [vp] * 9 + [sz, vp]
     i32p = ctypes.POINTER(ctypes.c_int32)
-    lib.ssd_state_seg_plan.argtypes = [sp, i32p, i32p, i32p]
+    lib.ssd_segment_plan.argtypes = [sp, i32p, i32p, i32p]
     lib.ssd_probe_read.argtypes = [vp, sz, vp, i32, i32, vp]
     lib.ssd_probe_write.argtypes = [vp, sz, i32, i32, vp]
     lib.ssd_probe_copy.argtypes = [vp, vp, sz, i32, i32, vp]
@@ -183,35 +183,40 @@ def ssd_chunk_out(shape, x, B, C, G, dt_t, states, D, y, stream=None):
            "ssd_chunk_out")
 
 
-def state_seg_workspace_bytes(shape: ssd_shape) -> int:
+def state_pass_segmented_workspace_bytes(shape: ssd_shape) -> int:
     n = ctypes.c_size_t(0)
-    _check(load_library().ssd_state_seg_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)),
-           "ssd_state_seg_workspace_bytes")
+    _check(load_library().ssd_state_pass_segmented_workspace_bytes(ctypes.byref(shape),
+                                                                   ctypes.byref(n)),
+           "ssd_state_pass_segmented_workspace_bytes")
     return int(n.value)
 
 
-def state_seg_plan(shape: ssd_shape):
+def segment_plan(shape: ssd_shape):
     """(heads per workgroup, chunks per segment, segments) of the segmented state pass;
     raises SSDError (SSD_ERR_UNSUPPORTED) for shapes without a plan."""
     h, k, n = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(load_library().ssd_state_seg_plan(ctypes.byref(shape), ctypes.byref(h),
-                                             ctypes.byref(k), ctypes.byref(n)),
-           "ssd_state_seg_plan")
+    _check(load_library().ssd_segment_plan(ctypes.byref(shape), ctypes.byref(h),
+                                           ctypes.byref(k), ctypes.byref(n)),
+           "ssd_segment_plan")
     return int(h.value), int(k.value), int(n.value)
 
 
-def ssd_state_seg(shape, x, A, B, G, dt_t, h0, states, final_state, workspace, stream=None):
+def ssd_state_pass_segmented(shape, x, A, B, G, dt_t, h0, seg_relative_states, final_state,
+                             workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().ssd_state_seg(ctypes.byref(shape), _p(x), _p(A), _p(B), _p(G), _p(dt_t),
-                                        _p(h0), _p(states), _p(final_state), _p(workspace),
-                                        nbytes, _stream(stream)), "ssd_state_seg")
+    _check(load_library().ssd_state_pass_segmented(
+        ctypes.byref(shape), _p(x), _p(A), _p(B), _p(G), _p(dt_t), _p(h0),
+        _p(seg_relative_states), _p(final_state), _p(workspace), nbytes, _stream(stream)),
+        "ssd_state_pass_segmented")
 
 
-def ssd_chunk_out_seg(shape, x, B, C, G, dt_t, states, D, y, workspace, stream=None):
+def ssd_chunk_out_segmented(shape, x, B, C, G, dt_t, D, seg_relative_states, y, workspace,
+                            stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().ssd_chunk_out_seg(ctypes.byref(shape), _p(x), _p(B), _p(C), _p(G),
-                                            _p(dt_t), _p(states), _p(D), _p(y), _p(workspace),
-                                            nbytes, _stream(stream)), "ssd_chunk_out_seg")
+    _check(load_library().ssd_chunk_out_segmented(
+        ctypes.byref(shape), _p(x), _p(B), _p(C), _p(G), _p(dt_t), _p(D),
+        _p(seg_relative_states), _p(y), _p(workspace), nbytes, _stream(stream)),
+        "ssd_chunk_out_segmented")
 
 
 def ssd_forward(shape, x, dt, A, B, C, D, h0, y, final_state, workspace, stream=None):

@@ -112,3 +112,25 @@ def full_errors(y, fin, cpu: dict, *, D="given", heads: int = 16):
             "y_rms_rel": (acc["y_err2"] / acc["y_n"]) ** 0.5 / y_rms,
             "final": acc["f_max"] / f_rms if f_rms > 0 else (0.0 if acc["f_max"] == 0 else
                                                              float("inf"))}
+
+
+def bf16_state_bound(cpu: dict, s_ref, chunk: int, K=None):
+    """Elementwise bound for bf16 chunk-initial states against the oracle's s_ref
+    [b, H, nC, P, S]. One rounding to nearest even moves a value v by at most half an ulp,
+    which is at most 2^-8 |v| (v just above a power of two); so 2^-8 |s_ref|, plus 1e-3
+    rms(s_ref) for the fp32 arithmetic before it. With a segment plan of K chunks per
+    segment, a chunk past the first segment is completed as bf16(L_c + f S_in) from the
+    bf16 relative state L_c = S_c - f S_in and the bf16 entering state S_in (f its exact
+    decay to the chunk): the two earlier roundings add at most 2^-8 (|L_c| + f |S_in|)
+    <= 2^-8 (|S_c| + 2 f |S_in|)."""
+    r = float(np.sqrt(np.mean(s_ref * s_ref)))
+    bound = 2.0 ** -8 * np.abs(s_ref) + 1e-3 * r
+    if K:
+        A = cpu["A"].double().numpy()
+        dtv = cpu["dt"].double().numpy()  # [b, L, H]
+        for c in range(K, s_ref.shape[2]):
+            c0 = (c // K) * K
+            f = np.exp(A[None, :] * dtv[:, c0 * chunk:c * chunk, :].sum(axis=1))  # [b, H]
+            fs = np.abs(f[:, :, None, None] * s_ref[:, :, c0])
+            bound[:, :, c] += 2.0 ** -8 * (np.abs(s_ref[:, :, c]) + 2.0 * fs)
+    return bound

@@ -74,78 +74,83 @@ def test_workspace_sizes():
     s = shape(states_dtype=ssd.SSD_BF16)
     nchunks = 512 // 256
     elems = 2 * 8 * nchunks * 64 * 128
-    assert ssd.state_pass_workspace_bytes(s) == elems * 4
     dec = 2 * 8 * 512 * 4
-    # bf16 inputs and states: the forward pass takes the segmented state pass, whose
-    # buffers replace the per-chunk increments; at least one segment's end state (fp32)
-    # and entering state (bf16) per (batch, head)
-    seg = ssd.state_seg_workspace_bytes(s)
+    # bf16 inputs and states: the state pass is segmented; its workspace (and that of the
+    # segmented pair) holds the segment buffers: at least one segment's end state (fp32) and
+    # entering state (bf16) per (batch, head); the forward's adds G, dt_t and the states
+    seg = ssd.state_pass_segmented_workspace_bytes(s)
     assert seg >= 2 * 8 * 64 * 128 * (4 + 2)
+    assert ssd.state_pass_workspace_bytes(s) == seg
     assert ssd.forward_workspace_bytes(s) == 2 * dec + seg + elems * 2
     # fp32 states: no segment plan, the two-kernel pass's increments
     s32 = shape(states_dtype=ssd.SSD_F32)
+    assert ssd.state_pass_workspace_bytes(s32) == elems * 4
     assert ssd.forward_workspace_bytes(s32) == 2 * dec + elems * 4 + elems * 4
     with pytest.raises(ssd.SSDError):
         ssd.forward_workspace_bytes(shape(ngroups=3))
     for kw in (dict(states_dtype=ssd.SSD_F32), dict(in_dtype=ssd.SSD_F32, states_dtype=ssd.SSD_F32),
                dict(headdim=128)):
         with pytest.raises(ssd.SSDError) as e:
-            ssd.state_seg_workspace_bytes(shape(**kw))
+            ssd.state_pass_segmented_workspace_bytes(shape(**kw))
         assert e.value.code == 4, kw
     # dstate 256 (128-token sub-blocks inside the kernel) has a plan at every chunk length
     for t in (64, 128, 256):
-        assert ssd.state_seg_workspace_bytes(shape(dstate=256, chunk=t)) > 0
-    assert ssd.state_seg_workspace_bytes(shape(seqlen=0)) == 0
+        assert ssd.state_pass_segmented_workspace_bytes(shape(dstate=256, chunk=t)) > 0
+    assert ssd.state_pass_segmented_workspace_bytes(shape(seqlen=0)) == 0
 
 
 def test_segment_plan_query():
     # the 2.7B layer: 2 heads per workgroup, 11 chunks per segment, 6 segments (480
     # 4-wave workgroups, two per CU)
     s = ssd.make_shape(2, 16384, 80, 64, 128, 1, 256, ssd.SSD_BF16)
-    assert ssd.state_seg_plan(s) == (2, 11, 6)
+    assert ssd.segment_plan(s) == (2, 11, 6)
     # the long layer at dstate 256: 2 heads x 43 chunks, 6 segments (240 workgroups)
-    assert ssd.state_seg_plan(ssd.make_shape(1, 65536, 80, 64, 256, 8, 256, ssd.SSD_BF16)) == (2, 43, 6)
+    assert ssd.segment_plan(ssd.make_shape(1, 65536, 80, 64, 256, 8, 256, ssd.SSD_BF16)) == (2, 43, 6)
     lib = ssd.load_library()
-    assert lib.ssd_state_seg_plan(ctypes.byref(s), None, None, None) == 0
+    assert lib.ssd_segment_plan(ctypes.byref(s), None, None, None) == 0
     for kw in (dict(states_dtype=ssd.SSD_F32), dict(headdim=128), dict(seqlen=0)):
         with pytest.raises(ssd.SSDError) as e:
-            ssd.state_seg_plan(shape(**kw))
+            ssd.segment_plan(shape(**kw))
         assert e.value.code == 4, kw
-    assert lib.ssd_state_seg_plan(ctypes.byref(shape(ngroups=3)), None, None, None) == 2
+    assert lib.ssd_segment_plan(ctypes.byref(shape(ngroups=3)), None, None, None) == 2
 
 
 def test_segmented_entry_points_reject_before_launch():
     lib = ssd.load_library()
     s = shape()
     f = _v(FAKE)
-    need = ssd.state_seg_workspace_bytes(s)
-    # x A B G dt_t h0 states final
+    need = ssd.state_pass_segmented_workspace_bytes(s)
+    # x A B G dt_t h0 seg_relative_states final
     args = [f, f, f, f, f, None, f, None]
     for i in (0, 1, 2, 3, 4, 6):  # required pointers
         bad = list(args)
         bad[i] = None
-        assert lib.ssd_state_seg(ctypes.byref(s), *bad, f, need, None) == 1, i
-    assert lib.ssd_state_seg(ctypes.byref(s), *args, f, need - 1, None) == 5
-    assert lib.ssd_state_seg(ctypes.byref(s), *args, None, need, None) == 5
+        assert lib.ssd_state_pass_segmented(ctypes.byref(s), *bad, f, need, None) == 1, i
+    assert lib.ssd_state_pass_segmented(ctypes.byref(s), *args, f, need - 1, None) == 5
+    assert lib.ssd_state_pass_segmented(ctypes.byref(s), *args, None, need, None) == 5
     bad = list(args)
     bad[6] = _v(FAKE + 4)
-    assert lib.ssd_state_seg(ctypes.byref(s), *bad, f, need, None) == 6
+    assert lib.ssd_state_pass_segmented(ctypes.byref(s), *bad, f, need, None) == 6
     s32 = shape(states_dtype=ssd.SSD_F32)
-    assert lib.ssd_state_seg(ctypes.byref(s32), *args, f, need, None) == 4
-    assert lib.ssd_state_seg(ctypes.byref(shape(ngroups=3)), *args, f, need, None) == 2
-    # x B C G dt_t states D y
-    oargs = [f, f, f, f, f, f, None, f]
-    for i in (0, 1, 2, 3, 4, 5, 7):
+    assert lib.ssd_state_pass_segmented(ctypes.byref(s32), *args, f, need, None) == 4
+    assert lib.ssd_state_pass_segmented(ctypes.byref(shape(ngroups=3)), *args, f, need, None) == 2
+    # x B C G dt_t D seg_relative_states y
+    oargs = [f, f, f, f, f, None, f, f]
+    for i in (0, 1, 2, 3, 4, 6, 7):
         bad = list(oargs)
         bad[i] = None
-        assert lib.ssd_chunk_out_seg(ctypes.byref(s), *bad, f, need, None) == 1, i
-    assert lib.ssd_chunk_out_seg(ctypes.byref(s), *oargs, f, need - 1, None) == 5
-    assert lib.ssd_chunk_out_seg(ctypes.byref(s), *oargs, None, need, None) == 5
-    assert lib.ssd_chunk_out_seg(ctypes.byref(s32), *oargs, f, need, None) == 4
+        assert lib.ssd_chunk_out_segmented(ctypes.byref(s), *bad, f, need, None) == 1, i
+    assert lib.ssd_chunk_out_segmented(ctypes.byref(s), *oargs, f, need - 1, None) == 5
+    assert lib.ssd_chunk_out_segmented(ctypes.byref(s), *oargs, None, need, None) == 5
+    assert lib.ssd_chunk_out_segmented(ctypes.byref(s32), *oargs, f, need, None) == 4
+    bad = list(oargs)
+    bad[3] = _v(FAKE + 4)
+    assert lib.ssd_chunk_out_segmented(ctypes.byref(s), *bad, f, need, None) == 6
     # the empty sequence: the final state only (none wanted here), no launch
     e = shape(seqlen=0)
-    assert lib.ssd_state_seg(ctypes.byref(e), None, f, *[None] * 6, None, 0, None) == 0
-    assert lib.ssd_chunk_out_seg(ctypes.byref(e), *[None] * 8, None, 0, None) == 0
+    assert lib.ssd_state_pass_segmented(ctypes.byref(e), None, f, *[None] * 6, None, 0,
+                                        None) == 0
+    assert lib.ssd_chunk_out_segmented(ctypes.byref(e), *[None] * 8, None, 0, None) == 0
 
 
 def _round256(n):

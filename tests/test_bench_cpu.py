@@ -29,8 +29,9 @@ def test_algorithmic_bytes_at_the_bench_shape():
     states = 2 * 80 * 64 * 64 * 128      # chunk-initial states, elements
     assert by["chunk_out"] == x + 2 * bc + 2 * dec + states * 2 + 80 * 4 + y
     # over segment-relative states (8 segments): plus the 7 states entering segments 1..
+    # and each chunk's decay from its segment's start
     by8, _ = bench.algorithmic(w, 8)
-    assert by8["chunk_out"] == by["chunk_out"] + 7 * 2 * 80 * 64 * 128 * 2
+    assert by8["chunk_out"] == by["chunk_out"] + 7 * 2 * 80 * 64 * 128 * 2 + 2 * 80 * 64 * 4
     assert by["chunk_state"] == x + bc + dec + 80 * 4 + states * 4
     # the page's per-head dense flops: 2 T^2 S + 2 T S P + 2 T^2 P per (batch, chunk, head)
     assert fl["chunk_out"] == 2 * 64 * 80 * (2.0 * 256 * 256 * 128 + 2.0 * 256 * 128 * 64
@@ -55,7 +56,7 @@ def test_recorded_traffic_is_consistent():
         from state_space_sequence_chunk_amd import ssd
         sh = ssd.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
                             w.chunk, ssd.SSD_BF16)
-        nseg = ssd.state_seg_plan(sh)[2]
+        nseg = ssd.segment_plan(sh)[2]
         assert nseg == 6
         by, _ = bench.algorithmic(w, nseg)
         assert abs(t - by["chunk_out"]) <= 0.01 * by["chunk_out"]

@@ -36,7 +36,7 @@ def _plan(w, chunk=None):
     sh = ssd.make_shape(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
                         chunk or w.chunk, gen.torch_dtype(w.dtype))
     try:
-        return ssd.state_seg_plan(sh)
+        return ssd.segment_plan(sh)
     except ssd.SSDError:
         return None
 

@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import (SSM_MAX_TOL_FP32, SSM_RMS_TOL, TOL, dev, gpu_forward, make, needs_gpu,
-                        np64, oracle_forward, reduced)
+from gpu_common import (SSM_MAX_TOL_FP32, SSM_RMS_TOL, TOL, bf16_state_bound, dev, gpu_forward,
+                        make, needs_gpu, np64, oracle_forward, reduced)
 from metrics import max_rel_rms, rms_rel
 from state_space_sequence_chunk_amd import inputs as gen
 from state_space_sequence_chunk_amd import ssd
@@ -102,11 +102,15 @@ def test_state_pass_stage(name, states):
         return
     got = np64(states_t)
     if st_dt == torch.bfloat16:
-        # Stored in bf16: rounding to nearest even alone moves each value by up to 2^-9 of
-        # itself, so the bound is elementwise: 2^-8 |ref| (rounding, with margin) plus
-        # 1e-3 rms(ref) for the fp32 arithmetic before the rounding.
+        # Stored in bf16: the bound of one rounding, plus the roundings of the completion
+        # of segment-relative states where the shape has a segment plan
         r = float(np.sqrt(np.mean(s_ref * s_ref)))
-        excess = np.abs(got - s_ref) - (2.0 ** -8 * np.abs(s_ref) + 1e-3 * r)
+        try:
+            K = ssd.segment_plan(sh)[1]
+        except ssd.SSDError:
+            K = None
+        bound = bf16_state_bound(cpu, s_ref, w.chunk, K)
+        excess = np.abs(got - s_ref) - bound
         _print(f"{name}/{states}: bf16 states, worst excess over the rounding bound "
                f"{excess.max() / r:.2e} rms")
         assert excess.max() <= 0.0

@@ -1,4 +1,4 @@
-"""The segmented state pass (ssd_state_seg + ssd_chunk_out_seg, which ssd_forward takes
+"""The segmented state pass (ssd_state_pass_segmented + ssd_chunk_out_segmented, which ssd_forward takes
 for bf16 inputs with bf16 states at headdim 64, dstate 64, 128 or 256) against the fp64
 oracle on the GPU.
 
@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import SSM_RMS_TOL, TOL, make, needs_gpu, oracle_forward
+from gpu_common import SSM_RMS_TOL, TOL, bf16_state_bound, make, needs_gpu, oracle_forward
 from metrics import max_rel_rms, rms_rel
 from state_space_sequence_chunk_amd import inputs as gen
 from state_space_sequence_chunk_amd import ssd
@@ -95,9 +95,39 @@ def test_forward_segmented_ssm_only(name):
 
 
 def test_staged_segmented_equals_forward():
-    """cumsum -> ssd_state_seg -> ssd_chunk_out_seg gives ssd_forward's y and final state
-    bit for bit (the same kernels in the same order)."""
+    """ssd_state_pass_segmented -> ssd_chunk_out_segmented gives ssd_forward's y and final
+    state bit for bit (the same kernels in the same order)."""
     w = CASES["short-seg-2x11"]
+    cpu, d = make(w)
+    y1, f1 = _forward(w, d)
+    sh = ssd.shape_of(d["x"], d["B"], w.chunk)
+    b, L, H, P = d["x"].shape
+    S = d["B"].shape[3]
+    nC = -(-L // w.chunk)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    st = torch.empty((b, H, nC, P, S), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((b, H, P, S), **f32)
+    y = torch.empty((b, L, H, P), **f32)
+    G = torch.empty((b, H, L), **f32)
+    dtt = torch.empty((b, H, L), **f32)
+    ws = torch.empty(ssd.state_pass_segmented_workspace_bytes(sh), dtype=torch.uint8,
+                     device="cuda")
+    ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dtt)
+    ssd.ssd_state_pass_segmented(sh, d["x"], d["A"], d["B"], G, dtt, d["h0"], st, fin, ws)
+    ssd.ssd_chunk_out_segmented(sh, d["x"], d["B"], d["C"], G, dtt, d["D"], st, y, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1) and torch.equal(fin, f1)
+
+
+@pytest.mark.parametrize("name", ["short-seg-2x11", "ragged-1x2", "groups4-2x4", "s256-2x3",
+                                  "s256-t64-1x2", "one-seg"])
+def test_boundary_stages_compose_to_forward(name):
+    """The boundary's three stages, ssd_chunk_cumsum -> ssd_state_pass -> ssd_chunk_out,
+    give ssd_forward's y and final state bit for bit: ssd_state_pass completes the
+    segment-relative states to the true chunk-initial ones with the arithmetic the output
+    kernel uses for the same sum, and both routes form G with the same routine. The
+    states it returns are the true ones (against the oracle, within bf16 rounding)."""
+    w = CASES[name]
     cpu, d = make(w)
     y1, f1 = _forward(w, d)
     sh = ssd.shape_of(d["x"], d["B"], w.chunk)
@@ -110,12 +140,23 @@ def test_staged_segmented_equals_forward():
     st = torch.empty((b, H, nC, P, S), dtype=torch.bfloat16, device="cuda")
     fin = torch.empty((b, H, P, S), **f32)
     y = torch.empty((b, L, H, P), **f32)
-    ws = torch.empty(ssd.state_seg_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, ssd.state_pass_workspace_bytes(sh)), dtype=torch.uint8,
+                     device="cuda")
     ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dtt)
-    ssd.ssd_state_seg(sh, d["x"], d["A"], d["B"], G, dtt, d["h0"], st, fin, ws)
-    ssd.ssd_chunk_out_seg(sh, d["x"], d["B"], d["C"], G, dtt, st, d["D"], y, ws)
+    ssd.ssd_state_pass(sh, d["x"], d["A"], d["B"], G, dtt, d["h0"], st, fin, ws)
+    ssd.ssd_chunk_out(sh, d["x"], d["B"], d["C"], G, dtt, st, d["D"], y)
     torch.cuda.synchronize()
-    assert torch.equal(y, y1) and torch.equal(fin, f1)
+    same_y, same_f = bool(torch.equal(y, y1)), bool(torch.equal(fin, f1))
+    _print(f"{name} (plan {ssd.segment_plan(sh)}): staged == forward: y {same_y}, final {same_f}")
+    assert same_y and same_f
+    # (a completed state S_c = bf16(L_c + 2^{D_c} S_in) carries the roundings of L_c and
+    # S_in as well as its own)
+    ref = oracle_forward(cpu, emit_every=w.chunk)["states"]
+    got = st.double().cpu().numpy()
+    bound = bf16_state_bound(cpu, ref, w.chunk, ssd.segment_plan(sh)[1])
+    r = float(np.max(np.abs(got - ref) / bound))
+    _print(f"{name}: true states, worst error / bound {r:.3f}")
+    assert r <= 1.0
 
 
 def _within_bf16_rounding(got, ref):
@@ -127,7 +168,7 @@ def _within_bf16_rounding(got, ref):
 
 
 def test_segmented_recorded_states_are_segment_relative():
-    """ssd_state_seg's recorded states: the true chunk-initial state minus the part
+    """ssd_state_pass_segmented's recorded states: the true chunk-initial state minus the part
     carried in from before the segment. In the first segment (which starts from h0) they
     are the true states; at the first chunk of every later segment they are zero."""
     w = CASES["ragged-1x2"]  # two chunks per segment
@@ -136,13 +177,13 @@ def test_segmented_recorded_states_are_segment_relative():
     b, L, H, P = d["x"].shape
     S = d["B"].shape[3]
     nC = -(-L // w.chunk)
-    f32 = dict(dtype=torch.float32, device="cuda")
-    G = torch.empty((b, H, L), **f32)
-    dtt = torch.empty((b, H, L), **f32)
     st = torch.empty((b, H, nC, P, S), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(ssd.state_seg_workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    G = torch.empty((b, H, L), dtype=torch.float32, device="cuda")
+    dtt = torch.empty_like(G)
+    ws = torch.empty(ssd.state_pass_segmented_workspace_bytes(sh), dtype=torch.uint8,
+                     device="cuda")
     ssd.ssd_chunk_cumsum(sh, d["dt"], d["A"], G, dtt)
-    ssd.ssd_state_seg(sh, d["x"], d["A"], d["B"], G, dtt, d["h0"], st, None, ws)
+    ssd.ssd_state_pass_segmented(sh, d["x"], d["A"], d["B"], G, dtt, d["h0"], st, None, ws)
     torch.cuda.synchronize()
     ref = oracle_forward(cpu, emit_every=w.chunk)
     true = ref["states"]  # [b, H, nC, P, S] fp64: the state entering each chunk

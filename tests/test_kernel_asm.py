@@ -81,3 +81,18 @@ def test_no_wide_store_data_overwritten_early(path):
     hits = wide_store_overwrites(open(path).read())
     assert not hits, "\n".join(f"{os.path.basename(path)}:{ln}: {s} -> {t} ({k[:60]})"
                                for k, ln, s, t in hits[:10])
+
+
+def test_log2_decay_is_never_fused():
+    """G = log2(e) * (running sum of A dt) is a rounded product wherever it is formed: the
+    cumulative-decay kernel stores it, and the output kernels that form it themselves
+    subtract it (G_e - G_j). Had the compiler fused that multiply into the subtraction (one
+    FMA with -log2(e)), the in-kernel G would skip a rounding the stored one has, and the
+    fused forward would no longer give the staged entry points' bits. No kernel may carry
+    log2(e) (0x3fb8aa3b, negated 0xbfb8aa3b) as an FMA operand."""
+    hits = []
+    for path in ASM:
+        for n, line in enumerate(open(path).read().splitlines(), 1):
+            if re.match(r"\s*v_fma", line) and re.search(r"0x[3b]fb8aa3b", line):
+                hits.append(f"{os.path.basename(path)}:{n}: {line.strip()}")
+    assert not hits, "\n".join(hits[:10])
