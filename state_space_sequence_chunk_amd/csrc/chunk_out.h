@@ -107,6 +107,20 @@ struct OutCfg {
                : HEAD_BYTES + B_BYTES <= LDS_MAX;
     static constexpr size_t REGION0 =
         SHARED ? (B_IN_LDS && B_BYTES > HEAD_BYTES ? B_BYTES : HEAD_BYTES) : HEAD_BYTES;
+    // SHARED mode with B too large for LDS: the tiles are built in passes over runs of
+    // B_PASS 16-row j-tiles, each run's B rows staged over the per-head region (free until
+    // the first head is staged); B_PASS is the largest divisor of NIT whose rows fit there.
+    // 0 when B is staged whole or the tiles are not shared.
+    static constexpr size_t BT_BYTES = (size_t)16 * BS * sizeof(TIn);  // one j-tile's B rows
+    static constexpr int pass_tiles() {
+        if (!SHARED || B_IN_LDS) return 0;
+        int best = 0;
+        for (int n = 1; n < NIT; ++n)
+            if (NIT % n == 0 && n * BT_BYTES <= HEAD_BYTES) best = n;
+        return best;
+    }
+    static constexpr int B_PASS = pass_tiles();
+    static constexpr int NBVP = B_PASS * 16 * S / VE / NTHR;  // B vectors / thread and pass
     static constexpr size_t BASE_BYTES =
         SHARED ? REGION0 + TILE_BYTES : HEAD_BYTES + (B_IN_LDS ? B_BYTES : 0);
     static constexpr size_t LDS_BYTES = BASE_BYTES + DEC_BYTES;
@@ -288,11 +302,33 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
             *(Vec16*)(s_b + r * BS + col) = pb[i];
         }
     }
-    // B rows of j-tile jt as the A operand of S^T = B_j C_i^T (lane: row j, 8 dstate values)
-    auto load_bfrag = [&](Frag<TIn>& f, int jt, int ks) {
+    // B_PASS: the B rows of j-tiles j0 .. j0 + B_PASS - 1 into s_b (rows past the chunk's
+    // real tokens as zeros)
+    auto stage_b_pass = [&](int j0) {
+        if constexpr (Cfg::B_PASS > 0) {
+            Vec16 pb[Cfg::NBVP];
+#pragma unroll
+            for (int i = 0; i < Cfg::NBVP; ++i) {
+                const int v = tid + i * NTHR;
+                const int r = j0 * 16 + v / (S / VE), col = (v % (S / VE)) * VE;
+                pb[i] = r < rows ? *(const Vec16*)(bg + (size_t)r * grow + col)
+                                 : Vec16{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < Cfg::NBVP; ++i) {
+                const int v = tid + i * NTHR;
+                const int r = v / (S / VE), col = (v % (S / VE)) * VE;
+                *(Vec16*)(s_b + r * BS + col) = pb[i];
+            }
+        }
+    };
+    if constexpr (Cfg::B_PASS > 0) stage_b_pass(0);
+    // B rows of j-tile jt as the A operand of S^T = B_j C_i^T (lane: row j, 8 dstate values);
+    // j0: the first j-tile staged in s_b
+    auto load_bfrag = [&](Frag<TIn>& f, int jt, int ks, int j0 = 0) {
         const int s0 = ks * 32 + g4 * 8;
-        if constexpr (Cfg::B_IN_LDS)
-            load8(f, s_b + (jt * 16 + l16) * BS + s0, s0 < S);
+        if constexpr (Cfg::B_IN_LDS || Cfg::B_PASS > 0)
+            load8(f, s_b + ((jt - j0) * 16 + l16) * BS + s0, s0 < S);
         else
             load8(f, bg + (size_t)(jt * 16 + l16) * grow + s0, s0 < S && jt * 16 + l16 < rows);
     };
@@ -306,25 +342,36 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
         if (corr && tid < NH) s_dec[tid] = dec_in[((size_t)b * H + h_first + tid) * nC + c];
     }
     if constexpr (Cfg::SHARED) {
-        // build this wave's interaction tiles once for all heads of the workgroup
-        if constexpr (Cfg::B_IN_LDS) lds_barrier();
+        // build this wave's interaction tiles once for all heads of the workgroup (in
+        // passes over runs of j-tiles when only a run's B rows fit in LDS)
+        constexpr int JB = Cfg::B_PASS > 0 ? Cfg::B_PASS : Cfg::NIT;
         const int itmax = its[1];
-        for (int jt = 0; jt <= itmax; ++jt) {
-            f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                Frag<TIn> bfr;
-                load_bfrag(bfr, jt, ks);
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    if (jt <= its[q]) mma(st[q], bfr, cf[q][ks]);
+        // every wave runs every pass (the barriers inside), with no tiles where j0 > itmax
+        for (int j0 = 0; j0 < Cfg::NIT; j0 += JB) {
+            if constexpr (Cfg::B_PASS > 0) {
+                if (j0 > 0) {
+                    lds_barrier();  // every wave is done with the previous run's rows
+                    stage_b_pass(j0);
+                }
             }
+            if constexpr (Cfg::B_IN_LDS || Cfg::B_PASS > 0) lds_barrier();
+            for (int jt = j0; jt <= min(itmax, j0 + JB - 1); ++jt) {
+                f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                if (jt > its[q]) continue;
-                TIn* dst = tile_ptr(q, jt);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    Frag<TIn> bfr;
+                    load_bfrag(bfr, jt, ks, j0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[r] = from_f32<TIn>(st[q][r]);
+                    for (int q = 0; q < 2; ++q)
+                        if (jt <= its[q]) mma(st[q], bfr, cf[q][ks]);
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (jt > its[q]) continue;
+                    TIn* dst = tile_ptr(q, jt);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[r] = from_f32<TIn>(st[q][r]);
+                }
             }
         }
         if (wave == 0) {
