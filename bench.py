@@ -32,12 +32,12 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
 
 
-def algorithmic(w, nseg=None):
-    """Bytes each stage must move (inputs read once, outputs written once) and the
-    per-head dense flop count of the matrix stages. With nseg (the segmented state pass's
-    segment count), chunk_out's bytes include the states entering segments 1.. (bf16) and
-    each chunk's decay from its segment's start, which it reads to complete the
-    segment-relative chunk states."""
+def algorithmic_split(w, nseg=None):
+    """(read, written) bytes each stage must move: inputs read once, outputs written once.
+    With nseg (the segmented state pass's segment count), chunk_out also reads the states
+    entering segments 1.. (bf16) and each chunk's decay from its segment's start, to
+    complete the segment-relative chunk states; the state pass's per-segment end states
+    are not counted (a few % at most)."""
     B, L, H, P, S, G, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     e = 2 if w.dtype == "bf16" else 4
     es = e  # chunk-initial states are stored in the input dtype
@@ -48,17 +48,25 @@ def algorithmic(w, nseg=None):
     bc = B * L * G * S * e
     h0 = B * H * P * S * 4 if w.h0 else 0
     fin = B * H * P * S * 4
-    by = {
-        "cumsum": B * L * H * e + H * 4 + 2 * dec,
-        "chunk_state": x + bc + dec + H * 4 + n_states * 4,
-        "state_carry": n_states * 4 + B * H * nC * 4 + h0 + n_states * es + fin,
-        # the segmented pass: inputs once, the (segment-relative) chunk states and the
-        # final state once; its per-segment states are not counted (a few % at most)
-        "state_seg": x + bc + 2 * dec + H * 4 + h0 + n_states * es + fin,
-        "chunk_out": x + 2 * bc + 2 * dec + n_states * es + H * 4 + B * L * H * P * 4,
+    rw = {
+        "cumsum": (B * L * H * e + H * 4, 2 * dec),
+        "chunk_state": (x + bc + dec + H * 4, n_states * 4),
+        "state_carry": (n_states * 4 + B * H * nC * 4 + h0, n_states * es + fin),
+        "state_seg": (x + bc + 2 * dec + H * 4 + h0, n_states * es + fin),
+        "chunk_out": (x + 2 * bc + 2 * dec + n_states * es + H * 4, B * L * H * P * 4),
     }
     if nseg:
-        by["chunk_out"] += (nseg - 1) * B * H * P * S * 2 + B * H * nC * 4
+        r, wr = rw["chunk_out"]
+        rw["chunk_out"] = (r + (nseg - 1) * B * H * P * S * 2 + B * H * nC * 4, wr)
+    return rw
+
+
+def algorithmic(w, nseg=None):
+    """Bytes each stage must move (the sums of algorithmic_split) and the per-head dense
+    flop count of the matrix stages."""
+    B, L, H, P, S, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk
+    nC = L // T
+    by = {k: r + wr for k, (r, wr) in algorithmic_split(w, nseg).items()}
     fl = {
         "chunk_state": 2.0 * B * nC * H * T * P * S,
         "chunk_out": B * nC * H * (2.0 * T * T * S + 2.0 * T * S * P + 2.0 * T * T * P),
@@ -192,6 +200,33 @@ def measure_hbm_ceiling(torch, ssd, stream, nbytes=1 << 30, reps=10, workgroups=
         out[kind] = max(out[f"{kind}_plain"], out[f"{kind}_nontemporal"])
     del src, dst, sink
     return {"unit": "GB/s", "bytes": nbytes, **out}
+
+
+def measure_mix_ceiling(torch, ssd, stream, read_bytes, write_bytes, reps=10):
+    """The stream ceiling of one kernel's own traffic: ssd_probe_mix reading read_bytes and
+    writing write_bytes in one pass (ordinary and non-temporal accesses, the better one),
+    in GB/s of DRAM traffic, and the time that takes."""
+    rb, wb = read_bytes // 16 * 16, write_bytes // 16 * 16
+    src = torch.ones(max(rb, 16) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty(max(wb, 16) // 4, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for mode in (0, 1):
+        fn = lambda: ssd.probe_mix(src, rb, dst, wb, mode=mode, stream=stream)  # noqa: E731
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        if best is None or ms < best:
+            best = ms
+    del src, dst
+    return {"read_bytes": rb, "write_bytes": wb, "ms": best,
+            "GBps": (rb + wb) / (best * 1e-3) / 1e9}
 
 
 def cpu_model():
@@ -528,10 +563,29 @@ def main():
             continue
         v["GBps"] = v["bytes"] / (v["ms"] * 1e-3) / 1e9
         v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
+    # each stage against a stream kernel that moves the same bytes in the same read/write mix
+    rw = algorithmic_split(w, ssd.segment_plan(sh)[2] if segmented else None)
+    rw["state_pass"] = rw["state_seg"] if segmented else tuple(
+        a + b for a, b in zip(rw["chunk_state"], rw["state_carry"]))
+    for k in ("cumsum", "state_pass", "chunk_out"):
+        v = kernels[k]
+        ceil = measure_mix_ceiling(torch, ssd, stream, *rw[k])
+        v["stream_ceiling"] = {"GBps": ceil["GBps"], "ms": ceil["ms"],
+                               "read_bytes": ceil["read_bytes"],
+                               "write_bytes": ceil["write_bytes"]}
+        v["frac_of_stream_ceiling"] = v["GBps"] / ceil["GBps"]
     co = kernels["chunk_out"]
     peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-    co["eff_TFLOPs"] = co["flops_per_head_dense"] / (co["ms"] * 1e-3) / 1e12
-    co["eff_mfma_frac"] = co["eff_TFLOPs"] / peak_tf
+    # per-head equivalent: the method's dense flops with C B^T counted once per head (the
+    # convention of the pages' per-head kernels); executed: what the launch runs on the
+    # matrix cores (C B^T once per workgroup when its heads share it), from the library's plan
+    co["per_head_equiv_TFLOPs"] = co["flops_per_head_dense"] / (co["ms"] * 1e-3) / 1e12
+    co["per_head_equiv_mfma_frac"] = co["per_head_equiv_TFLOPs"] / peak_tf
+    nh_wg, shared, executed = ssd.chunk_out_plan(sh)
+    co["plan"] = {"heads_per_workgroup": nh_wg, "shared_tiles": shared}
+    co["executed_flops"] = executed
+    co["executed_TFLOPs"] = executed / (co["ms"] * 1e-3) / 1e12
+    co["executed_mfma_frac"] = co["executed_TFLOPs"] / peak_tf
     dom = "chunk_out"
     roofline = {"bound": "hbm", "achieved": kernels[dom]["GBps"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": kernels[dom]["GBps"] / HBM_PEAK_GBS,

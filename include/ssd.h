@@ -97,6 +97,16 @@ ssd_status ssd_forward_workspace_bytes(const ssd_shape* shape, size_t* bytes);
 ssd_status ssd_state_pass_workspace_bytes(const ssd_shape* shape, size_t* bytes);
 
 /*
+ * The plan of the output kernel that ssd_forward launches for a shape (host-only): heads
+ * per workgroup, whether the interaction tiles C B^T are built once per workgroup and
+ * shared by its heads (1) or rebuilt per head (0), and the matrix-core flops one launch
+ * executes (every 16x16 product tile counted at its padded K, the shared tiles once per
+ * workgroup). Any output may be NULL. SSD_ERR_UNSUPPORTED for seqlen 0.
+ */
+ssd_status ssd_chunk_out_plan(const ssd_shape* shape, int32_t* heads_per_workgroup,
+                              int32_t* shared_tiles, double* mfma_flops);
+
+/*
  * Stage 1 -- per-chunk cumulative decay (section "Kernel 1: Computing cumulative sums").
  * For token t of chunk c = t / chunk:
  *     G[b,h,t]    = log2(e) * sum_{k = c*chunk .. t} A[h] * dt[b,k,h]   (inclusive, fp32)

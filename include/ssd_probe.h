@@ -12,8 +12,11 @@
  *                    cannot be dropped); sink must hold 16 bytes.
  *   ssd_probe_write  writes `bytes` of a constant pattern to dst.
  *   ssd_probe_copy   copies `bytes` from src to dst (the buffers must not overlap).
+ *   ssd_probe_mix    reads `read_bytes` from src and writes `write_bytes` to dst in one pass,
+ *                    loads and stores in that proportion all along the run (the stream mix
+ *                    of a kernel that reads R and writes W bytes); either size may be 0.
  *
- * `bytes` must be a positive multiple of 16 and every pointer 16-byte aligned (else
+ * `bytes` (for ssd_probe_mix the larger of the two sizes) must be a positive multiple of 16 and every pointer 16-byte aligned (else
  * SSD_ERR_SHAPE or SSD_ERR_ALIGN from ssd.h's status codes, nothing enqueued). `mode` 0 uses
  * ordinary vector loads and stores, 1 non-temporal ones (others: SSD_ERR_UNSUPPORTED).
  * `workgroups` sets the grid (256 threads each; 0 picks 8 per compute unit).
@@ -35,6 +38,8 @@ ssd_status ssd_probe_read(const void* src, size_t bytes, void* sink, int mode, i
 ssd_status ssd_probe_write(void* dst, size_t bytes, int mode, int workgroups, void* stream);
 ssd_status ssd_probe_copy(const void* src, void* dst, size_t bytes, int mode, int workgroups,
                           void* stream);
+ssd_status ssd_probe_mix(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+                         int mode, int workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -579,6 +579,26 @@ inline int heads_per_block(const Dims& d, size_t lds_bytes, int max_nh = 1 << 30
     return best;
 }
 
+// The launch plan of chunk_out_kernel for a shape (host-only): heads per workgroup, whether
+// the interaction tiles are shared by the workgroup's heads, and the matrix-core flops the
+// launch executes (each mma() call is 2 x 16 x 16 x 32 flops, on bf16 16x16x32 or eight
+// fp32 16x16x4 instructions): the tiles (once per workgroup when shared, else per head),
+// per head the carried-state product C_i . S_c (twice with split fp32 states) and the
+// masked products W x over the row tiles' column-tile pairs.
+template <typename TIn, typename TS, int P, int S, int T, bool SEGC>
+OutPlan out_plan_t(const Dims& d) {
+    using Cfg = OutCfg<TIn, TS, P, S, T, SEGC>;
+    const int nh = heads_per_block(d, Cfg::LDS_BYTES, SEGC ? 256 : 1 << 30);
+    const double nblocks = (double)d.batch * d.nchunks() * (d.nheads / nh);
+    long pairs = 0;  // column-tile pairs of every row tile
+    for (int it = 0; it < Cfg::NIT; ++it) pairs += it / 2 + 1;
+    const long tiles = (long)Cfg::NTILE * Cfg::NKS;
+    const long per_head = (long)Cfg::NIT * Cfg::NPT * Cfg::NKS * (StateFrag<TIn, TS>::kSplit ? 2 : 1) +
+                          (long)Cfg::NPT * pairs;
+    const double calls = (Cfg::SHARED ? (double)tiles : (double)tiles * nh) + (double)per_head * nh;
+    return OutPlan{nh, Cfg::SHARED, calls * nblocks * 2.0 * 16 * 16 * 32, (double)Cfg::LDS_BYTES};
+}
+
 template <typename TIn, typename TS, typename TY, int P, int S, int T, bool SEGC = false>
 hipError_t run_out(const void* x, const void* Bm, const void* Cm, const float* G,
                    const float* dt_t, const void* states, const float* D, void* y,

@@ -1,5 +1,5 @@
-// HBM stream probes (declared in include/ssd_probe.h): grid-stride read, write and copy
-// kernels of 16-byte vectors, each thread keeping UNR of them in flight per iteration, so
+// HBM stream probes (declared in include/ssd_probe.h): grid-stride read, write, copy and
+// mixed read/write kernels of 16-byte vectors, each thread keeping UNR of them in flight per iteration, so
 // that the measured rate is the DRAM's rather than a latency limit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -72,6 +72,32 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(const V4* __restri
         if (base + u * kThreads < n) st<NT>(dst + base + u * kThreads, ld<NT>(src + base + u * kThreads));
 }
 
+// Reads nr vectors and writes nw in one pass: index i of n = max(nr, nw) reads vector
+// i * nr / n and writes vector i * nw / n (each vector of the shorter buffer is touched by
+// one or more consecutive indices, so the loads and stores stay in the same proportion all
+// along the run). The written value depends on the loaded one, so no load can be dropped.
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void probe_mix_kernel(const V4* __restrict__ src, size_t nr,
+                                                           V4* __restrict__ dst, size_t nw,
+                                                           size_t n) {
+    const size_t stride = (size_t)gridDim.x * kThreads * kUnroll;
+    const V4 k = {0x3f800000u, 0u, 0x3f800000u, 0u};
+    for (size_t base = (size_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < n;
+         base += stride) {
+        V4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t i = base + u * kThreads;
+            v[u] = (i < n && nr) ? ld<NT>(src + i * nr / n) : k;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t i = base + u * kThreads;
+            if (i < n && nw) st<NT>(dst + i * nw / n, v[u] ^ k);
+        }
+    }
+}
+
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 ssd_status check(size_t bytes, int mode, int workgroups) {
@@ -128,6 +154,23 @@ ssd_status ssd_probe_copy(const void* src, void* dst, size_t bytes, int mode, in
     const unsigned g = grid_of(n, workgroups);
     if (mode) probe_copy_kernel<true><<<g, kThreads, 0, (hipStream_t)stream>>>((const V4*)src, (V4*)dst, n);
     else probe_copy_kernel<false><<<g, kThreads, 0, (hipStream_t)stream>>>((const V4*)src, (V4*)dst, n);
+    return done();
+}
+
+ssd_status ssd_probe_mix(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+                         int mode, int workgroups, void* stream) {
+    if ((read_bytes && !src) || (write_bytes && !dst)) return SSD_ERR_NULL;
+    if (!al16(src) || !al16(dst)) return SSD_ERR_ALIGN;
+    const size_t big = read_bytes > write_bytes ? read_bytes : write_bytes;
+    if (read_bytes % 16 != 0 || write_bytes % 16 != 0) return SSD_ERR_SHAPE;
+    const ssd_status s = check(big, mode, workgroups);
+    if (s != SSD_OK) return s;
+    const size_t nr = read_bytes / 16, nw = write_bytes / 16, n = big / 16;
+    const unsigned g = grid_of(n, workgroups);
+    if (mode)
+        probe_mix_kernel<true><<<g, kThreads, 0, (hipStream_t)stream>>>((const V4*)src, nr, (V4*)dst, nw, n);
+    else
+        probe_mix_kernel<false><<<g, kThreads, 0, (hipStream_t)stream>>>((const V4*)src, nr, (V4*)dst, nw, n);
     return done();
 }
 

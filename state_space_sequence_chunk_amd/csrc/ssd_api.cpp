@@ -260,6 +260,22 @@ ssd_status ssd_segment_plan(const ssd_shape* shape, int32_t* heads_per_workgroup
     return SSD_OK;
 }
 
+ssd_status ssd_chunk_out_plan(const ssd_shape* shape, int32_t* heads_per_workgroup,
+                             int32_t* shared_tiles, double* mfma_flops) {
+    ssd_status st = check_shape(shape);
+    if (st != SSD_OK) return st;
+    SSD_REQUIRE(shape->seqlen > 0, SSD_ERR_UNSUPPORTED);
+    ssd::SegPlan pl;
+    ssd::OutPlan op;
+    const bool segc = seg_plan_of(shape, &pl);  // the instance ssd_forward launches
+    SSD_REQUIRE(ssd::chunk_out_plan(shape->in_dtype, shape->states_dtype, segc, dims_of(shape), &op),
+                SSD_ERR_UNSUPPORTED);
+    if (heads_per_workgroup) *heads_per_workgroup = op.heads_per_wg;
+    if (shared_tiles) *shared_tiles = op.shared ? 1 : 0;
+    if (mfma_flops) *mfma_flops = op.mfma_flops;
+    return SSD_OK;
+}
+
 ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const void* dt, const float* A, float* G,
                             float* dt_t, void* stream) {
     ssd_status st = check_shape(shape);

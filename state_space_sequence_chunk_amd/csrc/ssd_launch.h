@@ -102,6 +102,15 @@ int bwd_mfma_chunk(int in_dtype, int P, int S);
 // it writes dB and dC directly); d.chunk is the backward's chunk length.
 int bwd_partials_per_group(int in_dtype, const Dims& d);
 
+// chunk_out's launch plan for a shape: heads per workgroup, shared interaction tiles, the
+// matrix-core flops the launch executes and its LDS bytes per workgroup (host-only; SEGC:
+// the instance over segment-relative states). False where no instance exists.
+struct OutPlan {
+    int heads_per_wg;
+    bool shared;
+    double mfma_flops, lds_bytes;
+};
+bool chunk_out_plan(int in_dtype, int states_dtype, bool segc, const Dims& d, OutPlan* plan);
 hipError_t launch_chunk_out(int in_dtype, int states_dtype, int out_dtype, const void* x,
                             const void* Bm, const void* Cm, const float* G, const float* dt_t,
                             const void* states, const float* D, void* y, const Dims& d,

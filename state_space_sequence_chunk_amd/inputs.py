@@ -51,7 +51,8 @@ class Workload:
         }
 
 
-# The five judged Mamba-2-shaped workloads (the second one in two input dtypes).
+# The five Mamba-2-shaped workloads (the second one in two input dtypes), and the
+# benchmark shape of the article's "Mamba-2 forward pass performance benchmarks" section.
 WORKLOADS = {
     "tiny-fp32": Workload("tiny-fp32", 1, 256, 2, 16, 16, 1, 64, "fp32", False, 1000),
     "small-fp32": Workload("small-fp32", 2, 2048, 24, 64, 64, 1, 64, "fp32", True, 1001),
@@ -59,6 +60,9 @@ WORKLOADS = {
     "780m-bf16": Workload("780m-bf16", 4, 4096, 48, 64, 128, 1, 256, "bf16", False, 1002),
     "2.7b-bf16": Workload("2.7b-bf16", 2, 16384, 80, 64, 128, 1, 256, "bf16", False, 1003),
     "long-bf16": Workload("long-bf16", 1, 65536, 80, 64, 256, 8, 256, "bf16", True, 1004),
+    # the one shape the article's benchmark section spells out (batch 4, 16K tokens, 8 heads
+    # of one group, dstate 128, headdim 64, chunk 128): only 32 (batch, head) pairs
+    "h8-t128-bf16": Workload("h8-t128-bf16", 4, 16384, 8, 64, 128, 1, 128, "bf16", False, 1005),
 }
 
 

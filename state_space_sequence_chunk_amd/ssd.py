@@ -27,9 +27,10 @@ EXPORTS = ("ssd_status_string", "ssd_validate_shape", "ssd_forward_workspace_byt
            "ssd_state_pass_workspace_bytes", "ssd_chunk_cumsum", "ssd_state_pass",
            "ssd_state_scan", "ssd_chunk_out", "ssd_forward", "ssd_decode_step", "ssd_backward_workspace_bytes",
            "ssd_backward", "ssd_state_pass_segmented_workspace_bytes", "ssd_state_pass_segmented",
-           "ssd_chunk_out_segmented", "ssd_segment_plan", "ssd_forward_noalloc")
+           "ssd_chunk_out_segmented", "ssd_segment_plan", "ssd_forward_noalloc",
+           "ssd_chunk_out_plan")
 # HBM stream probes declared in include/ssd_probe.h (measurement only).
-PROBE_EXPORTS = ("ssd_probe_read", "ssd_probe_write", "ssd_probe_copy")
+PROBE_EXPORTS = ("ssd_probe_read", "ssd_probe_write", "ssd_probe_copy", "ssd_probe_mix")
 
 
 class SSDError(RuntimeError):
@@ -82,9 +83,11 @@ def load_library():
     lib.ssd_chunk_out_segmented.argtypes = [sp] + [vp] * 9 + [sz, vp]
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.ssd_segment_plan.argtypes = [sp, i32p, i32p, i32p]
+    lib.ssd_chunk_out_plan.argtypes = [sp, i32p, i32p, ctypes.POINTER(ctypes.c_double)]
     lib.ssd_probe_read.argtypes = [vp, sz, vp, i32, i32, vp]
     lib.ssd_probe_write.argtypes = [vp, sz, i32, i32, vp]
     lib.ssd_probe_copy.argtypes = [vp, vp, sz, i32, i32, vp]
+    lib.ssd_probe_mix.argtypes = [vp, sz, vp, sz, i32, i32, vp]
     for name in EXPORTS[1:] + PROBE_EXPORTS:
         getattr(lib, name).restype = i32
     _lib = lib
@@ -201,6 +204,16 @@ def segment_plan(shape: ssd_shape):
     return int(h.value), int(k.value), int(n.value)
 
 
+def chunk_out_plan(shape: ssd_shape):
+    """(heads per workgroup, interaction tiles shared, executed matrix-core flops per launch)
+    of the output kernel ssd_forward launches for the shape."""
+    h, sh, fl = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_double(0.0)
+    _check(load_library().ssd_chunk_out_plan(ctypes.byref(shape), ctypes.byref(h),
+                                             ctypes.byref(sh), ctypes.byref(fl)),
+           "ssd_chunk_out_plan")
+    return int(h.value), bool(sh.value), float(fl.value)
+
+
 def ssd_state_pass_segmented(shape, x, A, B, G, dt_t, h0, seg_relative_states, final_state,
                              workspace, stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -256,6 +269,14 @@ def probe_copy(src, dst, *, mode=0, workgroups=0, stream=None):
         raise ValueError("probe_copy: src and dst sizes differ")
     _check(load_library().ssd_probe_copy(_p(src), _p(dst), src.numel() * src.element_size(),
                                          mode, workgroups, _stream(stream)), "ssd_probe_copy")
+
+
+def probe_mix(src, read_bytes, dst, write_bytes, *, mode=0, workgroups=0, stream=None):
+    """Read read_bytes of src and write write_bytes of dst in one pass (see ssd_probe.h)."""
+    if read_bytes > src.numel() * src.element_size() or write_bytes > dst.numel() * dst.element_size():
+        raise ValueError("probe_mix: sizes exceed the buffers")
+    _check(load_library().ssd_probe_mix(_p(src), read_bytes, _p(dst), write_bytes, mode,
+                                        workgroups, _stream(stream)), "ssd_probe_mix")
 
 
 def decode_step(x, dt, A, B, C, D, state, *, stream=None):

@@ -384,6 +384,12 @@ def test_backward_chunk_stays_within_size_limits():
     (lambda L: L.ssd_probe_write(4096, 1024, 0, -1, None), 2),
     (lambda L: L.ssd_probe_copy(4096, 8200, 1024, 0, 0, None), 6),
     (lambda L: L.ssd_probe_copy(4096, 8192, 1024, 5, 0, None), 4),
+    (lambda L: L.ssd_probe_mix(None, 1024, 8192, 1024, 0, 0, None), 1),
+    (lambda L: L.ssd_probe_mix(4096, 1024, None, 16, 0, 0, None), 1),
+    (lambda L: L.ssd_probe_mix(4096, 0, 8192, 0, 0, 0, None), 2),
+    (lambda L: L.ssd_probe_mix(4096, 1000, 8192, 1024, 0, 0, None), 2),
+    (lambda L: L.ssd_probe_mix(4104, 1024, 8192, 1024, 0, 0, None), 6),
+    (lambda L: L.ssd_probe_mix(4096, 1024, 8192, 2048, 3, 0, None), 4),
 ])
 def test_probe_argument_checks(call, code):
     assert call(ssd.load_library()) == code
@@ -407,3 +413,26 @@ def test_noalloc_rejects_too_large_on_host():
     # the bench shape fits
     bench = shape(batch=2, seqlen=16384, nheads=80, headdim=64, dstate=128, ngroups=1, chunk=256)
     assert ssd.forward_workspace_bytes(bench) <= ssd.NOALLOC_SCRATCH_BYTES
+
+
+def test_chunk_out_plan_counts_the_executed_products():
+    # the 2.7B layer: 40 heads per workgroup (256 workgroups of 8 waves fill the 256 CUs
+    # once), interaction tiles shared. Per workgroup: 136 lower-triangular 16x16 tiles of
+    # C B^T at K = 128 (4 products of K = 32); per head: C_i . S_c for 16 row tiles x 4
+    # p-tiles x 4 K-steps, and W x for the row tiles' column-tile pairs (72) x 4 p-tiles.
+    # Every product is 2 x 16 x 16 x 32 flops.
+    s = ssd.make_shape(2, 16384, 80, 64, 128, 1, 256, ssd.SSD_BF16)
+    nh, shared, flops = ssd.chunk_out_plan(s)
+    assert (nh, shared) == (40, True)
+    pairs = sum(it // 2 + 1 for it in range(16))
+    assert pairs == 72
+    per_wg = 136 * 4 + 40 * (16 * 4 * 4 + 72 * 4)
+    assert flops == per_wg * 256 * 2 * 16 * 16 * 32
+    # fp32 states with bf16 inputs: the carried-state product runs on a high/low split
+    s32 = ssd.make_shape(2, 16384, 80, 64, 128, 1, 256, ssd.SSD_BF16, states_dtype=ssd.SSD_F32)
+    nh32, sh32, f32 = ssd.chunk_out_plan(s32)
+    tiles = 136 * 4 * (1 if sh32 else nh32)
+    assert f32 == (tiles + nh32 * (16 * 4 * 4 * 2 + 72 * 4)) * (2 * 16384 * 80 // (256 * nh32)) * 16384
+    with pytest.raises(ssd.SSDError) as e:
+        ssd.chunk_out_plan(shape(seqlen=0))
+    assert e.value.code == 4
