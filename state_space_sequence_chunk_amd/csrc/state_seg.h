@@ -265,12 +265,14 @@ __global__ __launch_bounds__(64 * NW) void state_seg_kernel(
         const float gl = gls[q];  // this step's chunk decay, before set q is reloaded
         // Every step issues its loads unconditionally (past the segment's end they repeat its
         // last chunk and are never used), so no wait before a use depends on a runtime branch
-        // and the loads two steps ahead stay in flight.
-        load_head(q_c, min(c + dc2, c_first + nck - 1), u2 / NH, h_first + u2 % NH);
+        // and the loads two steps ahead stay in flight. The next sub-block's B rows go first:
+        // vector-memory waits are in issue order, so the wait for them at this step's end
+        // then leaves the loads two steps ahead in flight.
         if constexpr (hh == NH - 1) {  // the next sub-block's B rows
             if constexpr (sub + 1 < NSUB) load_b(c, sub + 1);
             else load_b(next ? c + 1 : c, 0);
         }
+        load_head(q_c, min(c + dc2, c_first + nck - 1), u2 / NH, h_first + u2 % NH);
         // stage the next step now (its loads were issued a step ago): LDS buffer q^1 was
         // last read by the previous step, which ended at a barrier; the next step reads
         // it after this step's barrier. Past the segment's end the copy is never read.
