@@ -534,6 +534,25 @@ def main():
                               "ms_per_step": ms16}
         del f16
 
+    # the same forward pass recorded once in a HIP graph and replayed (one graph launch per
+    # step instead of one launch per kernel: it matters for the small problems)
+    try:
+        fg = ssd.ForwardGraph(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=T)
+        for _ in range(args.warmup):
+            fg.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            fg.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        msg = e0.elapsed_time(e1) / K
+        variants["graph_replay"] = {"value": w.tokens / (msg * 1e-3), "unit": "tokens/s",
+                                    "ms_per_step": msg}
+        del fg
+    except Exception as exc:  # reported, never silently replaced
+        variants["graph_replay"] = {"error": f"{type(exc).__name__}: {exc}"}
+
     # the backward pass (gradients of every input), a separate figure from the forward
     try:
         variants["backward"] = time_backward(torch, ssd, gen, w, d, stream,

@@ -346,6 +346,38 @@ class Forward:
         return self.y, self.final
 
 
+class ForwardGraph:
+    """ssd_forward on fixed input buffers, recorded once in a HIP graph (through
+    torch.cuda.CUDAGraph) and replayed: a replay is one graph launch instead of one launch
+    per kernel, which is most of the time of a small problem. Every replay reads the input
+    tensors given here (update them in place between replays) and writes the same y and
+    final tensors. The forward pass records no memset and allocates nothing, so the graph
+    holds only its kernels."""
+
+    def __init__(self, x, dt, A, B, C, D=None, h0=None, *, chunk, states_dtype=None,
+                 out_dtype=None):
+        self.fwd = Forward(x, B, chunk, states_dtype, out_dtype=out_dtype)
+        self.args = (x, dt, A, B, C, D, h0)
+        # one call outside the capture (kernel attributes are set on first use)
+        self.fwd(*self.args)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.fwd(*self.args, stream=torch.cuda.current_stream())
+
+    @property
+    def y(self):
+        return self.fwd.y
+
+    @property
+    def final(self):
+        return self.fwd.final
+
+    def replay(self):
+        self.graph.replay()
+        return self.fwd.y, self.fwd.final
+
+
 def forward(x, dt, A, B, C, D=None, h0=None, *, chunk, states_dtype=None, out_dtype=None,
             stream=None):
     """One-shot forward pass; returns (y [b, L, h, P] in out_dtype (fp32 by default),
