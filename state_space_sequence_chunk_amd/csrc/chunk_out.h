@@ -123,7 +123,26 @@ struct OutCfg {
     static constexpr int NBVP = B_PASS * 16 * S / VE / NTHR;  // B vectors / thread and pass
     static constexpr size_t BASE_BYTES =
         SHARED ? REGION0 + TILE_BYTES : HEAD_BYTES + (B_IN_LDS ? B_BYTES : 0);
-    static constexpr size_t LDS_BYTES = BASE_BYTES + DEC_BYTES;
+    // fp32 y leaves through a per-wave LDS scratch of 16 rows x 32 columns (two p-tiles), so
+    // that each store instruction writes whole 128-byte row pieces; only where the scratch
+    // fits without lowering the workgroups resident per CU (the bf16-y instances of the
+    // same shape carry it unused, so that every instance of a shape has one launch plan)
+    static constexpr size_t Y_OFF = (BASE_BYTES + DEC_BYTES + 15) / 16 * 16;
+    static constexpr int YST = 36;  // scratch row stride in floats (rows 16 banks apart)
+    static constexpr size_t Y_SCR_BYTES = (size_t)NW * 16 * YST * 4;
+    // (measured: at 128-token chunks the article's shape went from 90 to 68 us; at 256 the
+    // 2.7B layer ran 1% slower, so the 8-wave form keeps the direct stores)
+    static constexpr bool Y_STAGE = NPT % 2 == 0 && T <= 128 && Y_OFF + Y_SCR_BYTES <= 163840 &&
+                                    163840 / (Y_OFF + Y_SCR_BYTES) ==
+                                        163840 / (BASE_BYTES + DEC_BYTES);
+    static constexpr size_t LDS_BYTES = Y_STAGE ? Y_OFF + Y_SCR_BYTES : BASE_BYTES + DEC_BYTES;
+    // minimum waves per SIMD asked of the register allocator: two for the shapes that fit
+    // them without spilling (bf16 inputs and states up to P 64, S 128; fp32 up to P 64,
+    // S 64, 128-token chunks), so that two workgroups share a compute unit where LDS allows
+    static constexpr int WPE = ((sizeof(TIn) == 2 && sizeof(TS) == 2 && P <= 64 && S <= 128) ||
+                                (sizeof(TIn) == 4 && P <= 64 && S <= 64 && T <= 128))
+                                   ? 2
+                                   : 1;
 };
 
 // y element store through a buffer descriptor: fp32, or bf16 rounded to nearest even.
@@ -139,7 +158,7 @@ __device__ __forceinline__ void store_y(float v, bf16*, BufRsrc r, uint32_t voff
 // (see state_seg.h); the state of chunk c in segment k >= 1 is states[c] +
 // 2^{dec_in[c]} seg_in[k], formed in fp32 while the state is staged and rounded once.
 template <typename TIn, typename TS, typename TY, int P, int S, int T, bool SEGC = false>
-__global__ __launch_bounds__(2 * T) void chunk_out_kernel(
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(OutCfg<TIn, TS, P, S, T, SEGC>::WPE))) void chunk_out_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ Bm, const TIn* __restrict__ Cm,
     const float* __restrict__ G, const float* __restrict__ dt_t, const TS* __restrict__ states,
     const float* __restrict__ Dv, TY* __restrict__ y, int L, int H, int ngroups, int NH,
@@ -549,10 +568,30 @@ __global__ __launch_bounds__(2 * T) void chunk_out_kernel(
                     for (int r = 0; r < 4; ++r)
                         xi[r] = s_x[(its[q] * 16 + 4 * g4 + r) * XS + pt * 16 + l16];
                 }
+                if constexpr (Cfg::Y_STAGE && sizeof(TY) == 4) {
+                    // into this wave's scratch (rows of the row tile, two p-tiles wide);
+                    // after each pair, 16-byte reads give each lane four consecutive
+                    // columns and 8 lanes cover a 128-byte row piece
+                    float* scr = (float*)(smem + Cfg::Y_OFF) + wave * 16 * Cfg::YST;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    store_y(yacc[q][pt][r] + dh * xi[r], y, ry,
-                            yoff[q][r] + pt * 16 * (uint32_t)sizeof(TY), yh);
+                    for (int r = 0; r < 4; ++r)
+                        scr[(4 * g4 + r) * Cfg::YST + (pt & 1) * 16 + l16] = yacc[q][pt][r] + dh * xi[r];
+                    if (pt & 1) {
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const int v = i * 64 + lane, rr = v >> 3, c4 = (v & 7) * 4;
+                            const f32x4 o = *(const f32x4*)(scr + rr * Cfg::YST + c4);
+                            buf_store16(__builtin_bit_cast(Vec16, o), ry,
+                                        (uint32_t)((((its[q] * 16 + rr) * HP) + h * P +
+                                                    (pt - 1) * 16 + c4) * sizeof(float)));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        store_y(yacc[q][pt][r] + dh * xi[r], y, ry,
+                                yoff[q][r] + pt * 16 * (uint32_t)sizeof(TY), yh);
+                }
             }
 
         lds_barrier();  // every wave is done with this head's LDS copies
