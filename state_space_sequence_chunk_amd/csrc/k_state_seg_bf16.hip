@@ -33,10 +33,10 @@ struct SegPick {
 template <int P, int S, int T> using SegCfgFor = typename SegPick<P, S, T>::Cfg;
 
 // Whether the shape has a kernel form; its workgroup slots per round, state-register and
-// head limits.
+// head limits, threads and sub-blocks per chunk.
 struct SegForm {
     bool fits;
-    int slots, max_state_regs, max_heads, nthr;
+    int slots, max_state_regs, max_heads, nthr, nsub;
 };
 SegForm seg_form(int P, int S, int T) {
     switch (P * 1000000 + S * 1000 + T) {
@@ -44,13 +44,13 @@ SegForm seg_form(int P, int S, int T) {
     case p * 1000000 + s * 1000 + t:                                                       \
         return SegForm{SegCfgFor<p, s, t>::FITS, SegPick<p, s, t>::SLOTS,                  \
                        SegPick<p, s, t>::MAX_STATE_REGS, SegPick<p, s, t>::MAX_HEADS,      \
-                       SegCfgFor<p, s, t>::NTHR};
+                       SegCfgFor<p, s, t>::NTHR, SegCfgFor<p, s, t>::NSUB};
         SSD_SEG_FITS(64, 64, 64) SSD_SEG_FITS(64, 64, 128) SSD_SEG_FITS(64, 64, 256)
         SSD_SEG_FITS(64, 128, 64) SSD_SEG_FITS(64, 128, 128) SSD_SEG_FITS(64, 128, 256)
         SSD_SEG_FITS(64, 256, 64) SSD_SEG_FITS(64, 256, 128) SSD_SEG_FITS(64, 256, 256)
 #undef SSD_SEG_FITS
     }
-    return SegForm{false, 0, 0, 0, 0};
+    return SegForm{false, 0, 0, 0, 0, 0};
 }
 
 template <int P, int S, int T, int NH>
@@ -116,10 +116,13 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // Plan: heads per workgroup (a divisor of the heads per group whose running states fit
 // in registers) and chunks per segment (at least 2 unless the sequence has one
 // chunk). Workgroups are resident one or two per CU (the form's LDS plan), so the grid
-// runs in rounds of 256 or 512; the cost of a plan is its rounds times one workgroup's
-// work, counted in (chunk, head) steps plus a fixed share per workgroup, per chunk (B rows,
-// one more barrier) and per head (its end state). Ties go to longer segments (fewer
-// corrections downstream).
+// runs in rounds of 256 or 512 workgroups; with two per CU, a last round that leaves
+// every CU at most one workgroup takes 0.9 of a full one. A workgroup's work is counted
+// in (sub-block, head) steps, plus 0.2 of a step per sub-block for the B rows its heads
+// share, 2 per head (entering and end states) and 2 per workgroup; each segment adds 0.3
+// for its carry and correction. These weights were fitted to measured forward times over
+// plans for five layer shapes (dstate 64 to 256, 8 to 80 heads, chunks of 64 to 256
+// tokens). Ties go to longer segments (fewer corrections downstream).
 bool state_seg_plan(int in_dtype, int states_dtype, const Dims& d, SegPlan* out) {
     if (in_dtype != kBF16 || states_dtype != kBF16) return false;
     const SegForm f = seg_form(d.headdim, d.dstate, d.chunk);
@@ -140,8 +143,10 @@ bool state_seg_plan(int in_dtype, int states_dtype, const Dims& d, SegPlan* out)
         for (int k = (nC == 1 ? 1 : 2); k <= nC; ++k) {
             const int nseg = (nC + k - 1) / k;
             const long wgs = (long)d.batch * nseg * (d.nheads / nh);
-            const long rounds = (wgs + f.slots - 1) / f.slots;
-            const double cost = (double)rounds * (nh * k + 1.0 + 0.5 * k + 0.7 * nh);
+            double rounds = (double)((wgs + f.slots - 1) / f.slots);
+            if (f.slots == 512 && wgs % 512 != 0 && wgs % 512 <= 256) rounds -= 0.1;
+            const double steps = (double)k * f.nsub;
+            const double cost = rounds * (nh * steps + 0.2 * steps + 2.0 * nh + 2.0) + 0.3 * nseg;
             if (cost < best - 1e-9 || (cost < best + 1e-9 && k > bp.chunks)) {
                 best = cost;
                 bp = SegPlan{nh, k, nseg};
