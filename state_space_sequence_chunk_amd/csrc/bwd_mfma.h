@@ -82,12 +82,14 @@ struct BmCfg {
     static constexpr size_t K_BYTES = (size_t)T * KS * 2;  // each part
     static constexpr size_t V_BYTES = (size_t)T * VS * 2;  // each part
     static constexpr size_t Z_BYTES = (size_t)N * KS * 2;  // each part
-    // dxh: dy's rows also kept in fp32 for the epilogue's D dy and dy . x
-    static constexpr int DS = P + 4;
-    static constexpr size_t DY_BYTES = OP == kOpX ? (size_t)T * DS * 4 : 0;
+    // dxh: x's rows of the head for the epilogue's x . dxh and dy . x (its D dy and dy . x
+    // take dy as the sum of its bf16 high and low parts in V, within 2^-17 of dy); the row
+    // stride puts the four rows a read touches in different banks
+    static constexpr int XR = P + 16;
+    static constexpr size_t X_BYTES = OP == kOpX ? (size_t)T * XR * 2 : 0;
     static constexpr size_t LDS_BYTES = K_BYTES * (KSPLIT ? 2 : 1) + V_BYTES * (VSPLIT ? 2 : 1) +
                                         2 * Z_BYTES + 3 * (size_t)T * 4 +
-                                        2 * NSPLIT * (size_t)T * 4 + DY_BYTES;
+                                        2 * NSPLIT * (size_t)T * 4 + X_BYTES;
     static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && NNT % NSPLIT == 0;
 };
 
@@ -110,18 +112,23 @@ struct Stager {
     static constexpr int NV = (NVEC + NTHR - 1) / NTHR;
     static constexpr bool F32 = sizeof(TSrc) == 4;
     f32x4 raw[F32 ? 2 * NV : NV];
+    // Every thread issues the same number of loads, with no branch around them, so that
+    // the compiler's waits for later loads count exactly; rows at or past `rows` lie
+    // outside the descriptor and read as zeros, as do the slots past the tile (offset
+    // 2^31).
     __device__ __forceinline__ void load(const TSrc* src, size_t sstride, int rows, int tid) {
+        const BufRsrc rs = make_rsrc(src, (uint32_t)((size_t)rows * sstride * sizeof(TSrc)));
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int v = tid + i * NTHR;
             const int r = v / PER, col = (v % PER) * 8;
-            const bool ok = v < NVEC && r < rows;
+            const uint32_t off =
+                v < NVEC ? (uint32_t)(((size_t)r * sstride + col) * sizeof(TSrc)) : 0x80000000u;
             if constexpr (F32) {
-                raw[2 * i] = ok ? *(const f32x4*)(src + r * sstride + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-                raw[2 * i + 1] =
-                    ok ? *(const f32x4*)(src + r * sstride + col + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+                raw[2 * i] = __builtin_bit_cast(f32x4, buf_load16(rs, off, 0u));
+                raw[2 * i + 1] = __builtin_bit_cast(f32x4, buf_load16(rs, off + 16u, 0u));
             } else {
-                raw[i] = ok ? *(const f32x4*)(src + r * sstride + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+                raw[i] = __builtin_bit_cast(f32x4, buf_load16(rs, off, 0u));
             }
         }
     }
@@ -163,14 +170,15 @@ struct StateTStager {
     static constexpr int NVEC = (P / 2) * (S / 4), NV = (NVEC + NTHR - 1) / NTHR;
     f32x4 raw[2 * NV];
     __device__ __forceinline__ void load(const float* src, int tid) {
+        const BufRsrc rs = make_rsrc(src, (uint32_t)(P * S * sizeof(float)));
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int v = tid + i * NTHR;
             const int p = 2 * (v % (P / 2)), s0 = 4 * (v / (P / 2));
-            const bool ok = v < NVEC;
-            raw[2 * i] = ok ? *(const f32x4*)(src + (size_t)p * S + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
-            raw[2 * i + 1] =
-                ok ? *(const f32x4*)(src + (size_t)(p + 1) * S + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+            // unconditional loads (see Stager::load); slots past the state read zeros
+            const uint32_t off = v < NVEC ? (uint32_t)((p * S + s0) * sizeof(float)) : 0x80000000u;
+            raw[2 * i] = __builtin_bit_cast(f32x4, buf_load16(rs, off, 0u));
+            raw[2 * i + 1] = __builtin_bit_cast(f32x4, buf_load16(rs, off + (uint32_t)(S * sizeof(float)), 0u));
         }
     }
     __device__ __forceinline__ void store(bf16* zh, bf16* zl, int ks, int tid) const {
@@ -217,7 +225,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
     float* s_dt = s_g + T;                               // [T]
     float* s_u = s_dt + T;                               // [T] per-token decay factors
     float* s_red = s_u + T;                              // [NSPLIT][2][T] row-sum partials
-    float* s_dy32 = s_red + 2 * Cfg::NSPLIT * T;         // dxh: [T][DS] dy (fp32)
+    bf16* s_xr = (bf16*)(s_red + 2 * Cfg::NSPLIT * T);   // dxh: [T][XR] x rows
 
     // workgroup: (batch, chunk, block of NH heads of one group)
     const int L = a.L, H = a.H, NG = a.G, NH = a.NH;
@@ -253,6 +261,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
                                       StateTStager<NTHR, P, S>>;
     Stager<KSrc, NTHR, T, KD, KSPLIT> stk;
     Stager<VSrc, NTHR, T, N, VSPLIT> stv;
+    Stager<bf16, NTHR, T, P, false> stx;  // dxh: x rows
     ZStage stz;
     // G at this token and at the start (backward in time) or end (forward) of its 16-token
     // tile; u = 2^{G - G_start}, or dt 2^{G_end - G}: the decay from the tile's edge (<= 1)
@@ -261,18 +270,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
         if constexpr (OP == kOpC) stk.load(xr_of(h), HP, rows, tid);
         else if constexpr (OP == kOpB) stk.load(dyr_of(h), HP, rows, tid);
         else stv.load(dyr_of(h), HP, rows, tid);
+        if constexpr (OP == kOpX) stx.load(xr_of(h), HP, rows, tid);
         if constexpr (OP == kOpX) stz.load(zsrc_of(h), S, P, tid);
         else stz.load(zsrc_of(h), tid);
-        if (tid < T) {
-            pg = a.Gc[bhl_of(h) + min(tid, rows - 1)];
-            pdt = tid < rows ? a.dtt[bhl_of(h) + tid] : 0.f;
-            pge = a.Gc[bhl_of(h) + min(REV ? (tid & ~15) : (tid | 15), rows - 1)];
-        }
+        // (every thread loads, those past T harmlessly: no branch around the loads)
+        const BufRsrc rg = make_rsrc(a.Gc + bhl_of(h), (uint32_t)(rows * sizeof(float)));
+        const BufRsrc rd = make_rsrc(a.dtt + bhl_of(h), (uint32_t)(rows * sizeof(float)));
+        const int tt = tid & (T - 1);
+        pg = buf_load_f32(rg, (uint32_t)(min(tt, rows - 1) * 4), 0u);
+        pdt = buf_load_f32(rd, (uint32_t)(tt * 4), 0u);  // zero past the real tokens
+        pge = buf_load_f32(rg, (uint32_t)(min(REV ? (tt & ~15) : (tt | 15), rows - 1) * 4), 0u);
     };
     auto store_head = [&]() {
         if constexpr (OP == kOpX) {
             stv.store(s_v, s_vl, VS, tid);
-            stv.store_f32(s_dy32, Cfg::DS, tid);
+            stx.store(s_xr, nullptr, Cfg::XR, tid);
         } else {
             stk.store(s_k, s_kl, KS, tid);
         }
@@ -320,21 +332,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
     // rows of the next (head, row tile) step are in flight during the current one
     constexpr bool QF32 = OP == kOpC;
     f32x4 qraw[NKS * (QF32 ? 2 : 1)];
+    // (unconditional loads; rows past the chunk's real tokens lie outside the descriptor)
     auto load_q = [&](int h, int it) {
         const int qrow = it * 16 + l16;
+        BufRsrc rq;
+        uint32_t rs;  // bytes per row
+        if constexpr (OP == kOpC) {
+            rs = (uint32_t)(HP * 4);
+            rq = make_rsrc(dyr_of(h), rows * rs);
+        } else if constexpr (OP == kOpB) {
+            rs = (uint32_t)(HP * 2);
+            rq = make_rsrc(xr_of(h), rows * rs);
+        } else {
+            rs = (uint32_t)(GS * 2);
+            rq = make_rsrc(br, rows * rs);
+        }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int k0 = ks * 32 + g4 * 8;
-            const bool ok = qrow < rows;
-            const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (OP == kOpC) {
-                const float* p = dyr_of(h) + qrow * HP + k0;
-                qraw[2 * ks] = ok ? *(const f32x4*)p : z4;
-                qraw[2 * ks + 1] = ok ? *(const f32x4*)(p + 4) : z4;
-            } else if constexpr (OP == kOpB) {
-                qraw[ks] = ok ? *(const f32x4*)(xr_of(h) + qrow * HP + k0) : z4;
+                const uint32_t o = qrow * rs + k0 * 4;
+                qraw[2 * ks] = __builtin_bit_cast(f32x4, buf_load16(rq, o, 0u));
+                qraw[2 * ks + 1] = __builtin_bit_cast(f32x4, buf_load16(rq, o + 16u, 0u));
             } else {
-                qraw[ks] = ok ? *(const f32x4*)(br + qrow * GS + k0) : z4;
+                qraw[ks] = __builtin_bit_cast(f32x4, buf_load16(rq, qrow * rs + k0 * 2, 0u));
             }
         }
     };
@@ -343,7 +364,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
 #pragma unroll 1
     for (int hh = 0; hh < NH; ++hh) {
         const int h = h_first + hh;
-        if (hh + 1 < NH) load_head(h + 1);  // lands in registers while this head computes
         const float g_end = s_g[T - 1];     // = G at the last real token
         const float dval = a.D ? a.D[h] : 0.f;
 #pragma unroll
@@ -362,23 +382,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
             }
             // the next step's rows
             if (qi == 0) load_q(h, NIT - 1 - wave);
-            else if (hh + 1 < NH) load_q(h + 1, wave);
-            // dxh epilogue: x at this lane's output elements, loaded ahead of use
+            else load_q(hh + 1 < NH ? h + 1 : h, wave);
             const uint32_t row0 = row0s[qi];
-            float xv[OP == kOpX ? 4 : 1][NNH];
-            if constexpr (OP == kOpX) {
-                const BufRsrc rxx = make_rsrc((const bf16*)a.x + tok0 * HP, (uint32_t)(rows * HP * 2));
-                const uint32_t soff2 = (uint32_t)(h * P * 2);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int j = 0; j < NNH; ++j) {
-                        const uint32_t vx = (row0 + r) * (uint32_t)(HP * 2) + l16 * 2;
-                        const uint16_t xb = __builtin_amdgcn_raw_buffer_load_b16(
-                            rxx, vx + (nt0 + j) * 32, soff2, 0);
-                        xv[r][j] = to_f32(__builtin_bit_cast(bf16, xb));
-                    }
-            }
+            // the next head's rows, issued after every load this head still waits for (Q's
+            // rows of the second row tile): vector-memory operations complete
+            // in issue order, so issued earlier they would be waited for within this head.
+            // Every memory operation of the loop is issued on every path (at the last head
+            // the loads repeat the current head and go unused; the per-row sums are stored
+            // through descriptors that drop the rows past the chunk), so the compiler's
+            // counted waits never fall back to waiting for everything.
+            if (qi == 0) load_head(hh + 1 < NH ? h + 1 : h);
             f32x4 acc[NNH];  // output columns 16 (nt0 + j) + l16
 #pragma unroll
             for (int j = 0; j < NNH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -508,10 +521,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
                     for (int j = 0; j < NNH; ++j) {
                         const int nt = nt0 + j;
                         const float o = acc[j][r];
-                        const float dyv = s_dy32[(row0 + r) * Cfg::DS + nt * 16 + l16];
+                        const int e = (row0 + r) * VS + nt * 16 + l16;
+                        const float dyv = to_f32(s_v[e]) + to_f32(s_vl[e]);
+                        const float xv = to_f32(s_xr[(row0 + r) * Cfg::XR + nt * 16 + l16]);
                         buf_store_f32(dval * dyv + dtr * o, rdx, vo + nt * 64, soff4);
-                        red[r] += xv[r][j] * o;
-                        red2[r] += xv[r][j] * dyv;
+                        red[r] += xv * o;
+                        red2[r] += xv * dyv;
                     }
                 }
             }
@@ -534,19 +549,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
         lds_barrier();  // every wave is done with this head's LDS and partials
         if constexpr (OP != kOpB) {
             const size_t bhl = bhl_of(h);
-            if (tid < rows) {
-                float s0 = 0.f, s1 = 0.f;
+            const int tt = tid & (T - 1);
+            float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-                for (int q = 0; q < Cfg::NSPLIT; ++q) {
-                    s0 += s_red[(2 * q) * T + tid];
-                    s1 += s_red[(2 * q + 1) * T + tid];
-                }
-                if constexpr (OP == kOpC) {
-                    a.q[bhl + tid] = s0;
-                } else {
-                    a.v[bhl + tid] = s0;
-                    a.dyx[bhl + tid] = s1;
-                }
+            for (int q = 0; q < Cfg::NSPLIT; ++q) {
+                s0 += s_red[(2 * q) * T + tt];
+                s1 += s_red[(2 * q + 1) * T + tt];
+            }
+            const uint32_t off = tid < rows ? (uint32_t)(tid * 4) : 0x80000000u;
+            const uint32_t nb = (uint32_t)(rows * 4);
+            if constexpr (OP == kOpC) {
+                buf_store_f32(s0, make_rsrc(a.q + bhl, nb), off, 0u);
+            } else {
+                buf_store_f32(s0, make_rsrc(a.v + bhl, nb), off, 0u);
+                buf_store_f32(s1, make_rsrc(a.dyx + bhl, nb), off, 0u);
             }
         }
         if (hh + 1 < NH) store_head();
