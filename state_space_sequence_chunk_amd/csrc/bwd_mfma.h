@@ -266,7 +266,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
     // G at this token and at the start (backward in time) or end (forward) of its 16-token
     // tile; u = 2^{G - G_start}, or dt 2^{G_end - G}: the decay from the tile's edge (<= 1)
     float pg = 0.f, pdt = 0.f, pge = 0.f;
+    // dxh: D of the head, loaded with its rows (zero when D is absent: a descriptor of no
+    // bytes), so that no load outside the prefetch is issued, and waited for, per head
+    float pdv = 0.f, dval = 0.f;
+    const BufRsrc rD = make_rsrc(a.D, a.D ? (uint32_t)(H * sizeof(float)) : 0u);
     auto load_head = [&](int h) {
+        if constexpr (OP == kOpX) pdv = buf_load_f32(rD, (uint32_t)(h * 4), 0u);
         if constexpr (OP == kOpC) stk.load(xr_of(h), HP, rows, tid);
         else if constexpr (OP == kOpB) stk.load(dyr_of(h), HP, rows, tid);
         else stv.load(dyr_of(h), HP, rows, tid);
@@ -282,6 +287,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
         pge = buf_load_f32(rg, (uint32_t)(min(REV ? (tt & ~15) : (tt | 15), rows - 1) * 4), 0u);
     };
     auto store_head = [&]() {
+        dval = pdv;
         if constexpr (OP == kOpX) {
             stv.store(s_v, s_vl, VS, tid);
             stx.store(s_xr, nullptr, Cfg::XR, tid);
@@ -359,13 +365,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
             }
         }
     };
+    // dxh: Q = B's rows, the same for every head: both row tiles loaded once, so the head
+    // loop issues no loads but the next head's, at its top
+    f32x4 qkeep[OP == kOpX ? 2 : 1][OP == kOpX ? NKS : 1];
+    if constexpr (OP == kOpX) {
+        load_q(h_first, NIT - 1 - wave);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qkeep[1][ks] = qraw[ks];
+    }
     load_q(h_first, wave);
+    if constexpr (OP == kOpX) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qkeep[0][ks] = qraw[ks];
+    }
 
 #pragma unroll 1
     for (int hh = 0; hh < NH; ++hh) {
         const int h = h_first + hh;
+        if constexpr (OP == kOpX) load_head(hh + 1 < NH ? h + 1 : h);
         const float g_end = s_g[T - 1];     // = G at the last real token
-        const float dval = a.D ? a.D[h] : 0.f;
 #pragma unroll
         for (int qi = 0; qi < 2; ++qi) {
             const int it = qi == 0 ? wave : NIT - 1 - wave;  // this wave's row tiles
@@ -376,22 +394,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
             for (int ks = 0; ks < NKS; ++ks) {
                 if constexpr (QF32) {
                     split8(qraw[2 * ks], qraw[2 * ks + 1], qf[ks].v, ql[ks].v);
+                } else if constexpr (OP == kOpX) {
+                    qf[ks].v = __builtin_bit_cast(bf16x8, qkeep[qi][ks]);
                 } else {
                     qf[ks].v = __builtin_bit_cast(bf16x8, qraw[ks]);
                 }
             }
             // the next step's rows
-            if (qi == 0) load_q(h, NIT - 1 - wave);
-            else load_q(hh + 1 < NH ? h + 1 : h, wave);
+            if constexpr (OP != kOpX) {
+                if (qi == 0) load_q(h, NIT - 1 - wave);
+                else load_q(hh + 1 < NH ? h + 1 : h, wave);
+            }
             const uint32_t row0 = row0s[qi];
-            // the next head's rows, issued after every load this head still waits for (Q's
-            // rows of the second row tile): vector-memory operations complete
-            // in issue order, so issued earlier they would be waited for within this head.
+            // dC, dB: the next head's rows, issued after every load this head still waits
+            // for (Q's rows of the second row tile): vector-memory operations complete in
+            // issue order, so issued earlier they would be waited for within this head.
             // Every memory operation of the loop is issued on every path (at the last head
             // the loads repeat the current head and go unused; the per-row sums are stored
             // through descriptors that drop the rows past the chunk), so the compiler's
             // counted waits never fall back to waiting for everything.
-            if (qi == 0) load_head(hh + 1 < NH ? h + 1 : h);
+            if (OP != kOpX && qi == 0) load_head(hh + 1 < NH ? h + 1 : h);
             f32x4 acc[NNH];  // output columns 16 (nt0 + j) + l16
 #pragma unroll
             for (int j = 0; j < NNH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
