@@ -87,9 +87,11 @@ struct BmCfg {
     // stride puts the four rows a read touches in different banks
     static constexpr int XR = P + 16;
     static constexpr size_t X_BYTES = OP == kOpX ? (size_t)T * XR * 2 : 0;
+    // dC, dB: Q's rows of the head (read by rows, like K; dy split into two parts)
+    static constexpr size_t Q_BYTES = OP == kOpX ? 0 : (size_t)T * KS * 2 * (QSPLIT ? 2 : 1);
     static constexpr size_t LDS_BYTES = K_BYTES * (KSPLIT ? 2 : 1) + V_BYTES * (VSPLIT ? 2 : 1) +
                                         2 * Z_BYTES + 3 * (size_t)T * 4 +
-                                        2 * NSPLIT * (size_t)T * 4 + X_BYTES;
+                                        2 * NSPLIT * (size_t)T * 4 + X_BYTES + Q_BYTES;
     static constexpr bool FITS = LDS_BYTES <= 163840 && KD % 32 == 0 && NNT % NSPLIT == 0;
 };
 
@@ -226,6 +228,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
     float* s_u = s_dt + T;                               // [T] per-token decay factors
     float* s_red = s_u + T;                              // [NSPLIT][2][T] row-sum partials
     bf16* s_xr = (bf16*)(s_red + 2 * Cfg::NSPLIT * T);   // dxh: [T][XR] x rows
+    bf16* s_q = (bf16*)((unsigned char*)s_xr + Cfg::X_BYTES);  // dC, dB: [T][KS] Q rows
+    bf16* s_ql = QSPLIT ? s_q + T * KS : nullptr;        // dC: [T][KS] low parts of Q
 
     // workgroup: (batch, chunk, block of NH heads of one group)
     const int L = a.L, H = a.H, NG = a.G, NH = a.NH;
@@ -262,6 +266,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
     Stager<KSrc, NTHR, T, KD, KSPLIT> stk;
     Stager<VSrc, NTHR, T, N, VSPLIT> stv;
     Stager<bf16, NTHR, T, P, false> stx;  // dxh: x rows
+    using QSrc = std::conditional_t<OP == kOpC, float, bf16>;
+    Stager<QSrc, NTHR, T, KD, QSPLIT> stq;  // dC, dB: Q rows (dy, x)
     ZStage stz;
     // G at this token and at the start (backward in time) or end (forward) of its 16-token
     // tile; u = 2^{G - G_start}, or dt 2^{G_end - G}: the decay from the tile's edge (<= 1)
@@ -276,6 +282,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
         else if constexpr (OP == kOpB) stk.load(dyr_of(h), HP, rows, tid);
         else stv.load(dyr_of(h), HP, rows, tid);
         if constexpr (OP == kOpX) stx.load(xr_of(h), HP, rows, tid);
+        if constexpr (OP == kOpC) stq.load(dyr_of(h), HP, rows, tid);
+        if constexpr (OP == kOpB) stq.load(xr_of(h), HP, rows, tid);
         if constexpr (OP == kOpX) stz.load(zsrc_of(h), S, P, tid);
         else stz.load(zsrc_of(h), tid);
         // (every thread loads, those past T harmlessly: no branch around the loads)
@@ -293,6 +301,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
             stx.store(s_xr, nullptr, Cfg::XR, tid);
         } else {
             stk.store(s_k, s_kl, KS, tid);
+            stq.store(s_q, s_ql, KS, tid);
         }
         stz.store(s_zh, s_zl, KS, tid);
         if (tid < T) {
@@ -334,55 +343,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
 #pragma unroll
         for (int j = 0; j < NNH; ++j) tot[qi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Q's rows (lane: row I0 + l16, k = 32 ks + 8 g4 + v) are loaded one step ahead: the
-    // rows of the next (head, row tile) step are in flight during the current one
-    constexpr bool QF32 = OP == kOpC;
-    f32x4 qraw[NKS * (QF32 ? 2 : 1)];
-    // (unconditional loads; rows past the chunk's real tokens lie outside the descriptor)
-    auto load_q = [&](int h, int it) {
-        const int qrow = it * 16 + l16;
-        BufRsrc rq;
-        uint32_t rs;  // bytes per row
-        if constexpr (OP == kOpC) {
-            rs = (uint32_t)(HP * 4);
-            rq = make_rsrc(dyr_of(h), rows * rs);
-        } else if constexpr (OP == kOpB) {
-            rs = (uint32_t)(HP * 2);
-            rq = make_rsrc(xr_of(h), rows * rs);
-        } else {
-            rs = (uint32_t)(GS * 2);
-            rq = make_rsrc(br, rows * rs);
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int k0 = ks * 32 + g4 * 8;
-            if constexpr (OP == kOpC) {
-                const uint32_t o = qrow * rs + k0 * 4;
-                qraw[2 * ks] = __builtin_bit_cast(f32x4, buf_load16(rq, o, 0u));
-                qraw[2 * ks + 1] = __builtin_bit_cast(f32x4, buf_load16(rq, o + 16u, 0u));
-            } else {
-                qraw[ks] = __builtin_bit_cast(f32x4, buf_load16(rq, qrow * rs + k0 * 2, 0u));
-            }
-        }
-    };
-    // dxh: Q = B's rows, the same for every head: both row tiles loaded once, so the head
-    // loop issues no loads but the next head's, at its top
+    // Q's rows (lane: row I0 + l16, k = 32 ks + 8 g4 + v): for dC (dy, split) and dB (x)
+    // staged in LDS with the head's other rows; for dxh B's rows, the same for every head,
+    // loaded once for both row tiles. So the head loop issues no loads but the next head's,
+    // at its top, and every wait inside a head leaves them in flight (vector-memory
+    // operations complete in issue order). Every memory operation of the loop is issued on
+    // every path (at the last head the loads repeat the current head and go unused; the
+    // per-row sums are stored through descriptors that drop the rows past the chunk), so
+    // the compiler's counted waits never fall back to waiting for everything.
     f32x4 qkeep[OP == kOpX ? 2 : 1][OP == kOpX ? NKS : 1];
     if constexpr (OP == kOpX) {
-        load_q(h_first, NIT - 1 - wave);
+        const BufRsrc rq = make_rsrc(br, (uint32_t)(rows * GS * 2));
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qkeep[1][ks] = qraw[ks];
-    }
-    load_q(h_first, wave);
-    if constexpr (OP == kOpX) {
+        for (int qi = 0; qi < 2; ++qi) {
+            const int qrow = (qi == 0 ? wave : NIT - 1 - wave) * 16 + l16;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qkeep[0][ks] = qraw[ks];
+            for (int ks = 0; ks < NKS; ++ks)
+                qkeep[qi][ks] = __builtin_bit_cast(
+                    f32x4, buf_load16(rq, (uint32_t)((qrow * GS + ks * 32 + g4 * 8) * 2), 0u));
+        }
     }
 
 #pragma unroll 1
     for (int hh = 0; hh < NH; ++hh) {
         const int h = h_first + hh;
-        if constexpr (OP == kOpX) load_head(hh + 1 < NH ? h + 1 : h);
+        load_head(hh + 1 < NH ? h + 1 : h);
         const float g_end = s_g[T - 1];     // = G at the last real token
 #pragma unroll
         for (int qi = 0; qi < 2; ++qi) {
@@ -392,28 +377,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
             Frag<bf16> qf[NKS], ql[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                if constexpr (QF32) {
-                    split8(qraw[2 * ks], qraw[2 * ks + 1], qf[ks].v, ql[ks].v);
-                } else if constexpr (OP == kOpX) {
+                if constexpr (OP == kOpX) {
                     qf[ks].v = __builtin_bit_cast(bf16x8, qkeep[qi][ks]);
                 } else {
-                    qf[ks].v = __builtin_bit_cast(bf16x8, qraw[ks]);
+                    const int o = qrow * KS + ks * 32 + g4 * 8;
+                    qf[ks].v = *(const bf16x8*)(s_q + o);
+                    if constexpr (QSPLIT) ql[ks].v = *(const bf16x8*)(s_ql + o);
                 }
             }
-            // the next step's rows
-            if constexpr (OP != kOpX) {
-                if (qi == 0) load_q(h, NIT - 1 - wave);
-                else load_q(hh + 1 < NH ? h + 1 : h, wave);
-            }
             const uint32_t row0 = row0s[qi];
-            // dC, dB: the next head's rows, issued after every load this head still waits
-            // for (Q's rows of the second row tile): vector-memory operations complete in
-            // issue order, so issued earlier they would be waited for within this head.
-            // Every memory operation of the loop is issued on every path (at the last head
-            // the loads repeat the current head and go unused; the per-row sums are stored
-            // through descriptors that drop the rows past the chunk), so the compiler's
-            // counted waits never fall back to waiting for everything.
-            if (OP != kOpX && qi == 0) load_head(hh + 1 < NH ? h + 1 : h);
             f32x4 acc[NNH];  // output columns 16 (nt0 + j) + l16
 #pragma unroll
             for (int j = 0; j < NNH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
