@@ -84,8 +84,9 @@ struct BmCfg {
     static constexpr size_t Z_BYTES = (size_t)N * KS * 2;  // each part
     // dxh: x's rows of the head for the epilogue's x . dxh and dy . x (its D dy and dy . x
     // take dy as the sum of its bf16 high and low parts in V, within 2^-17 of dy); the row
-    // stride puts the four rows a read touches in different banks
-    static constexpr int XR = P + 16;
+    // stride (4 mod 8 words) puts the four rows 4 apart that a read touches on disjoint
+    // banks
+    static constexpr int XR = row_stride<bf16>(P);
     static constexpr size_t X_BYTES = OP == kOpX ? (size_t)T * XR * 2 : 0;
     // dC, dB: Q's rows of the head (read by rows, like K; dy split into two parts)
     static constexpr size_t Q_BYTES = OP == kOpX ? 0 : (size_t)T * KS * 2 * (QSPLIT ? 2 : 1);
@@ -166,17 +167,24 @@ struct Stager {
 
 // The state [P][S] (fp32) transposed into LDS: Z[s][p], high and low bf16 parts. Each
 // thread takes two neighbouring rows p, p + 1 and four columns, so the lanes of a wave
-// write consecutive 4-byte words of a Z row (a pair of bf16 values each).
+// write consecutive 4-byte words of a Z row (a pair of bf16 values each). The groups of
+// four columns are taken in the order 0, 2, 1, 3 within each run of four groups, so that
+// at headdim 64 the two halves of a wave write Z rows 8 apart (288 words: disjoint banks)
+// rather than 4 apart (144 words: half the banks shared).
+__device__ __forceinline__ int col_group(int sg) {
+    return (sg & ~3) | ((sg & 1) << 1) | ((sg >> 1) & 1);
+}
 template <int NTHR, int P, int S>
 struct StateTStager {
     static constexpr int NVEC = (P / 2) * (S / 4), NV = (NVEC + NTHR - 1) / NTHR;
+    static_assert((S / 4) % 4 == 0, "column groups are permuted in runs of four");
     f32x4 raw[2 * NV];
     __device__ __forceinline__ void load(const float* src, int tid) {
         const BufRsrc rs = make_rsrc(src, (uint32_t)(P * S * sizeof(float)));
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int v = tid + i * NTHR;
-            const int p = 2 * (v % (P / 2)), s0 = 4 * (v / (P / 2));
+            const int p = 2 * (v % (P / 2)), s0 = 4 * col_group(v / (P / 2));
             // unconditional loads (see Stager::load); slots past the state read zeros
             const uint32_t off = v < NVEC ? (uint32_t)((p * S + s0) * sizeof(float)) : 0x80000000u;
             raw[2 * i] = __builtin_bit_cast(f32x4, buf_load16(rs, off, 0u));
@@ -188,7 +196,7 @@ struct StateTStager {
         for (int i = 0; i < NV; ++i) {
             const int v = tid + i * NTHR;
             if (v >= NVEC) continue;
-            const int p = 2 * (v % (P / 2)), s0 = 4 * (v / (P / 2));
+            const int p = 2 * (v % (P / 2)), s0 = 4 * col_group(v / (P / 2));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 uint32_t hw, lw;
