@@ -590,11 +590,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, BmCfg<OP, P, S, T>::NTH
 }
 
 // ---- per-chunk sums for the reverse carry: dR_c = sum_t 2^{G_t} dy_t C_t^T -------------
-// One workgroup of T/32 waves per (batch, chunk, head). The rows 2^{G_t} dy_t (fp32, split
-// into bf16 high and low parts) and C_t sit in LDS as [t][.]; each output tile [16 p x 16 s]
+// One workgroup of T/32 waves per (batch, chunk, block of `nhr` heads of one group). The
+// group's C rows are staged in LDS once; per head the rows 2^{G_t} dy_t (fp32, split into
+// bf16 high and low parts) are written to LDS as [t][.], and the next head's rows load
+// into registers while the current head's products run. Each output tile [16 p x 16 s]
 // contracts over the chunk's tokens with both operands read down the token axis by the
 // transposing LDS read (token slot (g, v) <-> t = 4 g + v, 16 + 4 g + v - 4 in each
-// 32-token step, the same for both operands).
+// 32-token step, the same for both operands). Every load and store is issued on every
+// path (rows past the chunk read zeros through the descriptors; the last head re-loads
+// its own rows), so the compiler's waits stay counted.
 template <int P, int S, int T>
 struct DrCfg {
     static constexpr int NW = T / 32, NTHR = 64 * NW;
@@ -606,82 +610,114 @@ struct DrCfg {
 };
 
 template <int P, int S, int T>
-__global__ __launch_bounds__(2 * T) void bwd_dR_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(2 * T) void bwd_dR_mfma_kernel(BwdArgs a, int nhr) {
     using Cfg = DrCfg<P, S, T>;
     constexpr int YS = Cfg::YS, CS = Cfg::CS, NTHR = Cfg::NTHR, NW = Cfg::NW;
     constexpr int NPT = P / 16, NST = S / 16, NTILE = NPT * NST;
+    // whole loops with compile-time trip counts, so the compiler counts the stores issued
+    // after the next head's loads and its waits for those loads leave the stores in flight
+    static_assert(NTILE % NW == 0, "tiles per wave");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     bf16* s_yh = (bf16*)smem;                              // [T][YS]
     bf16* s_yl = (bf16*)(smem + Cfg::Y_BYTES);             // [T][YS]
     bf16* s_c = (bf16*)(smem + 2 * Cfg::Y_BYTES);          // [T][CS]
 
     const int L = a.L, H = a.H, NG = a.G;
-    const int nC = (L + T - 1) / T;
+    const int nC = (L + T - 1) / T, nhb = H / nhr;
     const int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = id % H, c = (id / H) % nC, b = id / (H * nC);
-    const int g = h / (H / NG);
+    const int hb = id % nhb, c = (id / nhb) % nC, b = id / (nhb * nC);
+    const int h_first = hb * nhr;
+    const int g = h_first / (H / NG);  // nhr divides the heads per group
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
     const int t0 = c * T, rows = min(T, L - t0);
     const size_t HP = (size_t)H * P, GS = (size_t)NG * S;
-    const float* dyr = a.dy + (((size_t)b * L + t0) * H + h) * P;
-    const bf16* cr = (const bf16*)a.Cm + (((size_t)b * L + t0) * NG + g) * S;
-    const size_t bhl = ((size_t)b * H + h) * L + t0;
+    const size_t tok0 = (size_t)b * L + t0;
+    const bf16* cr = (const bf16*)a.Cm + (tok0 * NG + g) * S;
 
-    // rows of 2^{G_t} dy_t: every load in flight, then the weighted split into LDS
-    constexpr int PER = P / 8, NVY = (T * PER + NTHR - 1) / NTHR;
+    // one head's rows of dy (fp32) and its per-token log2 decays G_t, in registers
+    constexpr int PER = P / 8, NVY = T * PER / NTHR;
+    static_assert(T * PER % NTHR == 0, "dy vectors per thread");
     f32x4 ry[2 * NVY];
     float wt[NVY];
+    auto load_dy = [&](int h) {
+        const BufRsrc rd = make_rsrc(a.dy + (tok0 * H + h) * P, (uint32_t)(rows * HP * 4));
+        const BufRsrc rg = make_rsrc(a.Gc + ((size_t)b * H + h) * L + t0, (uint32_t)(rows * 4));
 #pragma unroll
-    for (int i = 0; i < NVY; ++i) {
-        const int v = tid + i * NTHR;
-        const int r = v / PER, col = (v % PER) * 8;
-        const bool ok = v < T * PER && r < rows;
-        ry[2 * i] = ok ? *(const f32x4*)(dyr + r * HP + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-        ry[2 * i + 1] = ok ? *(const f32x4*)(dyr + r * HP + col + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        wt[i] = ok ? a.Gc[bhl + r] : 0.f;
-    }
+        for (int i = 0; i < NVY; ++i) {
+            const int v = tid + i * NTHR;
+            const int r = v / PER, col = (v % PER) * 8;
+            const uint32_t o = (uint32_t)((r * HP + col) * 4);
+            ry[2 * i] = __builtin_bit_cast(f32x4, buf_load16(rd, o, 0u));
+            ry[2 * i + 1] = __builtin_bit_cast(f32x4, buf_load16(rd, o + 16u, 0u));
+            wt[i] = buf_load_f32(rg, (uint32_t)(r * 4), 0u);
+        }
+    };
     Stager<bf16, NTHR, T, S, false> stc;
     stc.load(cr, GS, rows, tid);
-#pragma unroll
-    for (int i = 0; i < NVY; ++i) {
-        const int v = tid + i * NTHR;
-        if (v >= T * PER) continue;
-        const int r = v / PER, col = (v % PER) * 8;
-        const float w = exp2_fast(wt[i]);
-        bf16x8 hi, lo;
-        split8(w * ry[2 * i], w * ry[2 * i + 1], hi, lo);
-        *(bf16x8*)(s_yh + r * YS + col) = hi;
-        *(bf16x8*)(s_yl + r * YS + col) = lo;
-    }
+    load_dy(h_first);
     stc.store(s_c, nullptr, CS, tid);
-    lds_barrier();
 
-    float* out = a.R + (((size_t)b * H + h) * nC + c) * P * S;
 #pragma unroll 1
-    for (int tile = wave; tile < NTILE; tile += NW) {
-        const int p0 = (tile / NST) * 16, s0 = (tile % NST) * 16;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < nhr; ++hh) {
+        const int h = h_first + hh;
+        if (hh > 0) lds_barrier();  // every wave is done with the previous head's rows
+        // the weighted split: 2^{G_t} dy_t as bf16 high and low parts
 #pragma unroll
-        for (int k0 = 0; k0 < T; k0 += 32) {
-            Frag<bf16> yh, yl, cf;
-            yh.v = __builtin_shufflevector(lds_col4(s_yh, YS, k0 + 4 * g4, p0, lane),
-                                           lds_col4(s_yh, YS, k0 + 16 + 4 * g4, p0, lane),
-                                           0, 1, 2, 3, 4, 5, 6, 7);
-            yl.v = __builtin_shufflevector(lds_col4(s_yl, YS, k0 + 4 * g4, p0, lane),
-                                           lds_col4(s_yl, YS, k0 + 16 + 4 * g4, p0, lane),
-                                           0, 1, 2, 3, 4, 5, 6, 7);
-            cf.v = __builtin_shufflevector(lds_col4(s_c, CS, k0 + 4 * g4, s0, lane),
-                                           lds_col4(s_c, CS, k0 + 16 + 4 * g4, s0, lane),
-                                           0, 1, 2, 3, 4, 5, 6, 7);
-            mma(acc, yh, cf);
-            mma(acc, yl, cf);
+        for (int i = 0; i < NVY; ++i) {
+            const int v = tid + i * NTHR;
+            const int r = v / PER, col = (v % PER) * 8;
+            const float w = exp2_fast(wt[i]);
+            bf16x8 hi, lo;
+            split8(w * ry[2 * i], w * ry[2 * i + 1], hi, lo);
+            *(bf16x8*)(s_yh + r * YS + col) = hi;
+            *(bf16x8*)(s_yl + r * YS + col) = lo;
         }
-        // element (row p0 + 4 g4 + r, column s0 + l16)
+        lds_barrier();
+        load_dy(hh + 1 < nhr ? h + 1 : h);  // in flight during this head's products
+        // (kept ahead of the products and stores: the scheduler would otherwise sink the
+        // loads among the stores, and the wait for them at the next head would then wait
+        // for this head's stores as well)
+        __builtin_amdgcn_sched_barrier(0);
+
+        const BufRsrc ro = make_rsrc(a.R + (((size_t)b * H + h) * nC + c) * P * S,
+                                     (uint32_t)(P * S * 4));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[(size_t)(p0 + 4 * g4 + r) * S + s0 + l16] = acc[r];
+        for (int k = 0; k < NTILE / NW; ++k) {
+            const int tile = wave + k * NW;
+            const int p0 = (tile / NST) * 16, s0 = (tile % NST) * 16;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < T; k0 += 32) {
+                Frag<bf16> yh, yl, cf;
+                yh.v = __builtin_shufflevector(lds_col4(s_yh, YS, k0 + 4 * g4, p0, lane),
+                                               lds_col4(s_yh, YS, k0 + 16 + 4 * g4, p0, lane),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+                yl.v = __builtin_shufflevector(lds_col4(s_yl, YS, k0 + 4 * g4, p0, lane),
+                                               lds_col4(s_yl, YS, k0 + 16 + 4 * g4, p0, lane),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+                cf.v = __builtin_shufflevector(lds_col4(s_c, CS, k0 + 4 * g4, s0, lane),
+                                               lds_col4(s_c, CS, k0 + 16 + 4 * g4, s0, lane),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+                mma(acc, yh, cf);
+                mma(acc, yl, cf);
+            }
+            // element (row p0 + 4 g4 + r, column s0 + l16)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                buf_store_f32(acc[r], ro, (uint32_t)(((p0 + 4 * g4 + r) * S + s0 + l16) * 4), 0u);
+        }
     }
+}
+
+// Heads per dR workgroup: the largest divisor of the heads per group that leaves at least
+// two workgroups per compute unit (512), so C's rows are staged once for that many heads.
+inline int dr_heads_per_block(int batch, int nC, int H, int hpg) {
+    int best = 1;
+    for (int d = 1; d <= hpg; ++d)
+        if (hpg % d == 0 && (long)batch * nC * (H / d) >= 512) best = d;
+    return best;
 }
 
 template <int P, int S, int T>
@@ -695,7 +731,8 @@ hipError_t run_bwd_dR_mfma(const BwdArgs& a, int batch, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const int nC = (a.L + T - 1) / T;
-    kern<<<batch * nC * a.H, 2 * T, Cfg::LDS_BYTES, stream>>>(a);
+    const int nhr = dr_heads_per_block(batch, nC, a.H, a.H / a.G);
+    kern<<<batch * nC * (a.H / nhr), 2 * T, Cfg::LDS_BYTES, stream>>>(a, nhr);
     return hipGetLastError();
 }
 
