@@ -158,6 +158,21 @@ def test_backward_full_size_sampled_heads():
           names=("dx", "ddt", "dA", "dD", "dh0"))
 
 
+@pytest.mark.parametrize("name", ["780m-bf16", "2.7b-bf16"])
+def test_backward_full_size_all_elements(name):
+    # Every element of every gradient at full size against the oracle (a few seconds on the
+    # host's threads). The shapes take the matrix-core kernels with their full plans: the
+    # per-chunk gradient sums over blocks of heads (12 at the 780M shape, 40 at 2.7B), and
+    # at 780M the heads of a group split over two workgroups (dB, dC summed afterwards).
+    w = W[name]
+    cpu = problem(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.dtype,
+                  w.seed, h0=True)
+    got = run_gpu(cpu, w.chunk)
+    got = {n: v.cpu() for n, v in got.items()}
+    ref = run_oracle(cpu)
+    check(name + " full size, all elements", got, ref, "bf16")
+
+
 def test_backward_long_full_size_sampled_heads():
     # The long workload at full size (65536 tokens, 80 heads in 8 groups): the matrix-core
     # plan runs at 64-token chunks, whose fp32 chunk states (5.4 GB for the batch row) pass
