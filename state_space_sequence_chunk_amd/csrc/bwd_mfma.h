@@ -21,15 +21,15 @@
 //
 // gfx950 mapping: one workgroup per (batch, chunk, block of NH heads of one group), the
 // heads one after another (the next head's rows loading while the current one computes),
-// with T/32 pairs of row tiles and NSPLIT waves per pair; K rows, V rows, the state (bf16
-// high and low parts of its fp32 values) and G, dt in LDS. Wave pair w owns row tiles w
-// and T/16-1-w (equal causal work). For each 32-wide block of j it builds
-// the two 16x16 tiles Z^T[j][i] = K_j . Q_i on MFMA with Q's row fragments held in
-// registers; the accumulator layout of Z^T (lane: column i, four consecutive j) is the
-// A-operand layout of out += W V, so the decay, mask and w are applied in registers and
-// W is rounded once to bf16; V's token-axis fragments come from the transposing LDS read.
-// dy (fp32) enters the MFMAs split into a bf16 high part and a bf16 remainder (two
-// products, as Q of dC, K of dB and V of dxh); everything accumulates in fp32.
+// with T/32 pairs of row tiles and NSPLIT waves per pair; K rows, V rows, Q rows (dC, dB;
+// dxh's Q, B's rows, stays in registers), the state (bf16 high and low parts of its fp32
+// values) and G, dt in LDS. Wave pair w owns row tiles w and T/16-1-w (equal causal
+// work). For each 32-wide block of j it builds the two 16x16 tiles Z^T[j][i] = K_j . Q_i
+// on MFMA with Q's row fragments; the accumulator layout of Z^T (lane: column i, four
+// consecutive j) is the A-operand layout of out += W V, so the decay, mask and w are
+// applied in registers and W is split into bf16 high and low parts; V's token-axis
+// fragments come from the transposing LDS read. dy (fp32) enters the MFMAs split the same
+// way (as Q of dC, K of dB and V of dxh); everything accumulates in fp32.
 #pragma once
 
 #include <type_traits>
