@@ -8,27 +8,26 @@ namespace {
 
 constexpr int kSegHeads[] = {1, 2, 3, 4, 5, 6, 8};  // instantiated heads per workgroup
 
-// The kernel form for a shape: 4 waves and sub-blocks of at most 128 tokens, two
-// workgroups per CU, where that LDS plan fits in half a CU (80 KB); otherwise 8 waves,
-// one workgroup per CU, with the whole chunk per step or 128-token sub-blocks where the
-// chunk's B rows (dstate 256) would not fit in LDS next to the x buffers.
+// The kernel form for a shape: 64-token steps; 4 waves, two workgroups per CU, where the
+// LDS plan of two heads fits in half a CU (80 KB) and a head's running state takes at
+// most 32 registers per lane (dstate up to 128); otherwise 8 waves, one workgroup per CU.
 template <int P, int S, int T>
 struct SegPick {
-    static constexpr int TB4 = T > 128 ? 128 : T;
-    using Cfg4 = SegCfg<P, S, T, TB4, 4>;
-    // (and whose running state takes at most 32 registers per lane and head, so that two
-    // workgroups' waves fit the register file)
-    static constexpr bool DUAL = Cfg4::FITS && Cfg4::LDS_BYTES <= 81920 && P * S <= 64 * 128;
+    static constexpr int TB = 64;
+    using Cfg4 = SegCfg<P, S, T, TB, 4>;
+    static constexpr bool DUAL = Cfg4::FITS && Cfg4::lds_bytes(2) <= 81920 && P * S <= 64 * 128;
     static constexpr int NW = DUAL ? 4 : 8;
-    static constexpr int TB = DUAL ? TB4 : (S >= 256 && T > 128 ? 128 : T);
     using Cfg = SegCfg<P, S, T, TB, NW>;
     static constexpr int SLOTS = DUAL ? 512 : 256;  // workgroups resident on 256 CUs
     // running-state registers per lane the plan allows: no spills, and with 4 waves at
-    // most 256 registers per wave so that two workgroups stay resident (at 128-token
-    // chunks and dstate 64 three or four heads' x buffers take more, so 32 there)
-    static constexpr int MAX_STATE_REGS = DUAL ? (S == 64 && T == 128 ? 32 : 64) : 80;
-    // with sub-blocks, one weight slot per head and chunk parity
-    static constexpr int MAX_HEADS = Cfg::NSUB > 1 ? Cfg::NWS / 2 : 8;
+    // most 256 registers per wave so that two workgroups stay resident
+    static constexpr int MAX_STATE_REGS = DUAL ? 64 : 80;
+    // heads whose x buffers and weight slots fit the form's LDS share
+    static constexpr size_t LDS_CAP = DUAL ? 81920 : 163840;
+    static constexpr int MAX_HEADS = Cfg::lds_bytes(8) <= LDS_CAP   ? 8
+                                     : Cfg::lds_bytes(4) <= LDS_CAP ? 4
+                                     : Cfg::lds_bytes(2) <= LDS_CAP ? 2
+                                                                    : 1;
 };
 template <int P, int S, int T> using SegCfgFor = typename SegPick<P, S, T>::Cfg;
 
@@ -60,14 +59,14 @@ hipError_t run_seg(const void* x, const void* Bm, const float* A, const float* G
     using Pick = SegPick<P, S, T>;
     using Cfg = typename Pick::Cfg;
     auto kern = state_seg_kernel<P, S, T, Pick::TB, Pick::NW, NH>;
-    if (Cfg::LDS_BYTES > 65536) {
+    constexpr size_t lds = Cfg::lds_bytes(NH);
+    if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)Cfg::LDS_BYTES);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int nblocks = d.batch * pl.nseg * (d.nheads / NH);
-    kern<<<nblocks, Cfg::NTHR, Cfg::LDS_BYTES, stream>>>(
+    kern<<<nblocks, Cfg::NTHR, lds, stream>>>(
         (const bf16*)x, (const bf16*)Bm, A, G, dt_t, h0, (bf16*)states, sb.seg_end, sb.dec_in,
         sb.dec_seg, d.seqlen, d.nheads, d.ngroups, pl.chunks);
     return hipGetLastError();
@@ -118,10 +117,10 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // chunk). Workgroups are resident one or two per CU (the form's LDS plan), so the grid
 // runs in rounds of 256 or 512 workgroups; with two per CU, a last round that leaves
 // every CU at most one workgroup takes 0.9 of a full one. A workgroup's work is counted
-// in (sub-block, head) steps, plus 0.2 of a step per sub-block for the B rows its heads
-// share, 2 per head (entering and end states) and 2 per workgroup; each segment adds 0.3
-// for its carry and correction. These weights were fitted to measured forward times over
-// plans for five layer shapes (dstate 64 to 256, 8 to 80 heads, chunks of 64 to 256
+// in (64-token sub-block, head) units, plus 0.2 of a unit per sub-block for the B rows its
+// heads share, 2 per head (entering and end states) and 2 per workgroup; each segment adds
+// 0.3 for its carry and correction. These weights were fitted to measured forward times
+// over plans for five layer shapes (dstate 64 to 256, 8 to 80 heads, chunks of 64 to 256
 // tokens). Ties go to longer segments (fewer corrections downstream).
 bool state_seg_plan(int in_dtype, int states_dtype, const Dims& d, SegPlan* out) {
     if (in_dtype != kBF16 || states_dtype != kBF16) return false;

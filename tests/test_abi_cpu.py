@@ -106,10 +106,10 @@ def test_segment_plan_query():
     assert ssd.segment_plan(s) == (2, 11, 6)
     # the long layer at dstate 256: 2 heads x 43 chunks, 6 segments (240 workgroups)
     assert ssd.segment_plan(ssd.make_shape(1, 65536, 80, 64, 256, 8, 256, ssd.SSD_BF16)) == (2, 43, 6)
-    # the smaller layers take one head per workgroup (no shared B rows): the 780M layer
-    # (8 chunks per segment, 2 segments), the 8-head benchmark shape with 128-token chunks
-    # (8 chunks, 16 segments) and the small layer (4 chunks, 8 segments)
-    assert ssd.segment_plan(ssd.make_shape(4, 4096, 48, 64, 128, 1, 256, ssd.SSD_BF16)) == (1, 8, 2)
+    # the 780M layer: 2 heads x 4 chunks (4 segments, 384 workgroups); the 8-head benchmark
+    # shape with 128-token chunks and the small layer take one head per workgroup (no
+    # shared B rows): 8 chunks, 16 segments and 4 chunks, 8 segments
+    assert ssd.segment_plan(ssd.make_shape(4, 4096, 48, 64, 128, 1, 256, ssd.SSD_BF16)) == (2, 4, 4)
     assert ssd.segment_plan(ssd.make_shape(4, 16384, 8, 64, 128, 1, 128, ssd.SSD_BF16)) == (1, 8, 16)
     assert ssd.segment_plan(ssd.make_shape(2, 2048, 24, 64, 64, 1, 64, ssd.SSD_BF16)) == (1, 4, 8)
     lib = ssd.load_library()
