@@ -84,8 +84,12 @@ struct SegCfg {
     }
     static constexpr size_t LDS_BYTES = lds_bytes(2);
     static constexpr int STATE_REGS = MST * 4;
+    // (the x and B rows of a step split evenly over the threads, so that no load or LDS
+    // write of the step loop sits under a per-lane condition: there the compiler cannot
+    // count the memory operations issued after a load and waits for all of them)
     static constexpr bool FITS = lds_bytes(1) <= 163840 && NPT <= NWAVE && NST % WPT == 0 &&
-                                 T % TB == 0 && TB % 32 == 0;
+                                 T % TB == 0 && TB % 32 == 0 && (TB * P / VE) % NTHR == 0 &&
+                                 (TB * S / VE) % NTHR == 0;
 };
 
 // (the 4-wave form asks the register allocator for two waves per SIMD: two workgroups per
@@ -135,10 +139,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
         (uint32_t)((p * S + (odd_g4 ? (st0 + 1) * 16 + 4 * (g4 - 1) : st0 * 16 + 4 * g4)) *
                    sizeof(bf16));
     static_assert(MST % 2 == 0, "recorded states are written as tile pairs");
+    static_assert((TB * P / VE) % NTHR == 0 && (TB * S / VE) % NTHR == 0,
+                  "a step's x and B rows split evenly over the threads");
 
     const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
     const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
     auto rows_of = [&](int c) { return min(T, L - c * T); };
+    auto rdec_in = [&](int h) {  // the (batch, head) row of chunk decays
+        return make_rsrc(dec_in + ((size_t)b * H + h) * nC, (uint32_t)(nC * sizeof(float)));
+    };
     auto x_rsrc = [&](int c) {
         return make_rsrc(x + ((size_t)b * L + (size_t)c * T) * HP,
                          (uint32_t)(rows_of(c) * HP * sizeof(bf16)));
@@ -161,11 +170,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
 #pragma unroll
             for (int i = 0; i < Cfg::NXV; ++i) {
                 const int v = tid + i * NTHR;
-                if (v < TB * P / VE) {
-                    const int r = sub * TB + v / (P / VE), col = (v % (P / VE)) * VE;
-                    px[q][hh][i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(bf16)),
-                                              (uint32_t)((h_first + hh) * P * sizeof(bf16)));
-                }
+                const int r = sub * TB + v / (P / VE), col = (v % (P / VE)) * VE;
+                px[q][hh][i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(bf16)),
+                                          (uint32_t)((h_first + hh) * P * sizeof(bf16)));
             }
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
@@ -180,10 +187,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
 #pragma unroll
         for (int i = 0; i < Cfg::NBV; ++i) {
             const int v = tid + i * NTHR;
-            if (v < TB * S / VE) {
-                const int r = sub * TB + v / (S / VE), col = (v % (S / VE)) * VE;
-                pb[i] = buf_load16(rb, (uint32_t)(((size_t)r * grow + col) * sizeof(bf16)), 0u);
-            }
+            const int r = sub * TB + v / (S / VE), col = (v % (S / VE)) * VE;
+            pb[i] = buf_load16(rb, (uint32_t)(((size_t)r * grow + col) * sizeof(bf16)), 0u);
         }
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
@@ -203,10 +208,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
 #pragma unroll
             for (int i = 0; i < Cfg::NXV; ++i) {
                 const int v = tid + i * NTHR;
-                if (v < TB * P / VE) {
-                    const int r = v / (P / VE), col = (v % (P / VE)) * VE;
-                    *(Vec16*)(bx + r * XS + col) = px[q][hh][i];
-                }
+                const int r = v / (P / VE), col = (v % (P / VE)) * VE;
+                *(Vec16*)(bx + r * XS + col) = px[q][hh][i];
             }
         }
     };
@@ -217,10 +220,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
 #pragma unroll
         for (int i = 0; i < Cfg::NBV; ++i) {
             const int v = tid + i * NTHR;
-            if (v < TB * S / VE) {
-                const int r = v / (S / VE), col = (v % (S / VE)) * VE;
-                *(Vec16*)(bb + r * BS + col) = pb[i];
-            }
+            const int r = v / (S / VE), col = (v % (S / VE)) * VE;
+            *(Vec16*)(bb + r * BS + col) = pb[i];
         }
         if (sub == 0) {
 #pragma unroll
@@ -274,6 +275,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
         const int c1 = min(c + dc1, c_first + nck - 1);
         load_bdt(c1, u1);
         load_x(q_c, min(c + dc2, c_first + nck - 1), u2);
+        // keep the loads here, a step ahead of their use: the scheduler would otherwise
+        // sink them past the products toward the LDS writes that consume them
+        __builtin_amdgcn_sched_barrier(0);
         // the next step's x into LDS buffers q^1 (last read by the previous step, which ended
         // at a barrier)
         constexpr IntC<q ^ 1> q1{};
@@ -302,7 +306,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
                     const Vec16 out = Vec16{first[0], first[1], second[0], second[1]};
                     buf_store16(out, rst, st_off + (uint32_t)(m * 16 * sizeof(bf16)));
                 }
-                if (tid == 0) dec_in[((size_t)b * H + h) * nC + c] = dacc[hh];
+                // one lane writes the decay (the others' offsets lie outside the
+                // descriptor and their stores are dropped): no store under a condition
+                buf_store_f32(dacc[hh], rdec_in(h), tid == 0 ? (uint32_t)(c * sizeof(float)) : 0x80000000u, 0u);
                 dacc[hh] += gl[hh];
                 const float dec = exp2_fast(gl[hh]);
 #pragma unroll
