@@ -10,21 +10,26 @@
 // state, so a prefill by ssd_forward continues token by token here.
 //
 // gfx950 mapping: the step is a read-modify-write of the state (8 bytes of HBM traffic per
-// element against 4 flops), so it is bound by HBM. Each 256-thread workgroup owns a
-// contiguous slice of one (batch, head) state of up to 2048 floats; a thread owns 4
-// consecutive state columns (one 16-byte load and store) of up to 2 rows, and issues both
-// rows' loads before using either. The S/4 threads that share a row are adjacent lanes of
-// one wave, so y's sum over s is a butterfly over those lanes (no LDS, no barrier).
+// element against 4 flops); at decode sizes (a few MB) its time is mostly the latency of
+// one round trip to memory. Each 256-thread workgroup owns a contiguous slice of one
+// (batch, head) state of up to 256 x ROWS x 4 floats; a thread owns 4 consecutive state
+// columns (one 16-byte load and store) of up to ROWS rows, and issues all its rows' loads
+// before using any. The S/4 threads that share a row are adjacent lanes of one wave, so y's
+// sum over s is a butterfly over those lanes (no LDS, no barrier). ROWS is 2, or 1 where
+// two rows per thread would leave fewer workgroups than compute units (measured on the
+// 2.7B layer's 160 states: 3.9 us with 2 rows, 4.0 with 1; on the article's 32 states:
+// 2.7 us with 2 rows, 2.4 with 1).
+#include <algorithm>
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
 constexpr int kDecodeThreads = 256;
-constexpr int kDecodeRows = 2;                              // state vectors per thread
-constexpr int kDecodeVecs = kDecodeThreads * kDecodeRows;  // per workgroup at most
 
-template <typename TIn, int S>
+template <typename TIn, int S, int ROWS>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ dt, const float* __restrict__ A,
     const TIn* __restrict__ Bm, const TIn* __restrict__ Cm, const float* __restrict__ Dv,
@@ -52,10 +57,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
     // vpw is a multiple of 64, so each wave is either wholly inside or wholly outside
     // the slice for a given j (the row butterfly below needs its whole lane group)
-    f32x4 sv[kDecodeRows];
-    float xv[kDecodeRows];
+    f32x4 sv[ROWS];
+    float xv[ROWS];
 #pragma unroll
-    for (int j = 0; j < kDecodeRows; ++j) {
+    for (int j = 0; j < ROWS; ++j) {
         const int t = threadIdx.x + kDecodeThreads * j;
         if (t < vpw) {
             sv[j] = *(const f32x4*)(st + (size_t)(v0 + t) * 4);
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         }
     }
 #pragma unroll
-    for (int j = 0; j < kDecodeRows; ++j) {
+    for (int j = 0; j < ROWS; ++j) {
         const int t = threadIdx.x + kDecodeThreads * j;
         if (t < vpw) {
             const int v = v0 + t, p = v / RL;
@@ -89,7 +94,9 @@ static hipError_t decode_by_s(const void* x, const void* dt, const float* A, con
                               const void* Cm, const float* D, float* state, float* y,
                               const Dims& d, hipStream_t stream) {
     const int vecs = d.headdim * d.dstate / 4;  // per (batch, head)
-    const int vpw = vecs < kDecodeVecs ? vecs : kDecodeVecs;
+    // two rows per thread unless that leaves fewer workgroups than compute units
+    const int rows = (long)d.batch * d.nheads * vecs / (2 * kDecodeThreads) >= 256 ? 2 : 1;
+    const int vpw = std::min(vecs, rows * kDecodeThreads);
     const int nblocks = d.batch * d.nheads * (vecs / vpw);
     auto go = [&](auto kern) {
         kern<<<nblocks, kDecodeThreads, 0, stream>>>((const TIn*)x, (const TIn*)dt, A,
@@ -97,14 +104,18 @@ static hipError_t decode_by_s(const void* x, const void* dt, const float* A, con
                                                      d.nheads, d.headdim, d.ngroups, vpw);
         return hipGetLastError();
     };
-    switch (d.dstate) {
-        case 16: return go(decode_kernel<TIn, 16>);
-        case 32: return go(decode_kernel<TIn, 32>);
-        case 64: return go(decode_kernel<TIn, 64>);
-        case 128: return go(decode_kernel<TIn, 128>);
-        case 256: return go(decode_kernel<TIn, 256>);
-    }
-    return hipErrorInvalidValue;
+    auto by_s = [&](auto rows_c) -> hipError_t {
+        constexpr int R = decltype(rows_c)::value;
+        switch (d.dstate) {
+            case 16: return go(decode_kernel<TIn, 16, R>);
+            case 32: return go(decode_kernel<TIn, 32, R>);
+            case 64: return go(decode_kernel<TIn, 64, R>);
+            case 128: return go(decode_kernel<TIn, 128, R>);
+            case 256: return go(decode_kernel<TIn, 256, R>);
+        }
+        return hipErrorInvalidValue;
+    };
+    return rows == 2 ? by_s(std::integral_constant<int, 2>{}) : by_s(std::integral_constant<int, 1>{});
 }
 
 hipError_t launch_decode(int in_dtype, const void* x, const void* dt, const float* A,
