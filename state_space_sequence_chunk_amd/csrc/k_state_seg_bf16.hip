@@ -59,14 +59,8 @@ hipError_t run_seg(const void* x, const void* Bm, const float* A, const float* G
     using Pick = SegPick<P, S, T>;
     using Cfg = typename Pick::Cfg;
     auto kern = state_seg_kernel<P, S, T, Pick::TB, Pick::NW, NH>;
-    constexpr size_t lds = Cfg::lds_bytes(NH);
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     const int nblocks = d.batch * pl.nseg * (d.nheads / NH);
-    kern<<<nblocks, Cfg::NTHR, lds, stream>>>(
+    kern<<<nblocks, Cfg::NTHR, 0, stream>>>(
         (const bf16*)x, (const bf16*)Bm, A, G, dt_t, h0, (bf16*)states, sb.seg_end, sb.dec_in,
         sb.dec_seg, d.seqlen, d.nheads, d.ngroups, pl.chunks);
     return hipGetLastError();

@@ -23,11 +23,13 @@
 // accumulator layout and stays in registers for the whole segment. A step is one (chunk,
 // 64-token sub-block) for all NH heads: the sub-block's B rows, staged in LDS once, give
 // each wave its B fragments once per 32 tokens, and those feed every head's products. B
-// rows and every head's x rows are double-buffered in LDS by step parity: x rows load
-// into registers two steps ahead and move to LDS at the top of the step before; B rows
-// and dt load at the top of the step before and move to LDS (dt, at a chunk's first
-// sub-block, as the head's decay weights) at its end, so the end of a step is a single
-// barrier. The contraction over the tokens is dS^T = B^T (w o x) on bf16 MFMA 16x16x32
+// rows and every head's x rows are double-buffered in LDS by step parity and go there
+// straight from memory (direct-to-LDS buffer loads, no registers), issued at the top of
+// the step before, right after the barrier that freed the buffers; the tiles are unpadded
+// with their 16-byte pieces swizzled per row, so the transposing reads stay free of bank
+// conflicts. dt loads into registers a step ahead and becomes the head's decay weights (at
+// a chunk's first sub-block) at the end of the step before, so the end of a step is a
+// single barrier, which also waits for the direct loads. The contraction over the tokens is dS^T = B^T (w o x) on bf16 MFMA 16x16x32
 // with both operands from the transposing LDS read; the fused operand w_j x_j is formed in
 // fp32 and split into a bf16 high part and a bf16 remainder (two MFMAs against the exact
 // bf16 B). The accumulator holds four consecutive state columns s of one row p per lane;
@@ -69,14 +71,13 @@ struct SegCfg {
     static constexpr int NPT = P / 16, NST = S / 16;
     static constexpr int WPT = NPT >= NWAVE ? 1 : NWAVE / NPT;  // waves per p-tile
     static constexpr int MST = (NST + WPT - 1) / WPT;           // s-tiles per wave
-    static constexpr int VE = 8;                                // bf16 per 16 bytes
-    static constexpr int XS = col_stride<bf16>(P), BS = col_stride<bf16>(S);
-    static constexpr int NXV = (TB * P / VE + NTHR - 1) / NTHR;  // x vectors per thread and head
-    static constexpr int NBV = (TB * S / VE + NTHR - 1) / NTHR;  // B vectors per thread
+    static constexpr int XRB = P * 2, BRB = S * 2;  // row bytes of the x and B tiles
+    static constexpr int NXI = TB * XRB / 1024 / NW;  // direct loads per wave and head (x)
+    static constexpr int NBI = TB * BRB / 1024 / NW;  // direct loads per wave (B)
     static constexpr int PER = T / 64;                          // tokens per lane in the scan
-    static constexpr size_t X_BYTES = (size_t)TB * XS * sizeof(bf16);  // one head's rows
+    static constexpr size_t X_BYTES = (size_t)TB * XRB;  // one head's rows
     static constexpr size_t W_BYTES = (size_t)T * sizeof(float);       // one chunk's weights
-    static constexpr size_t B_BYTES = (size_t)TB * BS * sizeof(bf16);
+    static constexpr size_t B_BYTES = (size_t)TB * BRB;
     // B and every head's x rows double-buffered by step parity; weights per (chunk parity,
     // head)
     static constexpr size_t lds_bytes(int nh) {
@@ -84,13 +85,48 @@ struct SegCfg {
     }
     static constexpr size_t LDS_BYTES = lds_bytes(2);
     static constexpr int STATE_REGS = MST * 4;
-    // (the x and B rows of a step split evenly over the threads, so that no load or LDS
-    // write of the step loop sits under a per-lane condition: there the compiler cannot
-    // count the memory operations issued after a load and waits for all of them)
+    // (the x and B tiles of a step split into whole 1 KB direct loads per wave, so that no
+    // load of the step loop sits under a condition: there the compiler cannot count the
+    // memory operations issued after a load and waits for all of them; the swizzle covers
+    // rows of 128 bytes and more)
     static constexpr bool FITS = lds_bytes(1) <= 163840 && NPT <= NWAVE && NST % WPT == 0 &&
-                                 T % TB == 0 && TB % 32 == 0 && (TB * P / VE) % NTHR == 0 &&
-                                 (TB * S / VE) % NTHR == 0;
+                                 T % TB == 0 && TB % 32 == 0 && (TB * XRB) % (1024 * NW) == 0 &&
+                                 (TB * BRB) % (1024 * NW) == 0 && (P == 64 || P == 128) &&
+                                 S >= 64;
 };
+
+// Swizzled tiles: the 16-byte piece c of row r sits at piece position c ^ swz(r), so that the
+// 8 rows x 2 pieces that 32 lanes read together through the transposing LDS read fall on
+// distinct banks without row padding (rows of 128 bytes: two rows per 64 banks; of 256 bytes
+// or more: a row per 64 banks).
+template <int RB> __device__ __forceinline__ int swz(int r) {
+    return RB == 128 ? 2 * ((r >> 1) & 3) : 2 * (r & 7);
+}
+template <int RB>
+__device__ __forceinline__ bf16x4 lds_col4_sw(const bf16* base, int r0, int c0, int lane) {
+    const int s = lane & 15;
+    const int r = r0 + (s >> 2), col = c0 + 4 * (s & 3);
+    const bf16* p = base + r * (RB / 2) + (((col >> 3) ^ swz<RB>(r)) << 3) + (col & 7);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(__attribute__((address_space(3))) bf16*)p);
+}
+// Rows row0 .. row0 + (NW NI 1024 / RB) - 1 of a row-major bf16 matrix (row stride gstride
+// elements) straight into a swizzled LDS tile: wave w issues the direct-to-LDS loads of
+// pieces (w NI + k) 64 + lane, k < NI (lane L of a load lands 16 L bytes past its base).
+template <int RB, int NI>
+__device__ __forceinline__ void dma_tile(bf16* lds, BufRsrc r, int row0, uint32_t gstride,
+                                         uint32_t soff, int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+        const int n = (wave * NI + k) * 64 + lane;
+        const int rr = n / (RB / 16), pp = n % (RB / 16);
+        const int c = pp ^ swz<RB>(rr);
+        const uint32_t voff = ((uint32_t)(row0 + rr) * gstride + (uint32_t)c * 8u) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds + (wave * NI + k) * 512), 16, voff,
+            soff, 0, 0);
+    }
+}
 
 // (the 4-wave form asks the register allocator for two waves per SIMD: two workgroups per
 // compute unit)
@@ -101,19 +137,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
     bf16* __restrict__ states, float* __restrict__ seg_end, float* __restrict__ dec_in,
     float* __restrict__ dec_seg, int L, int H, int ngroups, int K) {
     using Cfg = SegCfg<P, S, T, TB, NW>;
-    constexpr int VE = Cfg::VE, XS = Cfg::XS, BS = Cfg::BS, NTHR = Cfg::NTHR, PER = Cfg::PER;
+    constexpr int PER = Cfg::PER, XRB = Cfg::XRB, BRB = Cfg::BRB;
     constexpr int MST = Cfg::MST, WPT = Cfg::WPT, NSUB = Cfg::NSUB;
     constexpr int SPC = NSUB;  // steps per chunk
 
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    auto s_b = [&](int k) { return (bf16*)(smem + k * Cfg::B_BYTES); };  // [TB][BS]
-    auto s_x = [&](int k, int hh) {                                       // [TB][XS]
-        return (bf16*)(smem + 2 * Cfg::B_BYTES + (k * NH + hh) * Cfg::X_BYTES);
-    };
-    auto s_w = [&](int par, int hh) {  // [T] weights of one (chunk, head)
-        return (float*)(smem + 2 * Cfg::B_BYTES + 2 * NH * Cfg::X_BYTES +
-                        (par * NH + hh) * Cfg::W_BYTES);
-    };
+    // one LDS object per buffer parity, so that the compiler sees the direct loads into
+    // one parity's buffers and the reads of the other's as disjoint (it waits for a direct
+    // load before a read of LDS that it cannot show to be elsewhere)
+    __shared__ __attribute__((aligned(16))) bf16 sB0[TB * S], sB1[TB * S];   // [TB][S] swizzled
+    __shared__ __attribute__((aligned(16))) bf16 sX0[NH * TB * P], sX1[NH * TB * P];  // [NH][TB][P]
+    __shared__ __attribute__((aligned(16))) float sW[2 * NH * T];
+    auto s_b = [&](auto k_c) { return decltype(k_c)::value ? sB1 : sB0; };
+    auto s_x = [&](auto k_c, int hh) { return (decltype(k_c)::value ? sX1 : sX0) + hh * TB * P; };
+    auto s_w = [&](int par, int hh) { return sW + (par * NH + hh) * T; };  // [T] one (chunk, head)
 
     const int nC = (L + T - 1) / T;
     const int nseg = (nC + K - 1) / K;
@@ -139,8 +175,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
         (uint32_t)((p * S + (odd_g4 ? (st0 + 1) * 16 + 4 * (g4 - 1) : st0 * 16 + 4 * g4)) *
                    sizeof(bf16));
     static_assert(MST % 2 == 0, "recorded states are written as tile pairs");
-    static_assert((TB * P / VE) % NTHR == 0 && (TB * S / VE) % NTHR == 0,
-                  "a step's x and B rows split evenly over the threads");
+    static_assert(Cfg::NXI >= 1 && Cfg::NBI >= 1, "a step's rows split evenly over the waves");
 
     const BufRsrc rdt = make_rsrc(dt_t + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
     const BufRsrc rg = make_rsrc(G + (size_t)b * H * L, (uint32_t)((size_t)H * L * sizeof(float)));
@@ -154,42 +189,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
     };
 
     // ---- staging --------------------------------------------------------------------------
-    // x rows (all heads) and the chunk decay: into register set j % 2 two steps ahead, into
-    // LDS buffers one step ahead (at the top of the step before). B rows and dt: loaded at
-    // the top of the step before, into LDS (B) and the weight slot (dt, at a chunk's first
-    // sub-block) at its end, before its barrier.
-    Vec16 px[2][NH][Cfg::NXV], pb[Cfg::NBV];
+    // B rows and every head's x rows go straight from memory into the LDS buffers of the
+    // next step (issued at the top of the step before, after the barrier that freed them);
+    // the chunk decay two steps ahead and dt one step ahead go to registers, dt into the
+    // weight slot (at a chunk's first sub-block) at the end of the step before.
     float pdt[NH][PER];
     float gls[2][NH];
-    auto load_x = [&](auto set_c, int c, int sub) {
+    auto load_g = [&](auto set_c, int c) {
         constexpr int q = decltype(set_c)::value;
         const int rows = rows_of(c);
-        const BufRsrc rx = x_rsrc(c);
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-            for (int i = 0; i < Cfg::NXV; ++i) {
-                const int v = tid + i * NTHR;
-                const int r = sub * TB + v / (P / VE), col = (v % (P / VE)) * VE;
-                px[q][hh][i] = buf_load16(rx, (uint32_t)((r * HP + col) * sizeof(bf16)),
-                                          (uint32_t)((h_first + hh) * P * sizeof(bf16)));
-            }
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
             const uint32_t o = (uint32_t)(((size_t)(h_first + hh) * L + (size_t)c * T) * sizeof(float));
             gls[q][hh] = buf_load_f32(rg, (uint32_t)((rows - 1) * 4), o);
         }
     };
-    auto load_bdt = [&](int c, int sub) {
+    auto dma_rows = [&](auto kb, int c, int sub) {
         const int rows = rows_of(c);
         const BufRsrc rb = make_rsrc(Bm + (((size_t)b * L + (size_t)c * T) * ngroups + g) * S,
                                      (uint32_t)(((size_t)(rows - 1) * grow + S) * sizeof(bf16)));
+        dma_tile<BRB, Cfg::NBI>(s_b(kb), rb, sub * TB, (uint32_t)grow, 0u, wave, lane);
+        const BufRsrc rx = x_rsrc(c);
 #pragma unroll
-        for (int i = 0; i < Cfg::NBV; ++i) {
-            const int v = tid + i * NTHR;
-            const int r = sub * TB + v / (S / VE), col = (v % (S / VE)) * VE;
-            pb[i] = buf_load16(rb, (uint32_t)(((size_t)r * grow + col) * sizeof(bf16)), 0u);
-        }
+        for (int hh = 0; hh < NH; ++hh)
+            dma_tile<XRB, Cfg::NXI>(s_x(kb, hh), rx, sub * TB, (uint32_t)HP,
+                                    (uint32_t)((h_first + hh) * P * sizeof(bf16)), wave, lane);
+    };
+    auto load_dt = [&](int c) {
+        const int rows = rows_of(c);
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
             const uint32_t o = (uint32_t)(((size_t)(h_first + hh) * L + (size_t)c * T) * sizeof(float));
@@ -200,29 +227,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
             }
         }
     };
-    auto store_x = [&](auto set_c) {
-        constexpr int q = decltype(set_c)::value;
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-            bf16* bx = s_x(q, hh);
-#pragma unroll
-            for (int i = 0; i < Cfg::NXV; ++i) {
-                const int v = tid + i * NTHR;
-                const int r = v / (P / VE), col = (v % (P / VE)) * VE;
-                *(Vec16*)(bx + r * XS + col) = px[q][hh][i];
-            }
-        }
-    };
-    // B rows into LDS buffer kb; at a chunk's first sub-block wave hh turns head hh's dt into
-    // its weights, in the slot of the chunk's parity
-    auto store_bw = [&](int kb, int c, int sub) {
-        bf16* bb = s_b(kb);
-#pragma unroll
-        for (int i = 0; i < Cfg::NBV; ++i) {
-            const int v = tid + i * NTHR;
-            const int r = v / (S / VE), col = (v % (S / VE)) * VE;
-            *(Vec16*)(bb + r * BS + col) = pb[i];
-        }
+    // at a chunk's first sub-block wave hh turns head hh's dt into its weights, in the slot
+    // of the chunk's parity
+    auto store_w = [&](int c, int sub) {
         if (sub == 0) {
 #pragma unroll
             for (int hh = 0; hh < NH; ++hh) {
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
         constexpr int u = decltype(u_c)::value, q = decltype(q_c)::value;
         constexpr int sub = u;
         constexpr int u1 = (u + 1) % SPC, dc1 = (u + 1) / SPC;
-        constexpr int u2 = (u + 2) % SPC, dc2 = (u + 2) / SPC;
+        constexpr int dc2 = (u + 2) / SPC;  // the chunk two steps ahead
         const int c = c_first + ci;
         float gl[NH];
 #pragma unroll
@@ -273,15 +280,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
         // loads for the next step (B, dt) and two steps ahead (x); past the segment's end
         // they repeat its last chunk and are never used
         const int c1 = min(c + dc1, c_first + nck - 1);
-        load_bdt(c1, u1);
-        load_x(q_c, min(c + dc2, c_first + nck - 1), u2);
-        // keep the loads here, a step ahead of their use: the scheduler would otherwise
-        // sink them past the products toward the LDS writes that consume them
+        // the next step's rows into LDS buffers q^1 (last read by the previous step, which
+        // ended at a barrier); dt for the next step, the chunk decay two steps ahead
+        dma_rows(IntC<q ^ 1>{}, c1, u1);
+        load_dt(c1);
+        load_g(q_c, min(c + dc2, c_first + nck - 1));
         __builtin_amdgcn_sched_barrier(0);
-        // the next step's x into LDS buffers q^1 (last read by the previous step, which ended
-        // at a barrier)
-        constexpr IntC<q ^ 1> q1{};
-        store_x(q1);
 
         if constexpr (sub == 0) {
 #pragma unroll
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
             }
         }
 
-        const bf16* bb = s_b(q);
+        const bf16* bb = s_b(q_c);
         // slot (g4, v) carries token 32 ks + 16 (v/4) + 4 g4 + v%4 (two column reads)
 #pragma unroll 2
         for (int ks = 0; ks < TB / 32; ++ks) {
@@ -325,18 +329,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
 #pragma unroll
             for (int m = 0; m < MST; ++m) {
                 const int st = st0 + m;
-                const bf16x4 a = lds_col4(bb, BS, r_lo, st * 16, lane);
-                const bf16x4 q4 = lds_col4(bb, BS, r_hi, st * 16, lane);
+                const bf16x4 a = lds_col4_sw<BRB>(bb, r_lo, st * 16, lane);
+                const bf16x4 q4 = lds_col4_sw<BRB>(bb, r_hi, st * 16, lane);
                 bf[m].v = __builtin_shufflevector(a, q4, 0, 1, 2, 3, 4, 5, 6, 7);
             }
 #pragma unroll
             for (int hh = 0; hh < NH; ++hh) {
-                const bf16* bx = s_x(q, hh);
+                const bf16* bx = s_x(q_c, hh);
                 const float* bw = s_w(c & 1, hh) + sub * TB;
                 const f32x4 w_lo = *(const f32x4*)(bw + r_lo);
                 const f32x4 w_hi = *(const f32x4*)(bw + r_hi);
-                const bf16x4 a = lds_col4(bx, XS, r_lo, pt * 16, lane);
-                const bf16x4 q4 = lds_col4(bx, XS, r_hi, pt * 16, lane);
+                const bf16x4 a = lds_col4_sw<XRB>(bx, r_lo, pt * 16, lane);
+                const bf16x4 q4 = lds_col4_sw<XRB>(bx, r_hi, pt * 16, lane);
                 Frag<bf16> hi, lo;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -353,17 +357,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
                 }
             }
         }
-        // the next step's B rows and (at a chunk's first sub-block) weights
-        store_bw(q ^ 1, c + dc1, u1);
-        lds_barrier();  // every wave is done with buffers q before they are refilled
+        // the next chunk's weights (at its first sub-block)
+        store_w(c + dc1, u1);
+        lds_barrier();  // the next step's rows have landed; every wave is done with buffers q
     };
 
     // ---- prologue: steps 0 and 1 loaded, step 0 in LDS ----------------------------------
-    load_x(IntC<0>{}, c_first, 0);
-    load_bdt(c_first, 0);
-    load_x(IntC<1>{}, min(c_first + 1 / SPC, c_first + nck - 1), 1 % SPC);
-    store_x(IntC<0>{});
-    store_bw(0, c_first, 0);
+    dma_rows(IntC<0>{}, c_first, 0);
+    load_dt(c_first);
+    load_g(IntC<0>{}, c_first);
+    load_g(IntC<1>{}, min(c_first + 1 / SPC, c_first + nck - 1));
+    store_w(c_first, 0);
     lds_barrier();
 
     constexpr int CPP = SPC % 2 == 0 ? 1 : 2;  // chunks per pass
