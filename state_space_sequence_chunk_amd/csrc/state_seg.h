@@ -277,11 +277,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4
         float gl[NH];
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) gl[hh] = gls[q][hh];  // before set q is reloaded
-        // loads for the next step (B, dt) and two steps ahead (x); past the segment's end
-        // they repeat its last chunk and are never used
-        const int c1 = min(c + dc1, c_first + nck - 1);
         // the next step's rows into LDS buffers q^1 (last read by the previous step, which
-        // ended at a barrier); dt for the next step, the chunk decay two steps ahead
+        // ended at a barrier); dt for the next step, the chunk decay two steps ahead; past
+        // the segment's end the loads repeat its last chunk and are never used
+        const int c1 = min(c + dc1, c_first + nck - 1);
         dma_rows(IntC<q ^ 1>{}, c1, u1);
         load_dt(c1);
         load_g(q_c, min(c + dc2, c_first + nck - 1));
